@@ -1,0 +1,130 @@
+"""Seeded synthetic inputs for the attention workloads, shared by tests, bench and smoke.
+
+This module draws random numbers and rounds them to the storage dtype; it holds
+none of the attention arithmetic. Every draw comes from a NumPy
+``Generator(PCG64(seed))`` in a fixed order (sequence lengths, then Q, K, V,
+dO), as fp32 standard normals times ``std``, then rounded to the storage dtype
+with round-to-nearest-even on the host. The same bytes go to the GPU and to the
+fp64 checker.
+
+Named workloads (shapes of the pages' attention benchmarks, synthetic values):
+
+* ``fp32_small``   B=1, H=1, N=128, d=64, fp32, non-causal, forward only.
+* ``gpt2m``        B=8, H=16, N=1024, d=64, bf16, non-causal (GPT-2-medium shape).
+* ``long_causal``  B=1, H=32, N=16384, d=128, bf16, causal, std 1/sqrt(2).
+* ``varlen_alibi`` 32 packed sequences, lengths uniform in [64, 8192], H=16,
+  d=128, bf16, causal, ALiBi slopes 2^(-8(h+1)/H), forward only.
+* ``gqa``          B=2, H=32, Hkv=8, N=8192, d=128, bf16, causal.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field, replace
+from typing import Optional
+
+import numpy as np
+import torch
+
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "alibi_slopes", "flops"]
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    dtype: str  # "fp32" | "bf16" | "fp16"
+    B: int
+    H: int
+    Hkv: int
+    N: int
+    d: int
+    causal: bool = False
+    alibi: bool = False
+    std: float = 1.0
+    backward: bool = True
+    # packed sequences: number of sequences and inclusive length range
+    varlen: Optional[tuple] = None
+    extra: dict = field(default_factory=dict)
+
+    def with_(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+
+WORKLOADS = {
+    "fp32_small": Workload("fp32_small", "fp32", 1, 1, 1, 128, 64, backward=False),
+    "gpt2m": Workload("gpt2m", "bf16", 8, 16, 16, 1024, 64),
+    "long_causal": Workload("long_causal", "bf16", 1, 32, 32, 16384, 128, causal=True,
+                            std=1.0 / math.sqrt(2.0)),
+    "varlen_alibi": Workload("varlen_alibi", "bf16", 32, 16, 16, 8192, 128, causal=True,
+                             alibi=True, backward=False, varlen=(64, 8192)),
+    "gqa": Workload("gqa", "bf16", 2, 32, 8, 8192, 128, causal=True),
+}
+
+_TORCH_DTYPE = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}
+
+
+def alibi_slopes(H: int) -> torch.Tensor:
+    """Geometric ALiBi slopes 2^(-8 (h+1) / H) for heads h = 0..H-1, fp32."""
+    return torch.tensor([2.0 ** (-8.0 * (h + 1) / H) for h in range(H)], dtype=torch.float32)
+
+
+def _normal(rng: np.random.Generator, shape, std: float, dtype: str) -> torch.Tensor:
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        x *= np.float32(std)
+    return torch.from_numpy(x).to(_TORCH_DTYPE[dtype])
+
+
+def make_inputs(w: Workload, seed: int = 0, lengths=None, with_grad: Optional[bool] = None) -> dict:
+    """Draw one batch of inputs for workload ``w`` on the host.
+
+    Returns a dict with CPU tensors ``q``, ``k``, ``v`` (and ``do`` when the
+    workload has a backward), ``cu_seqlens`` (int32 [B+1] or None),
+    ``alibi_slopes`` (fp32 [H] or None), ``scale`` (1/sqrt(d)), ``max_seqlen``.
+    Dense layouts are q [B, N, H, d], k/v [B, N, Hkv, d]; packed layouts are
+    q [T, H, d], k/v [T, Hkv, d]. ``lengths`` overrides the drawn packed lengths.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    with_grad = w.backward if with_grad is None else with_grad
+    cu = None
+    if w.varlen is not None:
+        if lengths is None:
+            lo, hi = w.varlen
+            lengths = rng.integers(lo, hi + 1, size=w.B)
+        lengths = np.asarray(lengths, dtype=np.int64)
+        cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32))
+        rows = (int(cu[-1]),)
+        max_seqlen = int(lengths.max()) if len(lengths) else 0
+    else:
+        rows = (w.B, w.N)
+        max_seqlen = w.N
+    out = {
+        "q": _normal(rng, rows + (w.H, w.d), w.std, w.dtype),
+        "k": _normal(rng, rows + (w.Hkv, w.d), w.std, w.dtype),
+        "v": _normal(rng, rows + (w.Hkv, w.d), w.std, w.dtype),
+    }
+    out["do"] = _normal(rng, rows + (w.H, w.d), w.std, w.dtype) if with_grad else None
+    out["cu_seqlens"] = cu
+    out["alibi_slopes"] = alibi_slopes(w.H) if w.alibi else None
+    out["scale"] = 1.0 / math.sqrt(w.d)
+    out["max_seqlen"] = max_seqlen
+    return out
+
+
+def seq_lengths(inputs: dict, w: Workload) -> list:
+    """Per-sequence lengths of a drawn batch (all N for dense inputs)."""
+    cu = inputs["cu_seqlens"]
+    if cu is None:
+        return [w.N] * w.B
+    c = cu.tolist()
+    return [c[i + 1] - c[i] for i in range(len(c) - 1)]
+
+
+def flops(w: Workload, lengths=None, backward: bool = False) -> float:
+    """Dense attention work: 4*H*n^2*d per sequence, halved if causal, x2.5 for backward."""
+    if lengths is None:
+        lengths = [w.N] * w.B
+    f = sum(4.0 * w.H * float(n) * float(n) * w.d for n in lengths)
+    if w.causal:
+        f *= 0.5
+    return f * (2.5 if backward else 1.0)

@@ -1,0 +1,296 @@
+"""Plain fp64 CPU oracle for exact scaled-dot-product attention, forward and backward.
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or run anything in this
+package. The product path (``libfa`` and its Python binding) never calls it,
+and it shares no code, table or helper with that path.
+
+Sources, cited by page title and section:
+
+* [PN] "FlashAttention: Faster Attention Without Dropping a Single Interaction"
+  (awesome.papernotes.org). Method Deep Dive: Key design 1 (definition of S, P,
+  O), Key design 2 (mergeable (m, l, O) state and the saved-state table with
+  L = m + log l), Key design 3 (backward by recomputation, D_i and dS).
+* [RX] "FlashAttention: The Algorithm That Beat the Memory Wall"
+  (repo-explainer.com). "A Tile, a Register File, and a Trick Called Online
+  Softmax" (the per-tile loop) and "Varlen Is the Quiet Superpower" (packed
+  sequences).
+* [GL] "FlashAttention" glossary (inferensys.com): ALiBi and multi-query
+  variants are named, without formulas.
+
+What is computed (the plain definition, [PN] Key design 1): for each batch
+entry or packed sequence b and query head h, with kv head g = floor(h / G),
+G = H / Hkv, and positions i, j in [0, n):
+
+    S_ij = scale * <q_i, k_j> + beta_ij
+    P    = row-wise softmax of S          (entries with j > i removed if causal)
+    O    = P V,    lse_i = m_i + ln(sum_j exp(S_ij - m_i)),  m_i = max_j S_ij
+
+The method is exact in real arithmetic, so the oracle is that definition:
+two-pass softmax over a materialised S, no blocking, every value in fp64.
+
+Readings taken where the pages are silent or garbled (each is also listed in
+the design notes of the repository):
+
+1. Scale. The definition divides by sqrt(d); the printed loops omit it. S
+   carries an explicit ``scale`` (default 1/sqrt(d)) and, by the chain rule,
+   dQ and dK carry the same factor.
+2. l is the running sum of exponentials; the statistic kept for backward is
+   the natural-log L = m + ln l.
+3. Causal masking keeps key j <= query i (query and key lengths are equal).
+4. ALiBi (named only): beta_ij = -slope_h * |i - j|, added after scaling and
+   before the mask; under causal masking this is -slope_h * (i - j).
+5. GQA / MQA (named only): consecutive groups, kv head = floor(h / G); dK and
+   dV of a kv head are the sums over its G query heads.
+6. Varlen: packed rows [total, heads, d] with ``cu_seqlens`` [B+1]; each
+   sequence is an independent attention problem with local positions. The
+   statistic ``lse`` is laid out [B, H, Nmax] for both dense and packed
+   inputs; entries past a sequence's length are NaN here.
+7. A masked score contributes exactly zero; exp(-inf - (-inf)) never occurs in
+   the two-pass form because every causal row keeps its diagonal.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "attention_fwd",
+    "attention_bwd",
+    "head_fwd",
+    "head_bwd",
+    "head_rows_fwd",
+    "online_head_fwd",
+    "brute_fwd",
+]
+
+
+def _f64(x) -> np.ndarray:
+    """Exact fp64 copy of an array (torch CPU tensors, bf16 included, or numpy)."""
+    if hasattr(x, "detach"):  # torch tensor; bf16 has no numpy dtype
+        import torch  # local: the oracle itself only needs numpy
+
+        return x.detach().to("cpu", torch.float64).numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def _bias(rows: np.ndarray, n_keys: int, slope: float) -> np.ndarray:
+    """ALiBi bias -slope * |i - j| for query positions ``rows`` and keys [0, n_keys) (reading 4)."""
+    j = np.arange(n_keys, dtype=np.float64)
+    return -slope * np.abs(rows.astype(np.float64)[:, None] - j[None, :])
+
+
+def _scores(qh, kh, scale, causal, slope, rows=None):
+    """S = scale * Q K^T + beta with the causal entries set to -inf ([PN] Key design 1)."""
+    n = kh.shape[0]
+    if rows is None:
+        rows = np.arange(qh.shape[0])
+    s = scale * (qh @ kh.T)
+    if slope is not None:
+        s = s + _bias(rows, n, slope)
+    if causal:
+        s = np.where(np.arange(n)[None, :] > rows[:, None], -np.inf, s)
+    return s
+
+
+def _softmax_rows(s):
+    """Two-pass softmax of each row of S; also returns lse = m + ln(sum exp(S - m)) ([PN] saved-state table)."""
+    m = s.max(axis=1)
+    e = np.exp(s - m[:, None])
+    ell = e.sum(axis=1)
+    return e / ell[:, None], m + np.log(ell)
+
+
+def head_fwd(qh, kh, vh, scale, causal=False, slope=None):
+    """One (sequence, head): O = softmax(S) V and lse. Arrays are [n, d] fp64."""
+    p, lse = _softmax_rows(_scores(qh, kh, scale, causal, slope))
+    return p @ vh, lse
+
+
+def head_rows_fwd(qh, kh, vh, rows, scale, causal=False, slope=None):
+    """O and lse for the query positions ``rows`` only (the full K and V are used).
+
+    Row i of the output depends only on q_i, K and V, so a sample of rows can be
+    checked at sizes where a whole N x N matrix per head would be wasteful.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    p, lse = _softmax_rows(_scores(qh[rows], kh, scale, causal, slope, rows=rows))
+    return p @ vh, lse
+
+
+def head_bwd(qh, kh, vh, doh, scale, causal=False, slope=None):
+    """Gradients of sum(O * dO) for one (sequence, head), by recomputing P ([PN] Key design 3).
+
+    D_i is taken from its definition sum_j P_ij dP_ij; the identity D_i = dO_i . O_i
+    stated on the page is checked by the tests, not assumed here.
+    """
+    p, _ = _softmax_rows(_scores(qh, kh, scale, causal, slope))
+    dv = p.T @ doh
+    dp = doh @ vh.T
+    dcorr = (p * dp).sum(axis=1)
+    ds = p * (dp - dcorr[:, None])
+    dq = scale * (ds @ kh)
+    dk = scale * (ds.T @ qh)
+    return dq, dk, dv
+
+
+def _sequences(q, cu_seqlens):
+    """Yield (b, row slice, n) for dense [B, N, H, d] or packed [T, H, d] inputs."""
+    if cu_seqlens is None:
+        B, N = q.shape[0], q.shape[1]
+        for b in range(B):
+            yield b, (b, slice(0, N)), N
+    else:
+        cu = [int(c) for c in np.asarray(cu_seqlens).reshape(-1)]
+        for b in range(len(cu) - 1):
+            yield b, (slice(cu[b], cu[b + 1]),), cu[b + 1] - cu[b]
+
+
+def _heads(q, k):
+    H, Hkv = q.shape[-2], k.shape[-2]
+    if H % Hkv:
+        raise ValueError("query heads must be a multiple of kv heads")
+    return H, Hkv, H // Hkv
+
+
+def attention_fwd(q, k, v, scale=None, causal=False, alibi_slopes=None, cu_seqlens=None):
+    """Exact attention forward in fp64.
+
+    Dense: q [B, N, H, d], k and v [B, N, Hkv, d]. Packed (``cu_seqlens`` given):
+    q [T, H, d], k and v [T, Hkv, d]. Returns (o, lse): o in q's layout, lse
+    [B, H, Nmax] (NaN past each sequence's end).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    H, Hkv, G = _heads(q, k)
+    d = q.shape[-1]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    slopes = None if alibi_slopes is None else _f64(alibi_slopes).reshape(-1)
+    seqs = list(_sequences(q, cu_seqlens))
+    nmax = max([n for _, _, n in seqs] + [0])
+    o = np.zeros(q.shape[:-1] + v.shape[-1:])
+    lse = np.full((len(seqs), H, nmax), np.nan)
+    for b, idx, n in seqs:
+        if n == 0:
+            continue
+        for h in range(H):
+            g = h // G
+            oh, lh = head_fwd(q[idx][:, h], k[idx][:, g], v[idx][:, g], scale, causal,
+                              None if slopes is None else slopes[h])
+            o[idx + (h,)] = oh
+            lse[b, h, :n] = lh
+    return o, lse
+
+
+def attention_bwd(q, k, v, do, scale=None, causal=False, alibi_slopes=None, cu_seqlens=None):
+    """Exact attention backward in fp64: (dq, dk, dv) of the loss sum(O * dO).
+
+    Layouts as in :func:`attention_fwd`. dk and dv of a kv head sum over its
+    G query heads (reading 5); ALiBi slopes are constants and get no gradient.
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    H, Hkv, G = _heads(q, k)
+    d = q.shape[-1]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    slopes = None if alibi_slopes is None else _f64(alibi_slopes).reshape(-1)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b, idx, n in _sequences(q, cu_seqlens):
+        if n == 0:
+            continue
+        for h in range(H):
+            g = h // G
+            gq, gk, gv = head_bwd(q[idx][:, h], k[idx][:, g], v[idx][:, g], do[idx][:, h], scale,
+                                  causal, None if slopes is None else slopes[h])
+            dq[idx + (h,)] = gq
+            dk[idx + (g,)] += gk
+            dv[idx + (g,)] += gv
+    return dq, dk, dv
+
+
+def online_head_fwd(qh, kh, vh, scale, bounds, causal=False, slope=None):
+    """The blockwise online-softmax recurrence for one (sequence, head), in fp64.
+
+    Follows the merge of [PN] Key design 2 (also the per-tile loop of [RX]): keys
+    are visited in the tiles [bounds[t], bounds[t+1]); each tile's scores give a
+    tile maximum and local exponential sum, and the running (m, l, O) is rescaled
+    to the common maximum m' = max(m, m~):
+
+        l' = e^(m - m') l + e^(m~ - m') l~
+        O' = (e^(m - m') l O + e^(m~ - m') P~ V_j) / l'
+
+    State starts at m = -inf, l = 0, O = 0. A row whose tile is entirely masked
+    keeps its state unchanged (its tile contributes exactly zero). Returns (O, lse)
+    with lse = m + ln l. This is a second, independent route to the same values
+    as :func:`head_fwd`; by Theorem 1 the two agree up to rounding.
+    """
+    n_q = qh.shape[0]
+    rows = np.arange(n_q)
+    m = np.full(n_q, -np.inf)
+    ell = np.zeros(n_q)
+    o = np.zeros((n_q, vh.shape[1]))
+    for lo, hi in zip(bounds[:-1], bounds[1:]):
+        if hi <= lo:
+            continue
+        cols = np.arange(lo, hi)
+        s = scale * (qh @ kh[lo:hi].T)
+        if slope is not None:
+            s = s - slope * np.abs(rows[:, None] - cols[None, :]).astype(np.float64)
+        if causal:
+            s = np.where(cols[None, :] > rows[:, None], -np.inf, s)
+        live = np.isfinite(s).any(axis=1)
+        m_t = np.where(live, s.max(axis=1), -np.inf)
+        p_t = np.where(live[:, None], np.exp(s - np.where(live, m_t, 0.0)[:, None]), 0.0)
+        l_t = p_t.sum(axis=1)
+        m_new = np.maximum(m, m_t)
+        a_old = np.where(np.isfinite(m), np.exp(m - m_new), 0.0)
+        a_new = np.where(live, np.exp(m_t - m_new), 0.0)
+        l_new = a_old * ell + a_new * l_t
+        upd = l_new > 0
+        num = (a_old * ell)[:, None] * o + a_new[:, None] * (p_t @ vh[lo:hi])
+        o = np.where(upd[:, None], num / np.where(upd, l_new, 1.0)[:, None], o)
+        m, ell = np.where(upd, m_new, m), np.where(upd, l_new, ell)
+    return o, m + np.log(ell)
+
+
+def brute_fwd(q, k, v, scale=None, causal=False, alibi_slopes=None, cu_seqlens=None):
+    """Scalar-loop attention with textbook softmax, for tiny inputs (N <= 8).
+
+    Pure Python: nested lists, ``math.exp`` and running sums, no BLAS and no
+    max subtraction. Masked keys are left out of the sums instead of being set to
+    -inf. Same layouts and return values as :func:`attention_fwd`.
+    """
+    qa, ka, va = _f64(q), _f64(k), _f64(v)
+    H, Hkv = qa.shape[-2], ka.shape[-2]
+    G = H // Hkv
+    d = qa.shape[-1]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    slopes = None if alibi_slopes is None else [float(x) for x in _f64(alibi_slopes).reshape(-1)]
+    seqs = list(_sequences(qa, cu_seqlens))
+    nmax = max([n for _, _, n in seqs] + [0])
+    o = np.zeros(qa.shape[:-1] + va.shape[-1:])
+    lse = np.full((len(seqs), H, nmax), np.nan)
+    for b, idx, n in seqs:
+        qs, ks, vs = qa[idx].tolist(), ka[idx].tolist(), va[idx].tolist()
+        o_seq = o[idx]  # basic slicing: a view into o
+        for h in range(H):
+            g = h // G
+            for i in range(n):
+                keys = range(i + 1) if causal else range(n)
+                w = []
+                for j in keys:
+                    s = 0.0
+                    for c in range(d):
+                        s += qs[i][h][c] * ks[j][g][c]
+                    s *= scale
+                    if slopes is not None:
+                        s -= slopes[h] * abs(i - j)
+                    w.append(math.exp(s))
+                z = sum(w)
+                out = [0.0] * len(vs[0][g]) if n else []
+                for wj, j in zip(w, keys):
+                    for c in range(len(out)):
+                        out[c] += wj / z * vs[j][g][c]
+                o_seq[i, h] = out
+                lse[b, h, i] = math.log(z)
+    return o, lse
