@@ -1,0 +1,285 @@
+#!/usr/bin/env python3
+"""Attention forward+backward throughput on one MI355X, reported as one JSON line.
+
+A step is one pass of the whole path over one batch: ``fa_fwd`` (O and lse)
+then ``fa_bwd`` (D pre-pass, dK/dV, dQ), on inputs already resident in device
+memory. The default workload is the long-context causal case the headline
+metric is quoted on: B=1, H=32, N=16384, d=128, bf16, causal, synthetic N(0, 1/2)
+inputs. Work is counted as dense attention FLOPs: 4*B*H*N^2*d forward, halved
+for causal, and 2.5x that for backward.
+
+Besides the step rate the line carries:
+  * ``kernels``: each kernel timed alone with HIP events on the launch stream
+    (average over --kernel-reps launches) against its algorithmic work;
+  * ``roofline``: the kernel that takes longest per step, against the MI355X
+    dense bf16 MFMA peak (or HBM bandwidth for the memory-bound pre-pass), with
+    HBM traffic from the committed rocprofv3 counter summary when that summary
+    was taken on the current kernel sources (else null);
+  * ``cpu_baseline``: the fp64 CPU oracle timed on this host on one
+    (batch, head) slice of the same workload (forward + backward);
+  * ``memory``: device bytes the step allocates versus a materialised-score
+    baseline that stores S and P.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd/bwd TFLOP/s, bf16 causal d=128, and % of MI355X MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 4096 dense bf16 FLOP/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+CSRC = os.path.join(ROOT, "exact_io_aware_43_amd", "csrc")
+KERNEL_SOURCES = {
+    "fwd": ["fa_fwd.hip", "fa_device.hpp", "fa_internal.hpp"],
+    "bwd_dsum": ["fa_bwd.hip", "fa_device.hpp", "fa_internal.hpp"],
+    "bwd_dkdv": ["fa_bwd.hip", "fa_device.hpp", "fa_internal.hpp"],
+    "bwd_dq": ["fa_bwd.hip", "fa_device.hpp", "fa_internal.hpp"],
+}
+
+
+def source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="long_causal")
+    ap.add_argument("--kernel-reps", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=0)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the attention kernels run on a single device and this "
+              "build has no multi-GPU path (no collectives, no sharding); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import exact_io_aware_43_amd as fa
+    from exact_io_aware_43_amd.workloads import WORKLOADS, flops, make_inputs, seq_lengths
+
+    w = WORKLOADS[args.workload]
+    if not w.backward:
+        raise SystemExit(f"workload {w.name} has no backward pass; the step is forward+backward")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] workload {w}", file=sys.stderr, flush=True)
+
+    inp = make_inputs(w, args.seed, with_grad=True)
+    q, k, v, do = (inp[x].to(dev) for x in ("q", "k", "v", "do"))
+    cu = inp["cu_seqlens"].to(dev) if inp["cu_seqlens"] is not None else None
+    slopes = inp["alibi_slopes"].to(dev) if inp["alibi_slopes"] is not None else None
+    lens = seq_lengths(inp, w)
+    B, H, Hkv, N, d = w.B, w.H, w.Hkv, inp["max_seqlen"], w.d
+    dt = {"bf16": fa.FA_BF16, "fp16": fa.FA_FP16}[w.dtype]
+    scale = inp["scale"]
+    causal = int(w.causal)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    torch.cuda.synchronize()
+    mem0 = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws_bytes = fa.fa_bwd_workspace_size(B, H, Hkv, N, d, causal, int(cu is not None), dt)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    P = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+
+    def fwd():
+        st = fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, Hkv, N, d,
+                       scale, causal, P(slopes), P(cu), dt, sh)
+        if st:
+            raise fa.FaError(st)
+
+    def bwd(stages=fa.FA_BWD_ALL):
+        st = fa.fa_bwd_stages(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                              lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, N, d, scale,
+                              causal, P(slopes), P(cu), dt, ws.data_ptr(), ws_bytes, stages, sh)
+        if st:
+            raise fa.FaError(st)
+
+    def step():
+        fwd()
+        bwd()
+
+    step()
+    torch.cuda.synchronize()
+    lib_bytes = torch.cuda.max_memory_allocated() - mem0
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    print(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step (wall {wall:.2f} s)", file=sys.stderr, flush=True)
+
+    f_fwd = flops(w, lens)
+    f_bwd = flops(w, lens, backward=True)
+    value = (f_fwd + f_bwd) / (ms * 1e-3) / 1e12
+
+    # ---- each kernel alone, HIP events on the launch stream
+    def time_launches(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.kernel_reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.kernel_reps
+
+    row_bytes = 2 if w.dtype in ("bf16", "fp16") else 4
+    T = sum(lens)
+    dsum_bytes = 2 * T * H * d * row_bytes + 4 * T * H
+    kernels = {
+        "fwd": dict(ms=time_launches(fwd), work=f_fwd, bound="mfma"),
+        "bwd_dsum": dict(ms=time_launches(lambda: bwd(fa.FA_BWD_PREP)), work=dsum_bytes, bound="hbm"),
+        "bwd_dkdv": dict(ms=time_launches(lambda: bwd(fa.FA_BWD_DKDV)), work=2.0 * f_fwd, bound="mfma"),
+        "bwd_dq": dict(ms=time_launches(lambda: bwd(fa.FA_BWD_DQ)), work=0.5 * f_fwd, bound="mfma"),
+    }
+    for name, kr in kernels.items():
+        if kr["bound"] == "mfma":
+            kr["achieved"] = kr["work"] / (kr["ms"] * 1e-3) / 1e12
+            kr["unit"] = "TFLOP/s"
+            kr["frac"] = kr["achieved"] / PEAK_BF16_TFLOPS
+        else:
+            kr["achieved"] = kr["work"] / (kr["ms"] * 1e-3) / 1e9
+            kr["unit"] = "GB/s"
+            kr["frac"] = kr["achieved"] / PEAK_HBM_GBS
+    dom = max(kernels, key=lambda n: kernels[n]["ms"])
+    kd = kernels[dom]
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f).get(w.name, {}).get(dom)
+        if tr and tr.get("source_hash") == source_hash(dom):
+            traffic = tr["bytes_per_launch"]
+
+    roofline = {
+        "kernel": dom,
+        "bound": kd["bound"],
+        "achieved": round(kd["achieved"], 2),
+        "peak": PEAK_BF16_TFLOPS if kd["bound"] == "mfma" else PEAK_HBM_GBS,
+        "unit": kd["unit"],
+        "frac": round(kd["frac"], 4),
+        "traffic": traffic,
+        "avg_launch_ms": round(kd["ms"], 4),
+        "work_per_launch": kd["work"],
+    }
+
+    # ---- memory versus a materialised-score baseline (S and P stored in the input type)
+    nn = sum(float(n) * n for n in lens) * H
+    memory = {
+        "libfa_step_bytes": int(lib_bytes),
+        "materialised_sp_bytes": int(2 * nn * row_bytes),
+        "ratio": round(2 * nn * row_bytes / max(lib_bytes, 1), 1),
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, inp, lens)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "Hkv": Hkv, "N": N, "d": d, "causal": bool(w.causal),
+                   "alibi": bool(w.alibi), "pass": "forward+backward"},
+        "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "fwd_tflops": round(f_fwd / (kernels["fwd"]["ms"] * 1e-3) / 1e12, 2),
+        "bwd_tflops": round(f_bwd / (sum(kernels[n]["ms"] for n in ("bwd_dsum", "bwd_dkdv", "bwd_dq")) * 1e-3)
+                            / 1e12, 2),
+        "kernels": {n: {"ms": round(kr["ms"], 4), "achieved": round(kr["achieved"], 2), "unit": kr["unit"],
+                        "frac": round(kr["frac"], 4)} for n, kr in kernels.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "memory": memory,
+    }
+    out["fwd_frac_of_peak"] = round(out["fwd_tflops"] / PEAK_BF16_TFLOPS, 4)
+    out["bwd_frac_of_peak"] = round(out["bwd_tflops"] / PEAK_BF16_TFLOPS, 4)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(w, inp, lens):
+    """The fp64 oracle, as it is, on one (sequence 0, head 0) slice: forward + backward."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle.attention as OA
+    from exact_io_aware_43_amd.workloads import flops
+
+    n = lens[0]
+    G = w.H // w.Hkv
+    sl = (0, slice(0, n)) if inp["cu_seqlens"] is None else (slice(0, n),)
+    q = OA._f64(inp["q"][sl][:, 0])
+    k = OA._f64(inp["k"][sl][:, 0 // G])
+    v = OA._f64(inp["v"][sl][:, 0 // G])
+    do = OA._f64(inp["do"][sl][:, 0])
+    slope = None if inp["alibi_slopes"] is None else float(inp["alibi_slopes"][0])
+    print(f"[bench] cpu baseline: oracle fwd+bwd on one head, n={n}", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    OA.head_fwd(q, k, v, inp["scale"], w.causal, slope)
+    OA.head_bwd(q, k, v, do, inp["scale"], w.causal, slope)
+    t = time.perf_counter() - t0
+    one = w.with_(B=1, H=1, Hkv=1)
+    work = flops(one, [n]) + flops(one, [n], backward=True)
+    blas = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+    return {
+        "value": round(work / t / 1e12, 5),
+        "unit": "TFLOP/s",
+        "cores": int(max(blas) if blas else 1),
+        "kind": "oracle",
+        "sample": f"one (batch 0, head 0) slice of {w.name}: N={n}, d={w.d}, causal={w.causal}; "
+                  f"fp64 numpy forward + backward, {t:.1f} s",
+        "host_cpus_available": len(os.sched_getaffinity(0)),
+        "seconds": round(t, 2),
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,29 @@
+"""libfa: exact tiled attention (FlashAttention forward and backward) for MI355X / gfx950.
+
+The compute lives in ``libfa.so`` (hand-written HIP kernels behind the C ABI of
+``include/fa.h``); this package is its ctypes binding plus seeded workload
+generators.
+"""
+
+from ._binding import (  # noqa: F401
+    FA_BF16,
+    FA_BWD_ALL,
+    FA_BWD_DKDV,
+    FA_BWD_DQ,
+    FA_BWD_PREP,
+    FA_FP16,
+    FA_FP32,
+    FA_OK,
+    FaError,
+    FlashAttnFn,
+    LIB_PATH,
+    attention,
+    attention_bwd,
+    fa_bwd,
+    fa_bwd_stages,
+    fa_bwd_workspace_size,
+    fa_fwd,
+    fa_strerror,
+    fa_version,
+    lib,
+)

@@ -1,0 +1,140 @@
+// C-ABI entry points of libfa (declared in include/fa.h): argument checks,
+// selection of the compiled kernel instance, and the launches. Every check runs
+// before the first launch, so a rejected call enqueues and writes nothing.
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/fa.h"
+#include "fa_internal.hpp"
+
+namespace {
+
+constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_dtype(int dt) { return dt == FA_FP32 || dt == FA_FP16 || dt == FA_BF16; }
+
+// Checks shared by forward and backward. Returns FA_OK or the status to report.
+int check_common(int B, int H, int Hkv, int N, int d, float scale, int causal, int dtype) {
+    if (B <= 0 || H <= 0 || Hkv <= 0 || N <= 0 || d <= 0) return FA_ERR_INVALID_ARG;
+    if (H % Hkv != 0) return FA_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
+    if (!valid_dtype(dtype)) return FA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    // element offsets of one row-block are computed in 64 bits, but per-head row
+    // counts, lse indices and grid sizes are 32-bit
+    const long long rows = (long long)B * N;
+    if (rows * H >= (1ll << 31) || rows * Hkv >= (1ll << 31)) return FA_ERR_INVALID_ARG;
+    return FA_OK;
+}
+
+fa::Args make_args(const void* q, const void* k, const void* v, int B, int H, int Hkv, int N, float scale,
+                   const float* slopes, const int* cu) {
+    fa::Args a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.slopes = slopes;
+    a.cu = cu;
+    a.B = B;
+    a.H = H;
+    a.Hkv = Hkv;
+    a.N = N;
+    a.G = H / Hkv;
+    a.scale = scale;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    return a;
+}
+
+size_t workspace_bytes_for(int B, int H, int N) {
+    const size_t rows = (size_t)B * (size_t)H * (size_t)N;
+    return (rows * sizeof(float) + 255) & ~(size_t)255;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N, int d,
+           float scale, int causal, const float* alibi_slopes, const int* cu_seqlens, fa_dtype dtype,
+           void* stream) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+    int st = check_common(B, H, Hkv, N, d, scale, causal, (int)dtype);
+    if (st != FA_OK) return st;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+        return FA_ERR_INVALID_ARG;
+    if ((alibi_slopes && !aligned16(alibi_slopes)) || (cu_seqlens && !aligned16(cu_seqlens)))
+        return FA_ERR_INVALID_ARG;
+
+    fa::Args a = make_args(q, k, v, B, H, Hkv, N, scale, alibi_slopes, cu_seqlens);
+    a.out = o;
+    a.lse = lse;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (dtype == FA_FP32)
+        e = fa::launch_fwd_f32(a, d, causal != 0, alibi_slopes != nullptr, s);
+    else
+        e = fa::launch_fwd_mfma(a, (int)dtype, d, causal != 0, alibi_slopes != nullptr, s);
+    return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+size_t fa_bwd_workspace_size(int B, int H, int Hkv, int N, int d, int causal, int varlen, fa_dtype dtype) {
+    (void)varlen;
+    if (check_common(B, H, Hkv, N, d, 1.0f, causal, (int)dtype) != FA_OK) return 0;
+    return workspace_bytes_for(B, H, N);
+}
+
+int fa_bwd_stages(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                  void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d, float scale, int causal,
+                  const float* alibi_slopes, const int* cu_seqlens, fa_dtype dtype, void* workspace,
+                  size_t workspace_bytes, unsigned stages, void* stream) {
+    if (stages == 0 || (stages & ~(unsigned)FA_BWD_ALL) != 0) return FA_ERR_INVALID_ARG;
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
+    int st = check_common(B, H, Hkv, N, d, scale, causal, (int)dtype);
+    if (st != FA_OK) return st;
+    if (dtype == FA_FP32) return FA_ERR_UNSUPPORTED;
+    const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return FA_ERR_INVALID_ARG;
+    if ((alibi_slopes && !aligned16(alibi_slopes)) || (cu_seqlens && !aligned16(cu_seqlens)))
+        return FA_ERR_INVALID_ARG;
+    if (!workspace || !aligned16(workspace) || workspace_bytes < workspace_bytes_for(B, H, N))
+        return FA_ERR_WORKSPACE;
+
+    fa::Args a = make_args(q, k, v, B, H, Hkv, N, scale, alibi_slopes, cu_seqlens);
+    a.o = o;
+    a.dout = dout;
+    a.lse_in = lse;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.dsum = reinterpret_cast<float*>(workspace);
+    hipError_t e = fa::launch_bwd(a, (int)dtype, d, causal != 0, alibi_slopes != nullptr, stages,
+                                  reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse, void* dq,
+           void* dk, void* dv, int B, int H, int Hkv, int N, int d, float scale, int causal,
+           const float* alibi_slopes, const int* cu_seqlens, fa_dtype dtype, void* workspace,
+           size_t workspace_bytes, void* stream) {
+    return fa_bwd_stages(q, k, v, o, dout, lse, dq, dk, dv, B, H, Hkv, N, d, scale, causal, alibi_slopes,
+                         cu_seqlens, dtype, workspace, workspace_bytes, FA_BWD_ALL, stream);
+}
+
+const char* fa_strerror(int status) {
+    switch (status) {
+        case FA_OK: return "success";
+        case FA_ERR_INVALID_ARG: return "invalid argument";
+        case FA_ERR_UNSUPPORTED: return "unsupported configuration (head dim must be 64 or 128; fp32 is forward only)";
+        case FA_ERR_WORKSPACE: return "workspace missing, misaligned or smaller than fa_bwd_workspace_size()";
+        case FA_ERR_LAUNCH: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+int fa_version(void) { return kVersion; }
+
+}  // extern "C"

@@ -1,0 +1,501 @@
+// Backward attention for 16-bit inputs on gfx950 MFMA.
+//
+// Method: "FlashAttention: Faster Attention Without Dropping a Single
+// Interaction", Method Deep Dive, Key design 3. Nothing quadratic is read back:
+// every score tile is rebuilt from Q, K and the saved L = m + ln(l)
+// (P_ij = exp(S_ij - L_i)), and the softmax backward uses
+// D_i = dO_i . O_i, so dS = P o (dP - D). Three launches run in stream order:
+//
+//   1. bwd_dsum:  D_i = sum_c dO_ic O_ic in fp32 (memory bound, one pass over
+//                 O and dO; O is the stored forward output).
+//   2. bwd_dkdv:  one workgroup per (128-key tile, kv head, sequence). K and V
+//                 of the tile stay in registers; the workgroup walks every
+//                 query head of the kv group and every query tile that can see
+//                 the keys, accumulating dV = P^T dO and dK = dS^T Q in
+//                 registers. No atomics: each dK / dV row has one owner, and
+//                 the GQA group sum happens in the accumulators.
+//   3. bwd_dq:    one workgroup per (128-query tile, query head, sequence); Q
+//                 and dO stay in registers and K, V tiles stream through LDS;
+//                 dQ = dS K is accumulated in registers.
+// Splitting dQ from dK/dV recomputes S and dP twice but needs no atomic
+// reduction, so the result is bitwise reproducible (the deterministic option
+// the page's Limitations section discusses).
+//
+// Register orientation follows the MFMA layout notes in fa_device.hpp. The
+// dK/dV kernel computes S = Q K^T (queries x keys) so that each lane owns one
+// key column, and accumulates dV^T = dO^T P and dK^T = Q^T dS with P and dS as
+// B operands taken straight from the accumulators. The dQ kernel computes
+// S^T = K Q^T so that each lane owns one query, and accumulates
+// dQ^T = K^T dS^T. Transposed operands (dO^T, Q^T, K^T) are written to LDS
+// transposed by the staging threads.
+#include "fa_device.hpp"
+
+namespace fa {
+namespace {
+
+constexpr int NT = 256;
+
+// ---------------------------------------------------------------- D = dO . O
+template <typename T, int D>
+__global__ __launch_bounds__(NT) void bwd_dsum_kernel(Args a) {
+    constexpr int LPR = D / 8;        // lanes per (row, head)
+    constexpr int RPB = NT / LPR;     // rows per block
+    const int h = blockIdx.x, b = blockIdx.y;
+    int row0, len;
+    seq_bounds(a, b, row0, len);
+    const int i = blockIdx.z * RPB + threadIdx.x / LPR;
+    const int part = threadIdx.x % LPR;
+    float acc = 0.f;
+    if (i < len) {
+        const size_t off = ((size_t)(row0 + i) * a.H + h) * D + part * 8;
+        const uint4 uo = ld_g16(reinterpret_cast<const T*>(a.o) + off);
+        const uint4 ud = ld_g16(reinterpret_cast<const T*>(a.dout) + off);
+        const V8<T> vo = as_v8<T>(uo), vd = as_v8<T>(ud);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = fmaf((float)vo[e], (float)vd[e], acc);
+    }
+#pragma unroll
+    for (int w = LPR / 2; w >= 1; w >>= 1) acc += __shfl_xor(acc, w);
+    if (i < len && part == 0) a.dsum[((size_t)b * a.H + h) * a.N + i] = acc;
+}
+
+// ---------------------------------------------------------------- dK, dV
+constexpr int KV_BK = 128;  // keys per workgroup (32 per wave)
+constexpr int KV_BQ = 32;   // queries per step
+
+template <int D>
+struct KvLds {
+    static constexpr int RP = D + 8;          // row-major pitch (elements)
+    static constexpr int TP = KV_BQ + 4;      // transposed pitch: 18 dwords, conflict-free b64 reads
+    static constexpr int ROW = KV_BQ * RP;    // one row-major tile
+    static constexpr int TR = D * TP;         // one transposed tile
+    // Q, Q^T, dO, dO^T, then lse*log2e and D (fp32, KV_BQ each)
+    static constexpr int Q_OFF = 0, QT_OFF = ROW, DO_OFF = ROW + TR, DOT_OFF = 2 * ROW + TR;
+    static constexpr int VEC_OFF = 2 * ROW + 2 * TR;  // element offset of the fp32 vectors
+    static constexpr int STAGE = VEC_OFF + 2 * KV_BQ * 2;  // in 16-bit elements
+    static constexpr int GROUPS = (KV_BQ / 4) * (D / 8);    // (4 rows x 8 dims) groups per tensor
+    static constexpr int G_PER_THREAD = (2 * GROUPS + NT - 1) / NT;
+};
+
+template <typename T, int D, bool CAUSAL, bool ALIBI>
+__global__ __launch_bounds__(NT) void bwd_dkdv_kernel(Args a) {
+    using L = KvLds<D>;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * L::STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 31, kg = lane >> 5;
+    const int g = blockIdx.x, b = blockIdx.y;
+    const int kt = blockIdx.z;  // low key tiles see the most queries: dispatched first
+    int row0, len;
+    seq_bounds(a, b, row0, len);
+    const int k0 = kt * KV_BK;
+    if (k0 >= len) return;
+
+    const size_t ldq = (size_t)a.H * D, ldk = (size_t)a.Hkv * D;
+    const int kw = k0 + wave * 32;   // first key of this wave
+    const int key = kw + col;        // this lane's key (column of S)
+
+    // K^T and V^T fragments as B operands: lane holds key `key`, dims 16*kk + 8*kg + 0..7.
+    V8<T> kf[D / 16], vf[D / 16];
+    {
+        const T* Kp = reinterpret_cast<const T*>(a.k) + (size_t)(row0 + key) * ldk + (size_t)g * D;
+        const T* Vp = reinterpret_cast<const T*>(a.v) + (size_t)(row0 + key) * ldk + (size_t)g * D;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            uint4 uk = make_uint4(0, 0, 0, 0), uv = uk;
+            if (key < len) {
+                uk = ld_g16(Kp + 16 * kk + 8 * kg);
+                uv = ld_g16(Vp + 16 * kk + 8 * kg);
+            }
+            kf[kk] = as_v8<T>(uk);
+            vf[kk] = as_v8<T>(uv);
+        }
+    }
+
+    f32x16 dkacc[D / 32], dvacc[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+        dkacc[db] = f32x16{};
+        dvacc[db] = f32x16{};
+    }
+
+    // Query tiles that can see this key tile: all of them, or (causal) those
+    // ending at or after k0.
+    const int qt0 = CAUSAL ? k0 / KV_BQ : 0;
+    const int nqt = (len + KV_BQ - 1) / KV_BQ;
+    const int per_head = nqt - qt0;
+    const int steps = a.G * per_head;
+    const float c2 = a.scale_log2;
+
+    uint4 greg[L::G_PER_THREAD][4];
+    float vec_reg = 0.f;
+    auto step_coords = [&](int st, int& h, int& q0) {
+        const int hh = st / per_head;
+        h = g * a.G + hh;
+        q0 = (qt0 + st - hh * per_head) * KV_BQ;
+    };
+    auto gload = [&](int st) {
+        int h, q0;
+        step_coords(st, h, q0);
+#pragma unroll
+        for (int r = 0; r < L::G_PER_THREAD; ++r) {
+            const int gi = tid + r * NT;
+            const int tsel = gi / L::GROUPS;  // 0: Q, 1: dO
+            const int gl = gi % L::GROUPS;
+            const int dc = gl % (D / 8), rq = gl / (D / 8);
+            const T* base = reinterpret_cast<const T*>(tsel == 0 ? a.q : a.dout) + (size_t)h * D + dc * 8;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int qi = q0 + 4 * rq + e;
+                greg[r][e] = (gi < 2 * L::GROUPS && qi < len) ? ld_g16(base + (size_t)(row0 + qi) * ldq)
+                                                              : make_uint4(0, 0, 0, 0);
+            }
+        }
+        if (tid < 2 * KV_BQ) {
+            const int qi = q0 + (tid % KV_BQ);
+            const size_t idx = ((size_t)b * a.H + h) * a.N + qi;
+            if (tid < KV_BQ)
+                vec_reg = (qi < len) ? a.lse_in[idx] * kLog2e : INFINITY;  // P = 0 on padding rows
+            else
+                vec_reg = (qi < len) ? a.dsum[idx] : 0.f;
+        }
+    };
+    auto swrite = [&](int stage) {
+        uint16_t* S = smem + stage * L::STAGE;
+#pragma unroll
+        for (int r = 0; r < L::G_PER_THREAD; ++r) {
+            const int gi = tid + r * NT;
+            if (gi < 2 * L::GROUPS) {
+                const int tsel = gi / L::GROUPS;
+                const int gl = gi % L::GROUPS;
+                const int dc = gl % (D / 8), rq = gl / (D / 8);
+                uint16_t* rm = S + (tsel == 0 ? L::Q_OFF : L::DO_OFF);
+                uint16_t* tr = S + (tsel == 0 ? L::QT_OFF : L::DOT_OFF);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) st_s16(rm + (4 * rq + e) * L::RP + dc * 8, greg[r][e]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t lo = half_of(greg[r][0], e) | (half_of(greg[r][1], e) << 16);
+                    const uint32_t hi = half_of(greg[r][2], e) | (half_of(greg[r][3], e) << 16);
+                    st_s8(tr + (dc * 8 + e) * L::TP + 4 * rq, make_uint2(lo, hi));
+                }
+            }
+        }
+        if (tid < 2 * KV_BQ) reinterpret_cast<float*>(S + L::VEC_OFF)[tid] = vec_reg;
+    };
+
+    if (steps > 0) {
+        gload(0);
+        swrite(0);
+    }
+    __syncthreads();
+
+    for (int st = 0; st < steps; ++st) {
+        const int stage = st & 1;
+        if (st + 1 < steps) gload(st + 1);
+        int h, q0;
+        step_coords(st, h, q0);
+        // wave-uniform skips: keys past the sequence end, or (causal) a query
+        // tile entirely before this wave's first key
+        const bool active = (kw < len) && (!CAUSAL || q0 + KV_BQ - 1 >= kw);
+        if (active) {
+            const uint16_t* S = smem + stage * L::STAGE;
+            const float* lse2 = reinterpret_cast<const float*>(S + L::VEC_OFF);
+            const float* dsv = lse2 + KV_BQ;
+
+            // S = Q K^T and dP = dO V^T: queries (rows) x keys (columns)
+            f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk) {
+                const V8<T> qa = as_v8<T>(ld_s16(S + L::Q_OFF + col * L::RP + 16 * kk + 8 * kg));
+                s = Mfma<T>::mma(qa, kf[kk], s);
+                const V8<T> da = as_v8<T>(ld_s16(S + L::DO_OFF + col * L::RP + 16 * kk + 8 * kg));
+                dp = Mfma<T>::mma(da, vf[kk], dp);
+            }
+
+            const float slope2 = ALIBI ? a.slopes[h] * kLog2e : 0.f;
+            const bool need_mask = CAUSAL && (q0 < kw + 31);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float4 l4 = *reinterpret_cast<const float4*>(lse2 + 8 * i + 4 * kg);
+                const float4 d4 = *reinterpret_cast<const float4*>(dsv + 8 * i + 4 * kg);
+                const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+                const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 4 * i + j;
+                    const int qi = q0 + 8 * i + 4 * kg + j;
+                    float t = s[r] * c2;
+                    if (ALIBI) {
+                        const float dist = (float)(qi - key);
+                        t -= slope2 * (CAUSAL ? dist : fabsf(dist));
+                    }
+                    float p = exp2_fast(t - lv[j]);
+                    if (need_mask && key > qi) p = 0.f;
+                    s[r] = p;
+                    dp[r] = p * (dp[r] - dv4[j]);
+                }
+            }
+
+            // dV^T += dO^T P and dK^T += Q^T dS, 16 queries per MFMA
+#pragma unroll
+            for (int c = 0; c < KV_BQ / 16; ++c) {
+                const int r0 = 8 * c;
+                const V8<T> pb = pack8<T>(s[r0], s[r0 + 1], s[r0 + 2], s[r0 + 3], s[r0 + 4], s[r0 + 5], s[r0 + 6],
+                                          s[r0 + 7]);
+                const V8<T> db8 = pack8<T>(dp[r0], dp[r0 + 1], dp[r0 + 2], dp[r0 + 3], dp[r0 + 4], dp[r0 + 5],
+                                           dp[r0 + 6], dp[r0 + 7]);
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                    const int trow = (32 * db + col) * L::TP + 16 * c + 4 * kg;
+                    const uint2 olo = ld_s8(S + L::DOT_OFF + trow), ohi = ld_s8(S + L::DOT_OFF + trow + 8);
+                    dvacc[db] = Mfma<T>::mma(as_v8<T>(make_uint4(olo.x, olo.y, ohi.x, ohi.y)), pb, dvacc[db]);
+                    const uint2 qlo = ld_s8(S + L::QT_OFF + trow), qhi = ld_s8(S + L::QT_OFF + trow + 8);
+                    dkacc[db] = Mfma<T>::mma(as_v8<T>(make_uint4(qlo.x, qlo.y, qhi.x, qhi.y)), db8, dkacc[db]);
+                }
+            }
+        }
+        if (st + 1 < steps) swrite(stage ^ 1);
+        __syncthreads();
+    }
+
+    // epilogue: lane owns key `key`; accumulator rows are dims 32*db + 8*i + 4*kg + 0..3
+    if (key < len) {
+        T* dK = reinterpret_cast<T*>(a.dk) + (size_t)(row0 + key) * ldk + (size_t)g * D;
+        T* dV = reinterpret_cast<T*>(a.dv) + (size_t)(row0 + key) * ldk + (size_t)g * D;
+        const float sc = a.scale;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int d0 = 32 * db + 8 * i + 4 * kg;
+                const int r = 4 * i;
+                *reinterpret_cast<uint2*>(dK + d0) = pack4<T>(dkacc[db][r] * sc, dkacc[db][r + 1] * sc,
+                                                              dkacc[db][r + 2] * sc, dkacc[db][r + 3] * sc);
+                *reinterpret_cast<uint2*>(dV + d0) =
+                    pack4<T>(dvacc[db][r], dvacc[db][r + 1], dvacc[db][r + 2], dvacc[db][r + 3]);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- dQ
+constexpr int DQ_BQ = 128;  // queries per workgroup (32 per wave)
+constexpr int DQ_BK = 64;   // keys per K/V tile
+
+template <int D>
+struct DqLds {
+    static constexpr int RP = D + 8;        // K, V row-major pitch
+    static constexpr int TP = DQ_BK + 4;    // K^T pitch: 34 dwords, conflict-free b64 reads
+    static constexpr int ROW = DQ_BK * RP;
+    static constexpr int TR = D * TP;
+    static constexpr int K_OFF = 0, V_OFF = ROW, KT_OFF = 2 * ROW;
+    static constexpr int STAGE = 2 * ROW + TR;
+    static constexpr int GROUPS = (DQ_BK / 4) * (D / 8);  // (4 keys x 8 dims) groups per tensor
+    static constexpr int G_PER_THREAD = (2 * GROUPS + NT - 1) / NT;
+};
+
+template <typename T, int D, bool CAUSAL, bool ALIBI>
+__global__ __launch_bounds__(NT) void bwd_dq_kernel(Args a) {
+    using L = DqLds<D>;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * L::STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 31, kg = lane >> 5;
+    const int h = blockIdx.x, b = blockIdx.y;
+    const int qt = CAUSAL ? (int)(gridDim.z - 1 - blockIdx.z) : (int)blockIdx.z;
+    int row0, len;
+    seq_bounds(a, b, row0, len);
+    const int q0 = qt * DQ_BQ;
+    if (q0 >= len) return;
+
+    const int g = h / a.G;
+    const size_t ldq = (size_t)a.H * D, ldk = (size_t)a.Hkv * D;
+    const int qw = q0 + wave * 32;
+    const int qi = qw + col;
+    const bool wave_live = qw < len;
+
+    V8<T> qf[D / 16], df[D / 16];
+    {
+        const T* Qp = reinterpret_cast<const T*>(a.q) + (size_t)(row0 + qi) * ldq + (size_t)h * D;
+        const T* Dp = reinterpret_cast<const T*>(a.dout) + (size_t)(row0 + qi) * ldq + (size_t)h * D;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            uint4 uq = make_uint4(0, 0, 0, 0), ud = uq;
+            if (qi < len) {
+                uq = ld_g16(Qp + 16 * kk + 8 * kg);
+                ud = ld_g16(Dp + 16 * kk + 8 * kg);
+            }
+            qf[kk] = as_v8<T>(uq);
+            df[kk] = as_v8<T>(ud);
+        }
+    }
+    const size_t vidx = ((size_t)b * a.H + h) * a.N + qi;
+    const float lse2 = (qi < len) ? a.lse_in[vidx] * kLog2e : INFINITY;
+    const float dsum = (qi < len) ? a.dsum[vidx] : 0.f;
+    const float c2 = a.scale_log2;
+    const float slope2 = ALIBI ? a.slopes[h] * kLog2e : 0.f;
+
+    f32x16 dqacc[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) dqacc[db] = f32x16{};
+
+    const int kend = CAUSAL ? min(len, q0 + DQ_BQ) : len;
+    const int nkt = (kend + DQ_BK - 1) / DQ_BK;
+    const T* Kg = reinterpret_cast<const T*>(a.k) + (size_t)row0 * ldk + (size_t)g * D;
+    const T* Vg = reinterpret_cast<const T*>(a.v) + (size_t)row0 * ldk + (size_t)g * D;
+
+    uint4 greg[L::G_PER_THREAD][4];
+    auto gload = [&](int kt) {
+        const int k0 = kt * DQ_BK;
+#pragma unroll
+        for (int r = 0; r < L::G_PER_THREAD; ++r) {
+            const int gi = tid + r * NT;
+            const int tsel = gi / L::GROUPS;  // 0: K, 1: V
+            const int gl = gi % L::GROUPS;
+            const int dc = gl % (D / 8), rk = gl / (D / 8);
+            const T* base = (tsel == 0 ? Kg : Vg) + dc * 8;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int kj = k0 + 4 * rk + e;
+                greg[r][e] = (gi < 2 * L::GROUPS && kj < len) ? ld_g16(base + (size_t)kj * ldk)
+                                                              : make_uint4(0, 0, 0, 0);
+            }
+        }
+    };
+    auto swrite = [&](int stage) {
+        uint16_t* S = smem + stage * L::STAGE;
+#pragma unroll
+        for (int r = 0; r < L::G_PER_THREAD; ++r) {
+            const int gi = tid + r * NT;
+            if (gi < 2 * L::GROUPS) {
+                const int tsel = gi / L::GROUPS;
+                const int gl = gi % L::GROUPS;
+                const int dc = gl % (D / 8), rk = gl / (D / 8);
+                uint16_t* rm = S + (tsel == 0 ? L::K_OFF : L::V_OFF);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) st_s16(rm + (4 * rk + e) * L::RP + dc * 8, greg[r][e]);
+                if (tsel == 0) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const uint32_t lo = half_of(greg[r][0], e) | (half_of(greg[r][1], e) << 16);
+                        const uint32_t hi = half_of(greg[r][2], e) | (half_of(greg[r][3], e) << 16);
+                        st_s8(S + L::KT_OFF + (dc * 8 + e) * L::TP + 4 * rk, make_uint2(lo, hi));
+                    }
+                }
+            }
+        }
+    };
+
+    gload(0);
+    swrite(0);
+    __syncthreads();
+
+    for (int kt = 0; kt < nkt; ++kt) {
+        const int stage = kt & 1;
+        if (kt + 1 < nkt) gload(kt + 1);
+        const int k0 = kt * DQ_BK;
+        const bool active = wave_live && (!CAUSAL || k0 <= qw + 31);
+        if (active) {
+            const uint16_t* S = smem + stage * L::STAGE;
+            f32x16 s[DQ_BK / 32], dp[DQ_BK / 32];
+#pragma unroll
+            for (int kb = 0; kb < DQ_BK / 32; ++kb) {
+                s[kb] = f32x16{};
+                dp[kb] = f32x16{};
+#pragma unroll
+                for (int kk = 0; kk < D / 16; ++kk) {
+                    const V8<T> ka = as_v8<T>(ld_s16(S + L::K_OFF + (32 * kb + col) * L::RP + 16 * kk + 8 * kg));
+                    s[kb] = Mfma<T>::mma(ka, qf[kk], s[kb]);
+                    const V8<T> va = as_v8<T>(ld_s16(S + L::V_OFF + (32 * kb + col) * L::RP + 16 * kk + 8 * kg));
+                    dp[kb] = Mfma<T>::mma(va, df[kk], dp[kb]);
+                }
+            }
+            const bool need_mask = (k0 + DQ_BK > len) || (CAUSAL && k0 + DQ_BK - 1 > qw);
+#pragma unroll
+            for (int kb = 0; kb < DQ_BK / 32; ++kb) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int kj = k0 + 32 * kb + 8 * (r >> 2) + 4 * kg + (r & 3);
+                    float t = s[kb][r] * c2;
+                    if (ALIBI) {
+                        const float dist = (float)(qi - kj);
+                        t -= slope2 * (CAUSAL ? dist : fabsf(dist));
+                    }
+                    float p = exp2_fast(t - lse2);
+                    if (need_mask && (kj >= len || (CAUSAL && kj > qi))) p = 0.f;
+                    dp[kb][r] = p * (dp[kb][r] - dsum);
+                }
+            }
+            // dQ^T += K^T dS^T, 16 keys per MFMA
+#pragma unroll
+            for (int c = 0; c < DQ_BK / 16; ++c) {
+                const int kb = c >> 1, r0 = 8 * (c & 1);
+                const V8<T> dsb = pack8<T>(dp[kb][r0], dp[kb][r0 + 1], dp[kb][r0 + 2], dp[kb][r0 + 3], dp[kb][r0 + 4],
+                                           dp[kb][r0 + 5], dp[kb][r0 + 6], dp[kb][r0 + 7]);
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                    const int trow = L::KT_OFF + (32 * db + col) * L::TP + 16 * c + 4 * kg;
+                    const uint2 lo = ld_s8(S + trow), hi = ld_s8(S + trow + 8);
+                    dqacc[db] = Mfma<T>::mma(as_v8<T>(make_uint4(lo.x, lo.y, hi.x, hi.y)), dsb, dqacc[db]);
+                }
+            }
+        }
+        if (kt + 1 < nkt) swrite(stage ^ 1);
+        __syncthreads();
+    }
+
+    if (qi < len) {
+        T* dQ = reinterpret_cast<T*>(a.dq) + (size_t)(row0 + qi) * ldq + (size_t)h * D;
+        const float sc = a.scale;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int d0 = 32 * db + 8 * i + 4 * kg;
+                const int r = 4 * i;
+                *reinterpret_cast<uint2*>(dQ + d0) = pack4<T>(dqacc[db][r] * sc, dqacc[db][r + 1] * sc,
+                                                              dqacc[db][r + 2] * sc, dqacc[db][r + 3] * sc);
+            }
+        }
+    }
+}
+
+template <typename T, int D, bool CAUSAL, bool ALIBI>
+hipError_t launch(const Args& a, unsigned stages, hipStream_t s) {
+    if (stages & 1u) {
+        constexpr int RPB = NT / (D / 8);
+        dim3 grid(a.H, a.B, (a.N + RPB - 1) / RPB);
+        hipLaunchKernelGGL((bwd_dsum_kernel<T, D>), grid, dim3(NT), 0, s, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (stages & 2u) {
+        dim3 grid(a.Hkv, a.B, (a.N + KV_BK - 1) / KV_BK);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL, ALIBI>), grid, dim3(NT), 0, s, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (stages & 4u) {
+        dim3 grid(a.H, a.B, (a.N + DQ_BQ - 1) / DQ_BQ);
+        hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL, ALIBI>), grid, dim3(NT), 0, s, a);
+        return hipGetLastError();
+    }
+    return hipSuccess;
+}
+
+template <typename T, int D>
+hipError_t launch_d(const Args& a, bool causal, bool alibi, unsigned st, hipStream_t s) {
+    if (causal) return alibi ? launch<T, D, true, true>(a, st, s) : launch<T, D, true, false>(a, st, s);
+    return alibi ? launch<T, D, false, true>(a, st, s) : launch<T, D, false, false>(a, st, s);
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const Args& a, int dtype, int d, bool causal, bool alibi, unsigned st, hipStream_t s) {
+    if (dtype == 2)
+        return d == 64 ? launch_d<__bf16, 64>(a, causal, alibi, st, s) : launch_d<__bf16, 128>(a, causal, alibi, st, s);
+    return d == 64 ? launch_d<_Float16, 64>(a, causal, alibi, st, s) : launch_d<_Float16, 128>(a, causal, alibi, st, s);
+}
+
+}  // namespace fa

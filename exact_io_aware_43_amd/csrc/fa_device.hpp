@@ -1,0 +1,103 @@
+// Device-side building blocks for the gfx950 attention kernels: vector types,
+// the 32x32x16 MFMA wrappers and their register layouts, and small load/store
+// helpers.
+//
+// MFMA v_mfma_f32_32x32x16_{bf16,f16} register layout (wave64), used by every
+// kernel here. Lane l, with c = l % 32 and kg = l / 32:
+//   A (32 x 16, M x K): lane l holds A[m = c][k = 8*kg + e], e = 0..7
+//   B (16 x 32, K x N): lane l holds B[k = 8*kg + e][n = c], e = 0..7
+//   C (32 x 32, fp32):  acc[4*i + j] = C[m = 8*i + 4*kg + j][n = c], i, j = 0..3
+// Only the pairing matters for the K index: the kernels give element e of lane
+// l the same k in A and in B, so any consistent k permutation is a valid
+// contraction.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "fa_internal.hpp"
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <typename T>
+struct Mfma;
+
+template <>
+struct Mfma<__bf16> {
+    using V8 = bf16x8;
+    static __device__ __forceinline__ f32x16 mma(V8 a, V8 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+};
+
+template <>
+struct Mfma<_Float16> {
+    using V8 = f16x8;
+    static __device__ __forceinline__ f32x16 mma(V8 a, V8 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+};
+
+template <typename T>
+using V8 = typename Mfma<T>::V8;
+
+// Round-to-nearest-even conversion of 8 fp32 values into one MFMA operand.
+template <typename T>
+__device__ __forceinline__ V8<T> pack8(float x0, float x1, float x2, float x3, float x4, float x5,
+                                       float x6, float x7) {
+    V8<T> r;
+    r[0] = (T)x0; r[1] = (T)x1; r[2] = (T)x2; r[3] = (T)x3;
+    r[4] = (T)x4; r[5] = (T)x5; r[6] = (T)x6; r[7] = (T)x7;
+    return r;
+}
+
+// Four fp32 values -> four 16-bit values in 8 bytes (RNE).
+template <typename T>
+__device__ __forceinline__ uint2 pack4(float x0, float x1, float x2, float x3) {
+    typedef T T4 __attribute__((ext_vector_type(4)));
+    T4 r;
+    r[0] = (T)x0; r[1] = (T)x1; r[2] = (T)x2; r[3] = (T)x3;
+    return __builtin_bit_cast(uint2, r);
+}
+
+template <typename T>
+__device__ __forceinline__ V8<T> as_v8(uint4 u) {
+    return __builtin_bit_cast(V8<T>, u);
+}
+
+__device__ __forceinline__ uint4 ld_g16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ uint4 ld_s16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ uint2 ld_s8(const uint16_t* p) { return *reinterpret_cast<const uint2*>(p); }
+__device__ __forceinline__ void st_s16(uint16_t* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+__device__ __forceinline__ void st_s8(uint16_t* p, uint2 v) { *reinterpret_cast<uint2*>(p) = v; }
+
+// 16-bit element `e` (0..7) of a 16-byte chunk.
+__device__ __forceinline__ uint32_t half_of(const uint4& u, int e) {
+    const uint32_t w = (e < 2) ? u.x : (e < 4) ? u.y : (e < 6) ? u.z : u.w;
+    return (e & 1) ? (w >> 16) : (w & 0xffffu);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Sequence base row and length of batch entry / packed sequence b; lengths are
+// clamped to [0, N] so a malformed cu_seqlens cannot enlarge the grid's work.
+__device__ __forceinline__ void seq_bounds(const Args& a, int b, int& row0, int& len) {
+    if (a.cu) {
+        row0 = a.cu[b];
+        len = a.cu[b + 1] - row0;
+        len = len < 0 ? 0 : (len > a.N ? a.N : len);
+    } else {
+        row0 = b * a.N;
+        len = a.N;
+    }
+}
+
+}  // namespace fa

@@ -1,0 +1,39 @@
+// Launch arguments shared by the C-ABI layer (fa_api.hip) and the kernel files.
+// Host-visible only; no kernel code here.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+
+namespace fa {
+
+// One attention problem as the kernels see it. Pointers are device memory in
+// the layouts documented in include/fa.h; `cu` is NULL for dense inputs.
+struct Args {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;     // forward output / backward input
+    const void* dout;  // backward only
+    void* out;         // fa_fwd: O.  (backward writes dq/dk/dv below)
+    float* lse;        // [B, H, N]
+    const float* lse_in;
+    void* dq;
+    void* dk;
+    void* dv;
+    float* dsum;       // backward: D_i = dO_i . O_i, laid out like lse
+    const float* slopes;
+    const int* cu;
+    int B, H, Hkv, N, G;
+    float scale;       // softmax scale
+    float scale_log2;  // scale * log2(e)
+};
+
+// Each returns hipSuccess or the launch error. `dtype` follows fa_dtype.
+hipError_t launch_fwd_mfma(const Args& a, int dtype, int d, bool causal, bool alibi, hipStream_t s);
+hipError_t launch_fwd_f32(const Args& a, int d, bool causal, bool alibi, hipStream_t s);
+// `stages`: bit 0 = D pre-pass, bit 1 = dK/dV, bit 2 = dQ (enqueued in that order).
+hipError_t launch_bwd(const Args& a, int dtype, int d, bool causal, bool alibi, unsigned stages, hipStream_t s);
+
+}  // namespace fa

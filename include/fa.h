@@ -1,0 +1,144 @@
+/*
+ * libfa: exact tiled scaled-dot-product attention (forward and backward) for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Operation (page "FlashAttention: Faster Attention Without Dropping a Single
+ * Interaction", Method Deep Dive, Key design 1): for every batch entry or
+ * packed sequence b and query head h, with kv head g = h / (H / Hkv),
+ *
+ *     S_ij = scale * <q_i, k_j> + beta_ij,   P = softmax_rows(S),   O = P V,
+ *
+ * where beta_ij = -alibi_slopes[h] * |i - j| when slopes are given (0 otherwise)
+ * and, when causal, keys j > i are removed. The forward also stores the row
+ * statistic lse_i = m_i + ln(sum_j exp(S_ij - m_i)) (natural log; the saved-state
+ * table of Key design 2), which is all the backward needs to rebuild P (Key
+ * design 3). The N x N matrices S and P never reach device memory.
+ *
+ * Layouts (row-major, contiguous, element strides implied by the sizes):
+ *   dense   q, o, dout, dq : [B, N, H, d]       k, v, dk, dv : [B, N, Hkv, d]
+ *   packed  q, o, dout, dq : [total, H, d]      k, v, dk, dv : [total, Hkv, d]
+ *           (packed when cu_seqlens != NULL; total = cu_seqlens[B])
+ *   lse                    : float [B, H, N] in both modes; for packed inputs
+ *                            entries at positions >= a sequence's length are
+ *                            left untouched.
+ *   cu_seqlens             : int32 [B + 1], device memory, cu_seqlens[0] = 0,
+ *                            non-decreasing; every length must be <= N (N is
+ *                            the maximum sequence length in packed mode).
+ *   alibi_slopes           : float [H], device memory, or NULL for no bias.
+ *
+ * Element types (fa_dtype): FA_BF16 and FA_FP16 store q, k, v, o, dout, dq, dk,
+ * dv in that 16-bit type and accumulate in fp32; FA_FP32 stores fp32 and
+ * computes in fp32 (forward only).
+ *
+ * Ownership and execution: every pointer is caller-owned device memory. The
+ * library never allocates, frees or synchronises; all work is enqueued on
+ * `stream` (a hipStream_t, NULL for the default stream) and the call returns
+ * at once. Inputs are read-only; outputs must not alias inputs or each other.
+ * Base pointers must be 16-byte aligned. The library keeps no mutable global
+ * state, so concurrent calls from several host threads are safe.
+ *
+ * Errors: every entry returns FA_OK (0) or a negative fa_status. All argument
+ * checks run before any launch; a call that fails them enqueues nothing and
+ * writes nothing. FA_ERR_LAUNCH reports a failure of the launch itself.
+ */
+#ifndef LIBFA_FA_H
+#define LIBFA_FA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_dtype {
+    FA_FP32 = 0,
+    FA_FP16 = 1,
+    FA_BF16 = 2
+} fa_dtype;
+
+typedef enum fa_status {
+    FA_OK = 0,
+    FA_ERR_INVALID_ARG = -1, /* null pointer, bad size, H % Hkv != 0, non-finite scale, misalignment */
+    FA_ERR_UNSUPPORTED = -2, /* head dim not in {64, 128}; fp32 backward */
+    FA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than fa_bwd_workspace_size() */
+    FA_ERR_LAUNCH = -4       /* the kernel launch itself failed */
+} fa_status;
+
+/*
+ * Forward pass: O and lse from Q, K, V (Key design 1 and 2 of the page above;
+ * the tiled loop of "FlashAttention: The Algorithm That Beat the Memory Wall",
+ * "A Tile, a Register File, and a Trick Called Online Softmax"; packed
+ * sequences as in its "Varlen Is the Quiet Superpower").
+ *
+ *   B, H, Hkv, N, d : batch (number of sequences), query heads, kv heads
+ *                     (H % Hkv == 0), sequence length (maximum length when
+ *                     packed), head dimension (64 or 128).
+ *   scale           : multiplies Q K^T before the softmax (1/sqrt(d) is usual).
+ *   causal          : 0 or 1; 1 keeps key j <= query i.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int Hkv, int N, int d, float scale, int causal,
+           const float* alibi_slopes, const int* cu_seqlens, fa_dtype dtype,
+           void* stream);
+
+/*
+ * Bytes of device scratch fa_bwd needs for these sizes: the per-row
+ * D_i = dO_i . O_i of Key design 3 in fp32, laid out like lse. Linear in N.
+ * Returns 0 for invalid sizes.
+ */
+size_t fa_bwd_workspace_size(int B, int H, int Hkv, int N, int d, int causal,
+                             int varlen, fa_dtype dtype);
+
+/*
+ * Backward pass: dQ, dK, dV of the loss sum(O * dout) by recomputing the score
+ * tiles from lse (Key design 3): D_i = dO_i . O_i, dS = P o (dP - D),
+ * dV = P^T dO, dQ = scale * dS K, dK = scale * dS^T Q. `o` and `lse` must come
+ * from fa_fwd on the same inputs and arguments. dq, dk and dv are overwritten;
+ * dk and dv of a kv head hold the sum over its H / Hkv query heads. No atomics
+ * are used, so results are bitwise reproducible run to run. ALiBi slopes get no
+ * gradient. Only FA_BF16 and FA_FP16 are supported.
+ *
+ *   workspace, workspace_bytes : caller-owned device scratch of at least
+ *                                fa_bwd_workspace_size(...) bytes, 16-byte aligned.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+           const void* dout, const float* lse, void* dq, void* dk, void* dv,
+           int B, int H, int Hkv, int N, int d, float scale, int causal,
+           const float* alibi_slopes, const int* cu_seqlens, fa_dtype dtype,
+           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The three launches of fa_bwd, selectable one by one, for callers that split
+ * them across streams (dK/dV and dQ are independent once D is written) or time
+ * them separately. `stages` is a bitwise OR of the fa_bwd_stage values; the
+ * selected stages are enqueued on `stream` in the order PREP, DKDV, DQ. DKDV
+ * and DQ read the D values that PREP wrote into the same workspace, so the
+ * caller orders PREP before them. fa_bwd(...) equals fa_bwd_stages(...,
+ * FA_BWD_ALL, ...). Same arguments, checks and errors as fa_bwd; a zero or
+ * unknown mask is FA_ERR_INVALID_ARG.
+ */
+typedef enum fa_bwd_stage {
+    FA_BWD_PREP = 1, /* D_i = dO_i . O_i into the workspace (reads o, dout) */
+    FA_BWD_DKDV = 2, /* dk, dv (reads q, k, v, dout, lse, D) */
+    FA_BWD_DQ = 4,   /* dq (reads q, k, v, dout, lse, D) */
+    FA_BWD_ALL = 7
+} fa_bwd_stage;
+
+int fa_bwd_stages(const void* q, const void* k, const void* v, const void* o,
+                  const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                  int B, int H, int Hkv, int N, int d, float scale, int causal,
+                  const float* alibi_slopes, const int* cu_seqlens, fa_dtype dtype,
+                  void* workspace, size_t workspace_bytes, unsigned stages,
+                  void* stream);
+
+/* Static, human-readable text for a status code (never NULL, never freed). */
+const char* fa_strerror(int status);
+
+/* Library version as MAJOR * 10000 + MINOR * 100 + PATCH. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBFA_FA_H */

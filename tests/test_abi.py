@@ -1,0 +1,122 @@
+"""CPU checks of the C ABI: the library loads, exports every function include/fa.h
+declares, and rejects bad arguments with the documented status before launching.
+
+Every call here fails argument validation, so no kernel is launched (the fake
+device pointers are never dereferenced); that is the property under test.
+"""
+
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import exact_io_aware_43_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
+A = 0x10000  # fake, 16-byte aligned "device" addresses: never dereferenced
+PTR = [A + 0x1000 * i for i in range(12)]
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_expected_api():
+    assert declared_functions() == sorted(
+        ["fa_fwd", "fa_bwd", "fa_bwd_stages", "fa_bwd_workspace_size", "fa_strerror", "fa_version"])
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fa.lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\s[TW]\s+(\S+)", out))
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in exported, f"{name} not exported with C linkage"
+
+
+def test_version_and_strerror():
+    assert fa.fa_version() == 10000
+    for code in (OK, INVALID, UNSUPPORTED, WORKSPACE, -4):
+        s = fa.fa_strerror(code)
+        assert s and s != "unknown status"
+    assert fa.fa_strerror(123) == "unknown status"
+
+
+def _fwd(**kw):
+    a = dict(q=PTR[0], k=PTR[1], v=PTR[2], o=PTR[3], lse=PTR[4], B=1, H=4, Hkv=2, N=64, d=128, scale=0.125,
+             causal=0, alibi=None, cu=None, dtype=fa.FA_BF16, stream=None)
+    a.update(kw)
+    return fa.fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["N"], a["d"], a["scale"],
+                     a["causal"], a["alibi"], a["cu"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(v=None), INVALID), (dict(o=None), INVALID),
+    (dict(lse=None), INVALID), (dict(B=0), INVALID), (dict(H=0), INVALID), (dict(Hkv=0), INVALID),
+    (dict(N=0), INVALID), (dict(N=-5), INVALID), (dict(H=6, Hkv=4), INVALID), (dict(causal=2), INVALID),
+    (dict(scale=math.nan), INVALID), (dict(scale=math.inf), INVALID), (dict(dtype=3), INVALID),
+    (dict(d=96), UNSUPPORTED), (dict(d=256), UNSUPPORTED), (dict(d=0), INVALID),
+    (dict(q=PTR[0] + 8), INVALID), (dict(o=PTR[3] + 2), INVALID), (dict(lse=PTR[4] + 4), INVALID),
+    (dict(alibi=PTR[5] + 4), INVALID), (dict(cu=PTR[6] + 4), INVALID),
+    (dict(B=1 << 16, N=1 << 16, H=2, Hkv=2), INVALID),
+])
+def test_fwd_rejects(kw, expect):
+    assert _fwd(**kw) == expect
+
+
+def _bwd(stages=None, **kw):
+    a = dict(q=PTR[0], k=PTR[1], v=PTR[2], o=PTR[3], do=PTR[4], lse=PTR[5], dq=PTR[6], dk=PTR[7], dv=PTR[8],
+             B=2, H=4, Hkv=2, N=64, d=64, scale=0.125, causal=1, alibi=None, cu=None, dtype=fa.FA_BF16,
+             ws=PTR[9], ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    args = [a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"], a["B"], a["H"], a["Hkv"],
+            a["N"], a["d"], a["scale"], a["causal"], a["alibi"], a["cu"], a["dtype"], a["ws"], a["ws_bytes"]]
+    if stages is None:
+        return fa.fa_bwd(*args, a["stream"])
+    return fa.fa_bwd_stages(*args, stages, a["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), INVALID), (dict(do=None), INVALID), (dict(lse=None), INVALID), (dict(dq=None), INVALID),
+    (dict(dk=None), INVALID), (dict(dv=None), INVALID), (dict(H=3), INVALID), (dict(causal=-1), INVALID),
+    (dict(dtype=fa.FA_FP32), UNSUPPORTED), (dict(d=32), UNSUPPORTED),
+    (dict(dk=PTR[7] + 8), INVALID), (dict(ws=None), WORKSPACE), (dict(ws=PTR[9] + 8), WORKSPACE),
+    (dict(ws_bytes=2 * 4 * 64 * 4 - 1), WORKSPACE),
+])
+def test_bwd_rejects(kw, expect):
+    assert _bwd(**kw) == expect
+    assert _bwd(stages=fa.FA_BWD_ALL, **kw) == expect
+
+
+@pytest.mark.parametrize("stages", [0, 8, 9, 0xFF])
+def test_bwd_stage_mask_rejected(stages):
+    assert _bwd(stages=stages) == INVALID
+
+
+def test_workspace_size():
+    # fp32 D per (sequence, head, position), rounded up to 256 bytes
+    assert fa.fa_bwd_workspace_size(2, 4, 2, 64, 64, 1, 0, fa.FA_BF16) == 2 * 4 * 64 * 4
+    assert fa.fa_bwd_workspace_size(1, 32, 32, 16384, 128, 1, 0, fa.FA_BF16) == 32 * 16384 * 4
+    assert fa.fa_bwd_workspace_size(1, 1, 1, 3, 64, 0, 0, fa.FA_BF16) == 256
+    assert fa.fa_bwd_workspace_size(0, 4, 2, 64, 64, 1, 0, fa.FA_BF16) == 0
+    assert fa.fa_bwd_workspace_size(1, 4, 3, 64, 64, 1, 0, fa.FA_BF16) == 0
+    assert fa.fa_bwd_workspace_size(1, 4, 2, 64, 80, 1, 0, fa.FA_BF16) == 0
+
+
+def test_binding_shape_errors():
+    import torch
+
+    q = torch.zeros(2, 8, 4, 64)
+    with pytest.raises(ValueError):
+        fa.attention(q, q, q)  # host tensors are refused before any call
+    with pytest.raises(ValueError):
+        fa._binding._shape(torch.zeros(8, 4, 64), torch.zeros(8, 2, 64), torch.zeros(3, dtype=torch.int32), None)
+    assert fa._binding._shape(q, torch.zeros(2, 8, 2, 64), None, None) == (2, 4, 2, 8, 64)
