@@ -87,6 +87,33 @@ __device__ __forceinline__ uint32_t half_of(const uint4& u, int e) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Transposing LDS read (ds_read_b64_tr_b16). Within each group of 16 lanes,
+// lane 4a + c receives element c of the 8-byte chunks addressed by lanes
+// a, a + 4, a + 8 and a + 12 of the group, in that order. If lane r of a group
+// addresses row (row0 + r / 4), columns (col0 + 4 * (r % 4)) .. +3 of a
+// row-major 16-bit tile, lane r receives column (col0 + r) of rows
+// row0 .. row0 + 3: four consecutive rows of one column.
+__device__ __forceinline__ uint2 ld_s8_tr(const uint16_t* p) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)((__attribute__((address_space(3))) uint16_t*)p));
+    return __builtin_bit_cast(uint2, v);
+}
+
+// MFMA A operand for a product whose contraction index runs along the ROWS of
+// a row-major LDS tile (for example V^T from V[key][d]): lane l gets column
+// (col0 + l % 32) and rows row0 + {4*kg .. 4*kg+3, 8+4*kg .. 8+4*kg+3},
+// kg = l / 32, which is the k order the score accumulator hands to its
+// transposed operand (see the layout notes above).
+__device__ __forceinline__ uint4 ld_s16_rows_tr(const uint16_t* tile, int pitch, int row0, int col0, int lane) {
+    const int r = lane & 15, grp = lane >> 4;
+    const uint16_t* p = tile + (row0 + 4 * (grp >> 1) + (r >> 2)) * pitch + col0 + 16 * (grp & 1) + 4 * (r & 3);
+    const uint2 lo = ld_s8_tr(p);
+    const uint2 hi = ld_s8_tr(p + 8 * pitch);
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+
 // Sequence base row and length of batch entry / packed sequence b; lengths are
 // clamped to [0, N] so a malformed cu_seqlens cannot enlarge the grid's work.
 __device__ __forceinline__ void seq_bounds(const Args& a, int b, int& row0, int& len) {

@@ -10,42 +10,56 @@
 // Work decomposition. One workgroup of 4 waves owns BR = 128 query rows of one
 // (sequence, query head); each wave owns 32 of them. K and V of the head's kv
 // head stream through LDS in tiles of BC = 64 keys, double buffered: the next
-// tile's global loads are in flight while the current tile is multiplied.
+// tile's global loads are in flight while the current tile is multiplied. Two
+// workgroups share a compute unit, so each SIMD interleaves the matrix work of
+// one wave with the softmax of the other.
 //
 // Register orientation. Each wave computes the transposed score tile
 // S^T = K Q^T (keys x queries) so that in the MFMA accumulator every lane holds
 // scores of ONE query (its column) for 16 keys; the row max and row sum are
-// then in-lane reductions plus one exchange with lane l ^ 32. The output is
+// in-lane reductions plus one exchange with lane l ^ 32. The output is
 // accumulated transposed as well, O^T += V^T P^T, which takes P^T straight
 // from the score accumulator as the B operand and keeps the per-query rescale
-// factor in-lane. V is stored transposed in LDS ([d][key]) for that product.
+// factor in-lane. V stays row-major in LDS; its transposed operand comes from
+// the transposing LDS read.
 //
-// Numerics: scores, max, sums and the O accumulator are fp32; P is rounded to
-// the input type for the second product; exp is exp2 with scale*log2(e)
-// folded into one multiply; lse is converted back to natural log.
+// Softmax bookkeeping. Scores are kept in log2 units (scale * log2(e) folded
+// into one FMA before exp2). The reference maximum m is only raised when a
+// tile's maximum exceeds it by more than TAU = 8 (a factor 256): P = 2^(t - m)
+// then stays below 256, which fp32 accumulators and the 16-bit P operand hold
+// with their usual relative precision, and the rescale of O and l is skipped
+// for almost every tile. The result is unchanged in exact arithmetic because
+// the final division uses sums taken against the same reference.
+//
+// Numerics: scores, sums and the O accumulator are fp32; P is rounded to the
+// input type for the second product; lse is converted back to natural log.
 #include "fa_device.hpp"
 
 namespace fa {
 namespace {
 
-constexpr int BR = 128;  // query rows per workgroup
-constexpr int BC = 64;   // keys per K/V tile
-constexpr int NT = 256;  // threads per workgroup (4 waves)
+constexpr int BR = 128;    // query rows per workgroup
+constexpr int BC = 64;     // keys per K/V tile
+constexpr int NT = 256;    // threads per workgroup (4 waves)
+constexpr float TAU = 8.f; // lazy-rescale threshold, log2 units
 
 template <int D>
 struct FwdLds {
-    static constexpr int KP = D + 8;    // K row pitch (elements): 16-byte pad, conflict-free b128 reads
-    static constexpr int VP = BC + 4;   // V^T row pitch (elements): 34 dwords, conflict-free b64 reads
-    static constexpr int KT = BC * KP;  // K tile elements
-    static constexpr int VT = D * VP;   // V^T tile elements
+    // K: row-major, pitch = D + 8 elements (b128 reads of 16 keys hit distinct banks).
+    // V: row-major, pitch = D + 32 elements (the transposing b64 reads of 4 rows x 64 B
+    //    per half-wave hit distinct banks).
+    static constexpr int KP = D + 8;
+    static constexpr int VP = D + 32;
+    static constexpr int KT = BC * KP;
+    static constexpr int VT = BC * VP;
     static constexpr int STAGE = KT + VT;
-    static constexpr int K_LOADS = BC * D / 8 / NT;   // 16-byte K chunks per thread
-    static constexpr int V_GROUPS = (BC / 4) * (D / 8);  // (4 keys x 8 dims) groups per tile
-    static constexpr int V_LOADS = (V_GROUPS + NT - 1) / NT;
+    static constexpr int CHUNKS = BC * D / 8;             // 16-byte chunks per tile (each of K, V)
+    static constexpr int LOADS = CHUNKS / NT;             // per thread, per tensor
+    static_assert(CHUNKS % NT == 0, "tile must split evenly over the workgroup");
 };
 
 template <typename T, int D, bool CAUSAL, bool ALIBI>
-__global__ __launch_bounds__(NT) void fwd_mfma_kernel(Args a) {
+__global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(Args a) {
     using L = FwdLds<D>;
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * L::STAGE];
 
@@ -89,57 +103,37 @@ __global__ __launch_bounds__(NT) void fwd_mfma_kernel(Args a) {
     const int kend = CAUSAL ? min(len, q0 + BR) : len;
     const int nkt = (kend + BC - 1) / BC;
 
-    // ---- cooperative K/V tile staging (global -> registers -> LDS)
-    uint4 kreg[L::K_LOADS];
-    uint4 vreg[L::V_LOADS][4];
+    // ---- cooperative K/V staging: global -> registers -> LDS, 16 bytes per chunk.
+    // Chunk c of a tile is (key c / (D/8), dims 8 * (c % (D/8))); consecutive
+    // threads read consecutive 16 bytes of one key row.
+    uint4 kreg[L::LOADS], vreg[L::LOADS];
     auto gload = [&](int kt) {
         const int k0 = kt * BC;
 #pragma unroll
-        for (int r = 0; r < L::K_LOADS; ++r) {
+        for (int r = 0; r < L::LOADS; ++r) {
             const int c = tid + r * NT;
-            const int key = c / (D / 8), dc = c % (D / 8);
-            kreg[r] = (k0 + key < len) ? ld_g16(Kg + (size_t)(k0 + key) * ldk + dc * 8) : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int r = 0; r < L::V_LOADS; ++r) {
-            const int gi = tid + r * NT;
-            const int dc = gi % (D / 8), kq = gi / (D / 8);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int key = k0 + 4 * kq + e;
-                vreg[r][e] = (gi < L::V_GROUPS && key < len) ? ld_g16(Vg + (size_t)key * ldk + dc * 8)
-                                                            : make_uint4(0, 0, 0, 0);
-            }
+            const int key = k0 + c / (D / 8), dc = 8 * (c % (D / 8));
+            const bool ok = key < len;
+            kreg[r] = ok ? ld_g16(Kg + (size_t)key * ldk + dc) : make_uint4(0, 0, 0, 0);
+            vreg[r] = ok ? ld_g16(Vg + (size_t)key * ldk + dc) : make_uint4(0, 0, 0, 0);
         }
     };
     auto swrite = [&](int stage) {
         uint16_t* Ks = smem + stage * L::STAGE;
         uint16_t* Vs = Ks + L::KT;
 #pragma unroll
-        for (int r = 0; r < L::K_LOADS; ++r) {
+        for (int r = 0; r < L::LOADS; ++r) {
             const int c = tid + r * NT;
-            const int key = c / (D / 8), dc = c % (D / 8);
-            st_s16(Ks + key * L::KP + dc * 8, kreg[r]);
-        }
-#pragma unroll
-        for (int r = 0; r < L::V_LOADS; ++r) {
-            const int gi = tid + r * NT;
-            if (gi < L::V_GROUPS) {
-                const int dc = gi % (D / 8), kq = gi / (D / 8);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint32_t lo = half_of(vreg[r][0], e) | (half_of(vreg[r][1], e) << 16);
-                    const uint32_t hi = half_of(vreg[r][2], e) | (half_of(vreg[r][3], e) << 16);
-                    st_s8(Vs + (dc * 8 + e) * L::VP + 4 * kq, make_uint2(lo, hi));
-                }
-            }
+            const int key = c / (D / 8), dc = 8 * (c % (D / 8));
+            st_s16(Ks + key * L::KP + dc, kreg[r]);
+            st_s16(Vs + key * L::VP + dc, vreg[r]);
         }
     };
 
     f32x16 oacc[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
-    float m_run = -INFINITY;  // running max, log2 units
+    float m_ref = -INFINITY;  // reference max, log2 units (same in lanes l and l ^ 32)
     float l_run = 0.f;        // this lane's share of the running sum
 
     const float c2 = a.scale_log2;
@@ -159,7 +153,7 @@ __global__ __launch_bounds__(NT) void fwd_mfma_kernel(Args a) {
             const uint16_t* Ks = smem + stage * L::STAGE;
             const uint16_t* Vs = Ks + L::KT;
 
-            // S^T = K Q^T for BC keys x 32 queries
+            // S^T = K Q^T for BC keys x 32 queries (raw, unscaled scores)
             f32x16 s[BC / 32];
 #pragma unroll
             for (int kb = 0; kb < BC / 32; ++kb) {
@@ -171,42 +165,63 @@ __global__ __launch_bounds__(NT) void fwd_mfma_kernel(Args a) {
                 }
             }
 
-            // scale, bias, mask; tile max
-            const bool need_mask = (k0 + BC > len) || (CAUSAL && k0 + BC - 1 > qw);
-            float mt = -INFINITY;
+            // Scores in log2 units. Plain tiles keep the raw score and fold the
+            // scale into the exponent's FMA; ALiBi and edge tiles materialise
+            // t = s * c2 + bias (or -inf when masked) and use scale 1 below.
+            const bool edge = (k0 + BC > len) || (CAUSAL && k0 + BC - 1 > qw);
+            const bool materialise = ALIBI || edge;
+            float mt;
+            if (materialise) {
+                mt = -INFINITY;
 #pragma unroll
-            for (int kb = 0; kb < BC / 32; ++kb) {
+                for (int kb = 0; kb < BC / 32; ++kb) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * kg + (r & 3);
-                    float t = s[kb][r] * c2;
-                    if (ALIBI) {
-                        const float dist = (float)(qi - key);
-                        t -= slope2 * (CAUSAL ? dist : fabsf(dist));
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * kg + (r & 3);
+                        float t = s[kb][r] * c2;
+                        if (ALIBI) {
+                            const float dist = (float)(qi - key);
+                            t -= slope2 * (CAUSAL ? dist : fabsf(dist));
+                        }
+                        if (edge && (key >= len || (CAUSAL && key > qi))) t = -INFINITY;
+                        s[kb][r] = t;
+                        mt = fmaxf(mt, t);
                     }
-                    if (need_mask && (key >= len || (CAUSAL && key > qi))) t = -INFINITY;
-                    s[kb][r] = t;
-                    mt = fmaxf(mt, t);
                 }
+            } else {
+                float mx = s[0][0];
+#pragma unroll
+                for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+                mt = mx * c2;
             }
             mt = fmaxf(mt, __shfl_xor(mt, 32));
-            const float m_new = fmaxf(m_run, mt);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = exp2_fast(m_run - m_use);
+
+            // lazy rescale: raise the reference only when the tile max exceeds it by > TAU
+            const bool raise = mt > m_ref + TAU;
+            if (__any(raise)) {
+                const float m_new = raise ? mt : m_ref;
+                const float alpha = exp2_fast(m_ref - m_new);  // 0 on the first tile
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+                m_ref = m_new;
+            }
+            const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;  // rows with no key yet
+
+            const float sc = materialise ? 1.f : c2;
             float ls = 0.f;
 #pragma unroll
             for (int kb = 0; kb < BC / 32; ++kb) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const float p = exp2_fast(s[kb][r] - m_use);
+                    const float p = exp2_fast(fmaf(s[kb][r], sc, -m_use));
                     s[kb][r] = p;
                     ls += p;
                 }
             }
-            l_run = l_run * alpha + ls;
-            m_run = m_new;
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+            l_run += ls;
 
             // O^T += V^T P^T, 16 keys per MFMA
 #pragma unroll
@@ -216,9 +231,7 @@ __global__ __launch_bounds__(NT) void fwd_mfma_kernel(Args a) {
                                           s[kb][r0 + 4], s[kb][r0 + 5], s[kb][r0 + 6], s[kb][r0 + 7]);
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
-                    const uint16_t* vp = Vs + (32 * db + col) * L::VP + 16 * c + 4 * kg;
-                    const uint2 lo = ld_s8(vp), hi = ld_s8(vp + 8);
-                    const V8<T> vf = as_v8<T>(make_uint4(lo.x, lo.y, hi.x, hi.y));
+                    const V8<T> vf = as_v8<T>(ld_s16_rows_tr(Vs, L::VP, 16 * c, 32 * db, lane));
                     oacc[db] = Mfma<T>::mma(vf, pf, oacc[db]);
                 }
             }
@@ -242,7 +255,7 @@ __global__ __launch_bounds__(NT) void fwd_mfma_kernel(Args a) {
                              oacc[db][4 * i + 3] * inv);
             }
         }
-        if (kg == 0) a.lse[((size_t)b * a.H + h) * a.N + qi] = (m_run + __log2f(l_tot)) * kLn2;
+        if (kg == 0) a.lse[((size_t)b * a.H + h) * a.N + qi] = (m_ref + __log2f(l_tot)) * kLn2;
     }
 }
 
