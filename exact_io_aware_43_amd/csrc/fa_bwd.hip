@@ -10,13 +10,13 @@
 //                 O and dO; O is the stored forward output).
 //   2. bwd_dkdv:  one workgroup per (128-key tile, kv head, sequence). K and V
 //                 of the tile stay in registers; the workgroup walks every
-//                 query head of the kv group and every query tile that can see
-//                 the keys, accumulating dV = P^T dO and dK = dS^T Q in
+//                 query head of the kv group and every 64-query tile that can
+//                 see the keys, accumulating dV = P^T dO and dK = dS^T Q in
 //                 registers. No atomics: each dK / dV row has one owner, and
 //                 the GQA group sum happens in the accumulators.
 //   3. bwd_dq:    one workgroup per (128-query tile, query head, sequence); Q
-//                 and dO stay in registers and K, V tiles stream through LDS;
-//                 dQ = dS K is accumulated in registers.
+//                 and dO stay in registers and 64-key K, V tiles stream through
+//                 LDS; dQ = dS K is accumulated in registers.
 // Splitting dQ from dK/dV recomputes S and dP twice but needs no atomic
 // reduction, so the result is bitwise reproducible (the deterministic option
 // the page's Limitations section discusses).
@@ -26,14 +26,45 @@
 // key column, and accumulates dV^T = dO^T P and dK^T = Q^T dS with P and dS as
 // B operands taken straight from the accumulators. The dQ kernel computes
 // S^T = K Q^T so that each lane owns one query, and accumulates
-// dQ^T = K^T dS^T. Transposed operands (dO^T, Q^T, K^T) are written to LDS
-// transposed by the staging threads.
+// dQ^T = K^T dS^T. Tiles sit in LDS once, row-major and swizzled; the
+// transposed operands (dO^T, Q^T, K^T) come from the transposing LDS read.
 #include "fa_device.hpp"
 
 namespace fa {
 namespace {
 
 constexpr int NT = 256;
+
+// Staging of a 16-bit [ROWS x D] tile from global rows (row stride `ld`
+// elements) into a swizzled LDS tile: global -> registers -> LDS, 16 bytes per
+// chunk, consecutive threads on consecutive chunks of a row. Rows at or past
+// `nrows` read as zero.
+template <int D, int ROWS>
+struct TileStage {
+    static constexpr int CHUNKS = ROWS * D / 8;
+    static constexpr int PER_THREAD = CHUNKS / NT;
+    static_assert(CHUNKS % NT == 0, "tile must split evenly over the workgroup");
+    uint4 r[PER_THREAD];
+
+    template <typename T>
+    __device__ __forceinline__ void load(const T* base, size_t ld, int row_start, int nrows) {
+#pragma unroll
+        for (int i = 0; i < PER_THREAD; ++i) {
+            const int c = threadIdx.x + i * NT;
+            const int row = c / (D / 8), col = 8 * (c % (D / 8));
+            r[i] = (row_start + row < nrows) ? ld_g16(base + (size_t)(row_start + row) * ld + col)
+                                             : make_uint4(0, 0, 0, 0);
+        }
+    }
+    __device__ __forceinline__ void store(uint16_t* tile) const {
+#pragma unroll
+        for (int i = 0; i < PER_THREAD; ++i) {
+            const int c = threadIdx.x + i * NT;
+            const int row = c / (D / 8), col = 8 * (c % (D / 8));
+            st_s16(tile + swz<D>(row, col), r[i]);
+        }
+    }
+};
 
 // ---------------------------------------------------------------- D = dO . O
 template <typename T, int D>
@@ -61,24 +92,18 @@ __global__ __launch_bounds__(NT) void bwd_dsum_kernel(Args a) {
 
 // ---------------------------------------------------------------- dK, dV
 constexpr int KV_BK = 128;  // keys per workgroup (32 per wave)
-constexpr int KV_BQ = 32;   // queries per step
+constexpr int KV_BQ = 64;   // queries per step
 
 template <int D>
 struct KvLds {
-    static constexpr int RP = D + 8;          // row-major pitch (elements)
-    static constexpr int TP = KV_BQ + 4;      // transposed pitch: 18 dwords, conflict-free b64 reads
-    static constexpr int ROW = KV_BQ * RP;    // one row-major tile
-    static constexpr int TR = D * TP;         // one transposed tile
-    // Q, Q^T, dO, dO^T, then lse*log2e and D (fp32, KV_BQ each)
-    static constexpr int Q_OFF = 0, QT_OFF = ROW, DO_OFF = ROW + TR, DOT_OFF = 2 * ROW + TR;
-    static constexpr int VEC_OFF = 2 * ROW + 2 * TR;  // element offset of the fp32 vectors
-    static constexpr int STAGE = VEC_OFF + 2 * KV_BQ * 2;  // in 16-bit elements
-    static constexpr int GROUPS = (KV_BQ / 4) * (D / 8);    // (4 rows x 8 dims) groups per tensor
-    static constexpr int G_PER_THREAD = (2 * GROUPS + NT - 1) / NT;
+    static constexpr int TILE = KV_BQ * D;        // one swizzled [KV_BQ x D] tile
+    static constexpr int Q_OFF = 0, DO_OFF = TILE;
+    static constexpr int VEC_OFF = 2 * TILE;       // lse * log2(e), then D: fp32, KV_BQ each
+    static constexpr int STAGE = 2 * TILE + 2 * KV_BQ * 2;  // 16-bit elements
 };
 
 template <typename T, int D, bool CAUSAL, bool ALIBI>
-__global__ __launch_bounds__(NT) void bwd_dkdv_kernel(Args a) {
+__global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
     using L = KvLds<D>;
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * L::STAGE];
 
@@ -127,7 +152,7 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(Args a) {
     const int steps = a.G * per_head;
     const float c2 = a.scale_log2;
 
-    uint4 greg[L::G_PER_THREAD][4];
+    TileStage<D, KV_BQ> sq, sdo;
     float vec_reg = 0.f;
     auto step_coords = [&](int st, int& h, int& q0) {
         const int hh = st / per_head;
@@ -137,20 +162,8 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(Args a) {
     auto gload = [&](int st) {
         int h, q0;
         step_coords(st, h, q0);
-#pragma unroll
-        for (int r = 0; r < L::G_PER_THREAD; ++r) {
-            const int gi = tid + r * NT;
-            const int tsel = gi / L::GROUPS;  // 0: Q, 1: dO
-            const int gl = gi % L::GROUPS;
-            const int dc = gl % (D / 8), rq = gl / (D / 8);
-            const T* base = reinterpret_cast<const T*>(tsel == 0 ? a.q : a.dout) + (size_t)h * D + dc * 8;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int qi = q0 + 4 * rq + e;
-                greg[r][e] = (gi < 2 * L::GROUPS && qi < len) ? ld_g16(base + (size_t)(row0 + qi) * ldq)
-                                                              : make_uint4(0, 0, 0, 0);
-            }
-        }
+        sq.load(reinterpret_cast<const T*>(a.q) + (size_t)row0 * ldq + (size_t)h * D, ldq, q0, len);
+        sdo.load(reinterpret_cast<const T*>(a.dout) + (size_t)row0 * ldq + (size_t)h * D, ldq, q0, len);
         if (tid < 2 * KV_BQ) {
             const int qi = q0 + (tid % KV_BQ);
             const size_t idx = ((size_t)b * a.H + h) * a.N + qi;
@@ -162,32 +175,13 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(Args a) {
     };
     auto swrite = [&](int stage) {
         uint16_t* S = smem + stage * L::STAGE;
-#pragma unroll
-        for (int r = 0; r < L::G_PER_THREAD; ++r) {
-            const int gi = tid + r * NT;
-            if (gi < 2 * L::GROUPS) {
-                const int tsel = gi / L::GROUPS;
-                const int gl = gi % L::GROUPS;
-                const int dc = gl % (D / 8), rq = gl / (D / 8);
-                uint16_t* rm = S + (tsel == 0 ? L::Q_OFF : L::DO_OFF);
-                uint16_t* tr = S + (tsel == 0 ? L::QT_OFF : L::DOT_OFF);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) st_s16(rm + (4 * rq + e) * L::RP + dc * 8, greg[r][e]);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint32_t lo = half_of(greg[r][0], e) | (half_of(greg[r][1], e) << 16);
-                    const uint32_t hi = half_of(greg[r][2], e) | (half_of(greg[r][3], e) << 16);
-                    st_s8(tr + (dc * 8 + e) * L::TP + 4 * rq, make_uint2(lo, hi));
-                }
-            }
-        }
+        sq.store(S + L::Q_OFF);
+        sdo.store(S + L::DO_OFF);
         if (tid < 2 * KV_BQ) reinterpret_cast<float*>(S + L::VEC_OFF)[tid] = vec_reg;
     };
 
-    if (steps > 0) {
-        gload(0);
-        swrite(0);
-    }
+    gload(0);
+    swrite(0);
     __syncthreads();
 
     for (int st = 0; st < steps; ++st) {
@@ -200,58 +194,64 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(Args a) {
         const bool active = (kw < len) && (!CAUSAL || q0 + KV_BQ - 1 >= kw);
         if (active) {
             const uint16_t* S = smem + stage * L::STAGE;
+            const uint16_t* Qs = S + L::Q_OFF;
+            const uint16_t* Ds = S + L::DO_OFF;
             const float* lse2 = reinterpret_cast<const float*>(S + L::VEC_OFF);
             const float* dsv = lse2 + KV_BQ;
 
             // S = Q K^T and dP = dO V^T: queries (rows) x keys (columns)
-            f32x16 s = f32x16{}, dp = f32x16{};
+            f32x16 s[KV_BQ / 32], dp[KV_BQ / 32];
 #pragma unroll
-            for (int kk = 0; kk < D / 16; ++kk) {
-                const V8<T> qa = as_v8<T>(ld_s16(S + L::Q_OFF + col * L::RP + 16 * kk + 8 * kg));
-                s = Mfma<T>::mma(qa, kf[kk], s);
-                const V8<T> da = as_v8<T>(ld_s16(S + L::DO_OFF + col * L::RP + 16 * kk + 8 * kg));
-                dp = Mfma<T>::mma(da, vf[kk], dp);
+            for (int qb = 0; qb < KV_BQ / 32; ++qb) {
+                s[qb] = f32x16{};
+                dp[qb] = f32x16{};
+#pragma unroll
+                for (int kk = 0; kk < D / 16; ++kk) {
+                    const int row = 32 * qb + col, c = 16 * kk + 8 * kg;
+                    s[qb] = Mfma<T>::mma(as_v8<T>(ld_s16(Qs + swz<D>(row, c))), kf[kk], s[qb]);
+                    dp[qb] = Mfma<T>::mma(as_v8<T>(ld_s16(Ds + swz<D>(row, c))), vf[kk], dp[qb]);
+                }
             }
 
             const float slope2 = ALIBI ? a.slopes[h] * kLog2e : 0.f;
             const bool need_mask = CAUSAL && (q0 < kw + 31);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float4 l4 = *reinterpret_cast<const float4*>(lse2 + 8 * i + 4 * kg);
-                const float4 d4 = *reinterpret_cast<const float4*>(dsv + 8 * i + 4 * kg);
-                const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-                const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+            for (int qb = 0; qb < KV_BQ / 32; ++qb) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int r = 4 * i + j;
-                    const int qi = q0 + 8 * i + 4 * kg + j;
-                    float t = s[r] * c2;
-                    if (ALIBI) {
-                        const float dist = (float)(qi - key);
-                        t -= slope2 * (CAUSAL ? dist : fabsf(dist));
+                for (int i = 0; i < 4; ++i) {
+                    const float4 l4 = *reinterpret_cast<const float4*>(lse2 + 32 * qb + 8 * i + 4 * kg);
+                    const float4 d4 = *reinterpret_cast<const float4*>(dsv + 32 * qb + 8 * i + 4 * kg);
+                    const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+                    const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int r = 4 * i + j;
+                        const int qi = q0 + 32 * qb + 8 * i + 4 * kg + j;
+                        float bias = -lv[j];
+                        if (ALIBI) {
+                            const float dist = (float)(qi - key);
+                            bias -= slope2 * (CAUSAL ? dist : fabsf(dist));
+                        }
+                        float p = exp2_fast(fmaf(s[qb][r], c2, bias));
+                        if (need_mask && key > qi) p = 0.f;
+                        s[qb][r] = p;
+                        dp[qb][r] = p * (dp[qb][r] - dv4[j]);
                     }
-                    float p = exp2_fast(t - lv[j]);
-                    if (need_mask && key > qi) p = 0.f;
-                    s[r] = p;
-                    dp[r] = p * (dp[r] - dv4[j]);
                 }
             }
 
             // dV^T += dO^T P and dK^T += Q^T dS, 16 queries per MFMA
 #pragma unroll
             for (int c = 0; c < KV_BQ / 16; ++c) {
-                const int r0 = 8 * c;
-                const V8<T> pb = pack8<T>(s[r0], s[r0 + 1], s[r0 + 2], s[r0 + 3], s[r0 + 4], s[r0 + 5], s[r0 + 6],
-                                          s[r0 + 7]);
-                const V8<T> db8 = pack8<T>(dp[r0], dp[r0 + 1], dp[r0 + 2], dp[r0 + 3], dp[r0 + 4], dp[r0 + 5],
-                                           dp[r0 + 6], dp[r0 + 7]);
+                const int qb = c >> 1, r0 = 8 * (c & 1);
+                const V8<T> pb = pack8<T>(s[qb][r0], s[qb][r0 + 1], s[qb][r0 + 2], s[qb][r0 + 3], s[qb][r0 + 4],
+                                          s[qb][r0 + 5], s[qb][r0 + 6], s[qb][r0 + 7]);
+                const V8<T> db8 = pack8<T>(dp[qb][r0], dp[qb][r0 + 1], dp[qb][r0 + 2], dp[qb][r0 + 3],
+                                           dp[qb][r0 + 4], dp[qb][r0 + 5], dp[qb][r0 + 6], dp[qb][r0 + 7]);
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
-                    const int trow = (32 * db + col) * L::TP + 16 * c + 4 * kg;
-                    const uint2 olo = ld_s8(S + L::DOT_OFF + trow), ohi = ld_s8(S + L::DOT_OFF + trow + 8);
-                    dvacc[db] = Mfma<T>::mma(as_v8<T>(make_uint4(olo.x, olo.y, ohi.x, ohi.y)), pb, dvacc[db]);
-                    const uint2 qlo = ld_s8(S + L::QT_OFF + trow), qhi = ld_s8(S + L::QT_OFF + trow + 8);
-                    dkacc[db] = Mfma<T>::mma(as_v8<T>(make_uint4(qlo.x, qlo.y, qhi.x, qhi.y)), db8, dkacc[db]);
+                    dvacc[db] = Mfma<T>::mma(as_v8<T>(ld_swz_rows_tr<D>(Ds, 16 * c, 32 * db, lane)), pb, dvacc[db]);
+                    dkacc[db] = Mfma<T>::mma(as_v8<T>(ld_swz_rows_tr<D>(Qs, 16 * c, 32 * db, lane)), db8, dkacc[db]);
                 }
             }
         }
@@ -285,18 +285,13 @@ constexpr int DQ_BK = 64;   // keys per K/V tile
 
 template <int D>
 struct DqLds {
-    static constexpr int RP = D + 8;        // K, V row-major pitch
-    static constexpr int TP = DQ_BK + 4;    // K^T pitch: 34 dwords, conflict-free b64 reads
-    static constexpr int ROW = DQ_BK * RP;
-    static constexpr int TR = D * TP;
-    static constexpr int K_OFF = 0, V_OFF = ROW, KT_OFF = 2 * ROW;
-    static constexpr int STAGE = 2 * ROW + TR;
-    static constexpr int GROUPS = (DQ_BK / 4) * (D / 8);  // (4 keys x 8 dims) groups per tensor
-    static constexpr int G_PER_THREAD = (2 * GROUPS + NT - 1) / NT;
+    static constexpr int TILE = DQ_BK * D;
+    static constexpr int K_OFF = 0, V_OFF = TILE;
+    static constexpr int STAGE = 2 * TILE;
 };
 
 template <typename T, int D, bool CAUSAL, bool ALIBI>
-__global__ __launch_bounds__(NT) void bwd_dq_kernel(Args a) {
+__global__ __launch_bounds__(NT, 1) void bwd_dq_kernel(Args a) {
     using L = DqLds<D>;
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * L::STAGE];
 
@@ -345,46 +340,15 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(Args a) {
     const T* Kg = reinterpret_cast<const T*>(a.k) + (size_t)row0 * ldk + (size_t)g * D;
     const T* Vg = reinterpret_cast<const T*>(a.v) + (size_t)row0 * ldk + (size_t)g * D;
 
-    uint4 greg[L::G_PER_THREAD][4];
+    TileStage<D, DQ_BK> sk, sv;
     auto gload = [&](int kt) {
-        const int k0 = kt * DQ_BK;
-#pragma unroll
-        for (int r = 0; r < L::G_PER_THREAD; ++r) {
-            const int gi = tid + r * NT;
-            const int tsel = gi / L::GROUPS;  // 0: K, 1: V
-            const int gl = gi % L::GROUPS;
-            const int dc = gl % (D / 8), rk = gl / (D / 8);
-            const T* base = (tsel == 0 ? Kg : Vg) + dc * 8;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int kj = k0 + 4 * rk + e;
-                greg[r][e] = (gi < 2 * L::GROUPS && kj < len) ? ld_g16(base + (size_t)kj * ldk)
-                                                              : make_uint4(0, 0, 0, 0);
-            }
-        }
+        sk.load(Kg, ldk, kt * DQ_BK, len);
+        sv.load(Vg, ldk, kt * DQ_BK, len);
     };
     auto swrite = [&](int stage) {
         uint16_t* S = smem + stage * L::STAGE;
-#pragma unroll
-        for (int r = 0; r < L::G_PER_THREAD; ++r) {
-            const int gi = tid + r * NT;
-            if (gi < 2 * L::GROUPS) {
-                const int tsel = gi / L::GROUPS;
-                const int gl = gi % L::GROUPS;
-                const int dc = gl % (D / 8), rk = gl / (D / 8);
-                uint16_t* rm = S + (tsel == 0 ? L::K_OFF : L::V_OFF);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) st_s16(rm + (4 * rk + e) * L::RP + dc * 8, greg[r][e]);
-                if (tsel == 0) {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const uint32_t lo = half_of(greg[r][0], e) | (half_of(greg[r][1], e) << 16);
-                        const uint32_t hi = half_of(greg[r][2], e) | (half_of(greg[r][3], e) << 16);
-                        st_s8(S + L::KT_OFF + (dc * 8 + e) * L::TP + 4 * rk, make_uint2(lo, hi));
-                    }
-                }
-            }
-        }
+        sk.store(S + L::K_OFF);
+        sv.store(S + L::V_OFF);
     };
 
     gload(0);
@@ -397,7 +361,8 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(Args a) {
         const int k0 = kt * DQ_BK;
         const bool active = wave_live && (!CAUSAL || k0 <= qw + 31);
         if (active) {
-            const uint16_t* S = smem + stage * L::STAGE;
+            const uint16_t* Ks = smem + stage * L::STAGE + L::K_OFF;
+            const uint16_t* Vs = smem + stage * L::STAGE + L::V_OFF;
             f32x16 s[DQ_BK / 32], dp[DQ_BK / 32];
 #pragma unroll
             for (int kb = 0; kb < DQ_BK / 32; ++kb) {
@@ -405,10 +370,9 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(Args a) {
                 dp[kb] = f32x16{};
 #pragma unroll
                 for (int kk = 0; kk < D / 16; ++kk) {
-                    const V8<T> ka = as_v8<T>(ld_s16(S + L::K_OFF + (32 * kb + col) * L::RP + 16 * kk + 8 * kg));
-                    s[kb] = Mfma<T>::mma(ka, qf[kk], s[kb]);
-                    const V8<T> va = as_v8<T>(ld_s16(S + L::V_OFF + (32 * kb + col) * L::RP + 16 * kk + 8 * kg));
-                    dp[kb] = Mfma<T>::mma(va, df[kk], dp[kb]);
+                    const int row = 32 * kb + col, c = 16 * kk + 8 * kg;
+                    s[kb] = Mfma<T>::mma(as_v8<T>(ld_s16(Ks + swz<D>(row, c))), qf[kk], s[kb]);
+                    dp[kb] = Mfma<T>::mma(as_v8<T>(ld_s16(Vs + swz<D>(row, c))), df[kk], dp[kb]);
                 }
             }
             const bool need_mask = (k0 + DQ_BK > len) || (CAUSAL && k0 + DQ_BK - 1 > qw);
@@ -417,12 +381,12 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(Args a) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int kj = k0 + 32 * kb + 8 * (r >> 2) + 4 * kg + (r & 3);
-                    float t = s[kb][r] * c2;
+                    float bias = -lse2;
                     if (ALIBI) {
                         const float dist = (float)(qi - kj);
-                        t -= slope2 * (CAUSAL ? dist : fabsf(dist));
+                        bias -= slope2 * (CAUSAL ? dist : fabsf(dist));
                     }
-                    float p = exp2_fast(t - lse2);
+                    float p = exp2_fast(fmaf(s[kb][r], c2, bias));
                     if (need_mask && (kj >= len || (CAUSAL && kj > qi))) p = 0.f;
                     dp[kb][r] = p * (dp[kb][r] - dsum);
                 }
@@ -434,11 +398,8 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(Args a) {
                 const V8<T> dsb = pack8<T>(dp[kb][r0], dp[kb][r0 + 1], dp[kb][r0 + 2], dp[kb][r0 + 3], dp[kb][r0 + 4],
                                            dp[kb][r0 + 5], dp[kb][r0 + 6], dp[kb][r0 + 7]);
 #pragma unroll
-                for (int db = 0; db < D / 32; ++db) {
-                    const int trow = L::KT_OFF + (32 * db + col) * L::TP + 16 * c + 4 * kg;
-                    const uint2 lo = ld_s8(S + trow), hi = ld_s8(S + trow + 8);
-                    dqacc[db] = Mfma<T>::mma(as_v8<T>(make_uint4(lo.x, lo.y, hi.x, hi.y)), dsb, dqacc[db]);
-                }
+                for (int db = 0; db < D / 32; ++db)
+                    dqacc[db] = Mfma<T>::mma(as_v8<T>(ld_swz_rows_tr<D>(Ks, 16 * c, 32 * db, lane)), dsb, dqacc[db]);
             }
         }
         if (kt + 1 < nkt) swrite(stage ^ 1);

@@ -114,6 +114,30 @@ __device__ __forceinline__ uint4 ld_s16_rows_tr(const uint16_t* tile, int pitch,
     return make_uint4(lo.x, lo.y, hi.x, hi.y);
 }
 
+// Swizzled 16-bit tile in LDS: rows of exactly D elements, and the 16-byte chunk
+// c of row r stored at chunk position c ^ f(r), f(r) = ((r & 3) * D / 32) ^ ((r >> 2) & 3).
+// With it, three access patterns are free of bank conflicts: 16-byte reads of
+// one chunk from 32 consecutive rows (row-major MFMA operands), the transposing
+// 8-byte reads of 4 rows x 64 bytes per half-wave (transposed operands), and
+// 16-byte writes of whole rows by consecutive lanes. `col` is a multiple of 4.
+template <int D>
+__device__ __forceinline__ int swz(int row, int col) {
+    const int f = ((row & 3) * (D / 32)) ^ ((row >> 2) & 3);
+    return row * D + (((col >> 3) ^ f) << 3) + (col & 7);
+}
+
+// Swizzled-tile variant of ld_s16_rows_tr: the MFMA A operand whose contraction
+// index runs along the rows, columns col0 + (lane % 32).
+template <int D>
+__device__ __forceinline__ uint4 ld_swz_rows_tr(const uint16_t* tile, int row0, int col0, int lane) {
+    const int r = lane & 15, grp = lane >> 4;
+    const int row = row0 + 4 * (grp >> 1) + (r >> 2);
+    const int col = col0 + 16 * (grp & 1) + 4 * (r & 3);
+    const uint2 lo = ld_s8_tr(tile + swz<D>(row, col));
+    const uint2 hi = ld_s8_tr(tile + swz<D>(row + 8, col));
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+
 // Sequence base row and length of batch entry / packed sequence b; lengths are
 // clamped to [0, N] so a malformed cu_seqlens cannot enlarge the grid's work.
 __device__ __forceinline__ void seq_bounds(const Args& a, int b, int& row0, int& len) {
