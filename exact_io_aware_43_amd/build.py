@@ -24,6 +24,8 @@ ARCH = "gfx950"
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary VGPRs: avoids AGPR<->VGPR copies around the softmax
+    "-mllvm", "-amdgpu-mfma-vgpr-form=true",
     "-I", os.path.join(ROOT, "include"),
     "-Wno-unused-command-line-argument",
 ]

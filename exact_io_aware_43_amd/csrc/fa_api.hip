@@ -48,9 +48,10 @@ fa::Args make_args(const void* q, const void* k, const void* v, int B, int H, in
     return a;
 }
 
+// D and lse * log2(e), fp32 each, laid out like lse: [B, H, N].
+size_t workspace_rows(int B, int H, int N) { return (size_t)B * (size_t)H * (size_t)N; }
 size_t workspace_bytes_for(int B, int H, int N) {
-    const size_t rows = (size_t)B * (size_t)H * (size_t)N;
-    return (rows * sizeof(float) + 255) & ~(size_t)255;
+    return (2 * workspace_rows(B, H, N) * sizeof(float) + 255) & ~(size_t)255;
 }
 
 }  // namespace
@@ -111,6 +112,7 @@ int fa_bwd_stages(const void* q, const void* k, const void* v, const void* o, co
     a.dk = dk;
     a.dv = dv;
     a.dsum = reinterpret_cast<float*>(workspace);
+    a.lse2 = a.dsum + workspace_rows(B, H, N);
     hipError_t e = fa::launch_bwd(a, (int)dtype, d, causal != 0, alibi_slopes != nullptr, stages,
                                   reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;

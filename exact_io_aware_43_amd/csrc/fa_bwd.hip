@@ -26,45 +26,22 @@
 // key column, and accumulates dV^T = dO^T P and dK^T = Q^T dS with P and dS as
 // B operands taken straight from the accumulators. The dQ kernel computes
 // S^T = K Q^T so that each lane owns one query, and accumulates
-// dQ^T = K^T dS^T. Tiles sit in LDS once, row-major and swizzled; the
+// dQ^T = K^T dS^T. Tiles are staged with direct global-to-LDS loads into
+// row-major LDS tiles whose 16-byte chunks are XOR-swizzled per row; the
 // transposed operands (dO^T, Q^T, K^T) come from the transposing LDS read.
+//
+// Workspace: D (fp32, laid out like lse) followed by L * log2(e) in the same
+// layout, both written by the pre-pass; positions past a packed sequence's end
+// get L * log2(e) = +inf and D = 0, so any row the later kernels read there
+// contributes exactly zero.
+#include <type_traits>
+
 #include "fa_device.hpp"
 
 namespace fa {
 namespace {
 
 constexpr int NT = 256;
-
-// Staging of a 16-bit [ROWS x D] tile from global rows (row stride `ld`
-// elements) into a swizzled LDS tile: global -> registers -> LDS, 16 bytes per
-// chunk, consecutive threads on consecutive chunks of a row. Rows at or past
-// `nrows` read as zero.
-template <int D, int ROWS>
-struct TileStage {
-    static constexpr int CHUNKS = ROWS * D / 8;
-    static constexpr int PER_THREAD = CHUNKS / NT;
-    static_assert(CHUNKS % NT == 0, "tile must split evenly over the workgroup");
-    uint4 r[PER_THREAD];
-
-    template <typename T>
-    __device__ __forceinline__ void load(const T* base, size_t ld, int row_start, int nrows) {
-#pragma unroll
-        for (int i = 0; i < PER_THREAD; ++i) {
-            const int c = threadIdx.x + i * NT;
-            const int row = c / (D / 8), col = 8 * (c % (D / 8));
-            r[i] = (row_start + row < nrows) ? ld_g16(base + (size_t)(row_start + row) * ld + col)
-                                             : make_uint4(0, 0, 0, 0);
-        }
-    }
-    __device__ __forceinline__ void store(uint16_t* tile) const {
-#pragma unroll
-        for (int i = 0; i < PER_THREAD; ++i) {
-            const int c = threadIdx.x + i * NT;
-            const int row = c / (D / 8), col = 8 * (c % (D / 8));
-            st_s16(tile + swz<D>(row, col), r[i]);
-        }
-    }
-};
 
 // ---------------------------------------------------------------- D = dO . O
 template <typename T, int D>
@@ -76,6 +53,7 @@ __global__ __launch_bounds__(NT) void bwd_dsum_kernel(Args a) {
     seq_bounds(a, b, row0, len);
     const int i = blockIdx.z * RPB + threadIdx.x / LPR;
     const int part = threadIdx.x % LPR;
+    if (i >= a.N) return;
     float acc = 0.f;
     if (i < len) {
         const size_t off = ((size_t)(row0 + i) * a.H + h) * D + part * 8;
@@ -87,25 +65,24 @@ __global__ __launch_bounds__(NT) void bwd_dsum_kernel(Args a) {
     }
 #pragma unroll
     for (int w = LPR / 2; w >= 1; w >>= 1) acc += __shfl_xor(acc, w);
-    if (i < len && part == 0) a.dsum[((size_t)b * a.H + h) * a.N + i] = acc;
+    if (part == 0) {
+        const size_t idx = ((size_t)b * a.H + h) * a.N + i;
+        a.dsum[idx] = (i < len) ? acc : 0.f;
+        a.lse2[idx] = (i < len) ? a.lse_in[idx] * kLog2e : INFINITY;
+    }
 }
 
 // ---------------------------------------------------------------- dK, dV
 constexpr int KV_BK = 128;  // keys per workgroup (32 per wave)
 constexpr int KV_BQ = 64;   // queries per step
 
-template <int D>
-struct KvLds {
-    static constexpr int TILE = KV_BQ * D;        // one swizzled [KV_BQ x D] tile
-    static constexpr int Q_OFF = 0, DO_OFF = TILE;
-    static constexpr int VEC_OFF = 2 * TILE;       // lse * log2(e), then D: fp32, KV_BQ each
-    static constexpr int STAGE = 2 * TILE + 2 * KV_BQ * 2;  // 16-bit elements
-};
-
 template <typename T, int D, bool CAUSAL, bool ALIBI>
 __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
-    using L = KvLds<D>;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * L::STAGE];
+    // stage: Q tile, dO tile (swizzled [KV_BQ x D] each), then L*log2(e) and D (fp32, KV_BQ each)
+    constexpr int TILE = KV_BQ * D;
+    constexpr int STAGE = 2 * TILE + 2 * KV_BQ * 2;
+    __shared__ __attribute__((aligned(16))) uint16_t stA[STAGE];
+    __shared__ __attribute__((aligned(16))) uint16_t stB[STAGE];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int col = lane & 31, kg = lane >> 5;
@@ -137,6 +114,15 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
         }
     }
 
+    int roff[D / 16], toff[D / 32][2];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) roff[kk] = swz_row_off<D>(lane, kk);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+        toff[db][0] = swz_tr_off<D>(lane, db, 0);
+        toff[db][1] = swz_tr_off<D>(lane, db, 1);
+    }
+
     f32x16 dkacc[D / 32], dvacc[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
@@ -145,76 +131,62 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
     }
 
     // Query tiles that can see this key tile: all of them, or (causal) those
-    // ending at or after k0.
+    // ending at or after k0; for every query head of the kv group.
     const int qt0 = CAUSAL ? k0 / KV_BQ : 0;
     const int nqt = (len + KV_BQ - 1) / KV_BQ;
     const int per_head = nqt - qt0;
     const int steps = a.G * per_head;
     const float c2 = a.scale_log2;
+    const T* Qb = reinterpret_cast<const T*>(a.q) + (size_t)row0 * ldq;
+    const T* Db = reinterpret_cast<const T*>(a.dout) + (size_t)row0 * ldq;
 
-    TileStage<D, KV_BQ> sq, sdo;
-    float vec_reg = 0.f;
     auto step_coords = [&](int st, int& h, int& q0) {
         const int hh = st / per_head;
         h = g * a.G + hh;
         q0 = (qt0 + st - hh * per_head) * KV_BQ;
     };
-    auto gload = [&](int st) {
+
+    DmaTile<D, KV_BQ, NT / 64> dma;
+    dma.init(wave, lane);
+    auto issue = [&](uint16_t* S, int st) {
         int h, q0;
         step_coords(st, h, q0);
-        sq.load(reinterpret_cast<const T*>(a.q) + (size_t)row0 * ldq + (size_t)h * D, ldq, q0, len);
-        sdo.load(reinterpret_cast<const T*>(a.dout) + (size_t)row0 * ldq + (size_t)h * D, ldq, q0, len);
-        if (tid < 2 * KV_BQ) {
-            const int qi = q0 + (tid % KV_BQ);
-            const size_t idx = ((size_t)b * a.H + h) * a.N + qi;
-            if (tid < KV_BQ)
-                vec_reg = (qi < len) ? a.lse_in[idx] * kLog2e : INFINITY;  // P = 0 on padding rows
-            else
-                vec_reg = (qi < len) ? a.dsum[idx] : 0.f;
-        }
-    };
-    auto swrite = [&](int stage) {
-        uint16_t* S = smem + stage * L::STAGE;
-        sq.store(S + L::Q_OFF);
-        sdo.store(S + L::DO_OFF);
-        if (tid < 2 * KV_BQ) reinterpret_cast<float*>(S + L::VEC_OFF)[tid] = vec_reg;
+        dma.issue(S, reinterpret_cast<const uint16_t*>(Qb + (size_t)h * D), ldq, q0, len, wave, lane);
+        dma.issue(S + TILE, reinterpret_cast<const uint16_t*>(Db + (size_t)h * D), ldq, q0, len, wave, lane);
+        // the pre-pass filled positions [len, N) with +inf / 0; stop at N
+        const size_t vbase = ((size_t)b * a.H + h) * a.N + q0;
+        if (wave == 0) dma_vec64(reinterpret_cast<float*>(S + 2 * TILE), a.lse2 + vbase, a.N - q0, INFINITY, lane);
+        if (wave == 1) dma_vec64(reinterpret_cast<float*>(S + 2 * TILE) + KV_BQ, a.dsum + vbase, a.N - q0, 0.f, lane);
     };
 
-    gload(0);
-    swrite(0);
-    __syncthreads();
-
-    for (int st = 0; st < steps; ++st) {
-        const int stage = st & 1;
-        if (st + 1 < steps) gload(st + 1);
+    auto compute = [&](const uint16_t* S, int st) {
         int h, q0;
         step_coords(st, h, q0);
         // wave-uniform skips: keys past the sequence end, or (causal) a query
         // tile entirely before this wave's first key
-        const bool active = (kw < len) && (!CAUSAL || q0 + KV_BQ - 1 >= kw);
-        if (active) {
-            const uint16_t* S = smem + stage * L::STAGE;
-            const uint16_t* Qs = S + L::Q_OFF;
-            const uint16_t* Ds = S + L::DO_OFF;
-            const float* lse2 = reinterpret_cast<const float*>(S + L::VEC_OFF);
-            const float* dsv = lse2 + KV_BQ;
+        if (!((kw < len) && (!CAUSAL || q0 + KV_BQ - 1 >= kw))) return;
+        const uint16_t* Qs = S;
+        const uint16_t* Ds = S + TILE;
+        const float* lse2 = reinterpret_cast<const float*>(S + 2 * TILE);
+        const float* dsv = lse2 + KV_BQ;
 
-            // S = Q K^T and dP = dO V^T: queries (rows) x keys (columns)
-            f32x16 s[KV_BQ / 32], dp[KV_BQ / 32];
+        // S = Q K^T and dP = dO V^T: queries (rows) x keys (columns)
+        f32x16 s[KV_BQ / 32], dp[KV_BQ / 32];
 #pragma unroll
-            for (int qb = 0; qb < KV_BQ / 32; ++qb) {
-                s[qb] = f32x16{};
-                dp[qb] = f32x16{};
+        for (int qb = 0; qb < KV_BQ / 32; ++qb) {
+            s[qb] = f32x16{};
+            dp[qb] = f32x16{};
 #pragma unroll
-                for (int kk = 0; kk < D / 16; ++kk) {
-                    const int row = 32 * qb + col, c = 16 * kk + 8 * kg;
-                    s[qb] = Mfma<T>::mma(as_v8<T>(ld_s16(Qs + swz<D>(row, c))), kf[kk], s[qb]);
-                    dp[qb] = Mfma<T>::mma(as_v8<T>(ld_s16(Ds + swz<D>(row, c))), vf[kk], dp[qb]);
-                }
+            for (int kk = 0; kk < D / 16; ++kk) {
+                s[qb] = Mfma<T>::mma(as_v8<T>(ld_s16(Qs + 32 * qb * D + roff[kk])), kf[kk], s[qb]);
+                dp[qb] = Mfma<T>::mma(as_v8<T>(ld_s16(Ds + 32 * qb * D + roff[kk])), vf[kk], dp[qb]);
             }
+        }
 
-            const float slope2 = ALIBI ? a.slopes[h] * kLog2e : 0.f;
-            const bool need_mask = CAUSAL && (q0 < kw + 31);
+        // P = exp2(S * scale * log2(e) - L * log2(e)) [+ ALiBi], dS = P (dP - D).
+        // Only tiles that straddle the diagonal take the masked path.
+        const float slope2 = ALIBI ? a.slopes[h] * kLog2e : 0.f;
+        auto softmax_bwd = [&](auto masked) {
 #pragma unroll
             for (int qb = 0; qb < KV_BQ / 32; ++qb) {
 #pragma unroll
@@ -233,31 +205,39 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
                             bias -= slope2 * (CAUSAL ? dist : fabsf(dist));
                         }
                         float p = exp2_fast(fmaf(s[qb][r], c2, bias));
-                        if (need_mask && key > qi) p = 0.f;
+                        if (decltype(masked)::value && key > qi) p = 0.f;
                         s[qb][r] = p;
                         dp[qb][r] = p * (dp[qb][r] - dv4[j]);
                     }
                 }
             }
+        };
+        if (CAUSAL && q0 < kw + 31)
+            softmax_bwd(std::true_type{});
+        else
+            softmax_bwd(std::false_type{});
 
-            // dV^T += dO^T P and dK^T += Q^T dS, 16 queries per MFMA
+        // dV^T += dO^T P and dK^T += Q^T dS, 16 queries per MFMA
 #pragma unroll
-            for (int c = 0; c < KV_BQ / 16; ++c) {
-                const int qb = c >> 1, r0 = 8 * (c & 1);
-                const V8<T> pb = pack8<T>(s[qb][r0], s[qb][r0 + 1], s[qb][r0 + 2], s[qb][r0 + 3], s[qb][r0 + 4],
-                                          s[qb][r0 + 5], s[qb][r0 + 6], s[qb][r0 + 7]);
-                const V8<T> db8 = pack8<T>(dp[qb][r0], dp[qb][r0 + 1], dp[qb][r0 + 2], dp[qb][r0 + 3],
-                                           dp[qb][r0 + 4], dp[qb][r0 + 5], dp[qb][r0 + 6], dp[qb][r0 + 7]);
+        for (int c = 0; c < KV_BQ / 16; ++c) {
+            const int qb = c >> 1, r0 = 8 * (c & 1);
+            const V8<T> pb = pack8<T>(s[qb][r0], s[qb][r0 + 1], s[qb][r0 + 2], s[qb][r0 + 3], s[qb][r0 + 4],
+                                      s[qb][r0 + 5], s[qb][r0 + 6], s[qb][r0 + 7]);
+            const V8<T> db8 = pack8<T>(dp[qb][r0], dp[qb][r0 + 1], dp[qb][r0 + 2], dp[qb][r0 + 3], dp[qb][r0 + 4],
+                                       dp[qb][r0 + 5], dp[qb][r0 + 6], dp[qb][r0 + 7]);
 #pragma unroll
-                for (int db = 0; db < D / 32; ++db) {
-                    dvacc[db] = Mfma<T>::mma(as_v8<T>(ld_swz_rows_tr<D>(Ds, 16 * c, 32 * db, lane)), pb, dvacc[db]);
-                    dkacc[db] = Mfma<T>::mma(as_v8<T>(ld_swz_rows_tr<D>(Qs, 16 * c, 32 * db, lane)), db8, dkacc[db]);
-                }
+            for (int db = 0; db < D / 32; ++db) {
+                const uint2 olo = ld_s8_tr(Ds + 16 * c * D + toff[db][0]);
+                const uint2 ohi = ld_s8_tr(Ds + 16 * c * D + toff[db][1]);
+                dvacc[db] = Mfma<T>::mma(as_v8<T>(make_uint4(olo.x, olo.y, ohi.x, ohi.y)), pb, dvacc[db]);
+                const uint2 qlo = ld_s8_tr(Qs + 16 * c * D + toff[db][0]);
+                const uint2 qhi = ld_s8_tr(Qs + 16 * c * D + toff[db][1]);
+                dkacc[db] = Mfma<T>::mma(as_v8<T>(make_uint4(qlo.x, qlo.y, qhi.x, qhi.y)), db8, dkacc[db]);
             }
         }
-        if (st + 1 < steps) swrite(stage ^ 1);
-        __syncthreads();
-    }
+    };
+
+    two_stage_loop(stA, stB, steps, issue, compute);
 
     // epilogue: lane owns key `key`; accumulator rows are dims 32*db + 8*i + 4*kg + 0..3
     if (key < len) {
@@ -283,17 +263,11 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
 constexpr int DQ_BQ = 128;  // queries per workgroup (32 per wave)
 constexpr int DQ_BK = 64;   // keys per K/V tile
 
-template <int D>
-struct DqLds {
-    static constexpr int TILE = DQ_BK * D;
-    static constexpr int K_OFF = 0, V_OFF = TILE;
-    static constexpr int STAGE = 2 * TILE;
-};
-
 template <typename T, int D, bool CAUSAL, bool ALIBI>
 __global__ __launch_bounds__(NT, 1) void bwd_dq_kernel(Args a) {
-    using L = DqLds<D>;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * L::STAGE];
+    constexpr int TILE = DQ_BK * D;  // stage: K tile then V tile, swizzled
+    __shared__ __attribute__((aligned(16))) uint16_t stA[2 * TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t stB[2 * TILE];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int col = lane & 31, kg = lane >> 5;
@@ -326,10 +300,19 @@ __global__ __launch_bounds__(NT, 1) void bwd_dq_kernel(Args a) {
         }
     }
     const size_t vidx = ((size_t)b * a.H + h) * a.N + qi;
-    const float lse2 = (qi < len) ? a.lse_in[vidx] * kLog2e : INFINITY;
+    const float lse2 = (qi < len) ? a.lse2[vidx] : INFINITY;
     const float dsum = (qi < len) ? a.dsum[vidx] : 0.f;
     const float c2 = a.scale_log2;
     const float slope2 = ALIBI ? a.slopes[h] * kLog2e : 0.f;
+
+    int roff[D / 16], toff[D / 32][2];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) roff[kk] = swz_row_off<D>(lane, kk);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+        toff[db][0] = swz_tr_off<D>(lane, db, 0);
+        toff[db][1] = swz_tr_off<D>(lane, db, 1);
+    }
 
     f32x16 dqacc[D / 32];
 #pragma unroll
@@ -340,42 +323,32 @@ __global__ __launch_bounds__(NT, 1) void bwd_dq_kernel(Args a) {
     const T* Kg = reinterpret_cast<const T*>(a.k) + (size_t)row0 * ldk + (size_t)g * D;
     const T* Vg = reinterpret_cast<const T*>(a.v) + (size_t)row0 * ldk + (size_t)g * D;
 
-    TileStage<D, DQ_BK> sk, sv;
-    auto gload = [&](int kt) {
-        sk.load(Kg, ldk, kt * DQ_BK, len);
-        sv.load(Vg, ldk, kt * DQ_BK, len);
-    };
-    auto swrite = [&](int stage) {
-        uint16_t* S = smem + stage * L::STAGE;
-        sk.store(S + L::K_OFF);
-        sv.store(S + L::V_OFF);
+    DmaTile<D, DQ_BK, NT / 64> dma;
+    dma.init(wave, lane);
+    auto issue = [&](uint16_t* S, int kt) {
+        dma.issue(S, reinterpret_cast<const uint16_t*>(Kg), ldk, kt * DQ_BK, len, wave, lane);
+        dma.issue(S + TILE, reinterpret_cast<const uint16_t*>(Vg), ldk, kt * DQ_BK, len, wave, lane);
     };
 
-    gload(0);
-    swrite(0);
-    __syncthreads();
-
-    for (int kt = 0; kt < nkt; ++kt) {
-        const int stage = kt & 1;
-        if (kt + 1 < nkt) gload(kt + 1);
+    auto compute = [&](const uint16_t* S, int kt) {
         const int k0 = kt * DQ_BK;
-        const bool active = wave_live && (!CAUSAL || k0 <= qw + 31);
-        if (active) {
-            const uint16_t* Ks = smem + stage * L::STAGE + L::K_OFF;
-            const uint16_t* Vs = smem + stage * L::STAGE + L::V_OFF;
-            f32x16 s[DQ_BK / 32], dp[DQ_BK / 32];
+        if (!(wave_live && (!CAUSAL || k0 <= qw + 31))) return;
+        const uint16_t* Ks = S;
+        const uint16_t* Vs = S + TILE;
+        f32x16 s[DQ_BK / 32], dp[DQ_BK / 32];
 #pragma unroll
-            for (int kb = 0; kb < DQ_BK / 32; ++kb) {
-                s[kb] = f32x16{};
-                dp[kb] = f32x16{};
+        for (int kb = 0; kb < DQ_BK / 32; ++kb) {
+            s[kb] = f32x16{};
+            dp[kb] = f32x16{};
 #pragma unroll
-                for (int kk = 0; kk < D / 16; ++kk) {
-                    const int row = 32 * kb + col, c = 16 * kk + 8 * kg;
-                    s[kb] = Mfma<T>::mma(as_v8<T>(ld_s16(Ks + swz<D>(row, c))), qf[kk], s[kb]);
-                    dp[kb] = Mfma<T>::mma(as_v8<T>(ld_s16(Vs + swz<D>(row, c))), df[kk], dp[kb]);
-                }
+            for (int kk = 0; kk < D / 16; ++kk) {
+                s[kb] = Mfma<T>::mma(as_v8<T>(ld_s16(Ks + 32 * kb * D + roff[kk])), qf[kk], s[kb]);
+                dp[kb] = Mfma<T>::mma(as_v8<T>(ld_s16(Vs + 32 * kb * D + roff[kk])), df[kk], dp[kb]);
             }
-            const bool need_mask = (k0 + DQ_BK > len) || (CAUSAL && k0 + DQ_BK - 1 > qw);
+        }
+        // dS^T = P^T (dP^T - D), P^T = exp2(S^T * scale * log2(e) - L * log2(e)) [+ ALiBi];
+        // only tiles with keys past the end or across the diagonal take the masked path.
+        auto softmax_bwd = [&](auto masked) {
 #pragma unroll
             for (int kb = 0; kb < DQ_BK / 32; ++kb) {
 #pragma unroll
@@ -387,24 +360,31 @@ __global__ __launch_bounds__(NT, 1) void bwd_dq_kernel(Args a) {
                         bias -= slope2 * (CAUSAL ? dist : fabsf(dist));
                     }
                     float p = exp2_fast(fmaf(s[kb][r], c2, bias));
-                    if (need_mask && (kj >= len || (CAUSAL && kj > qi))) p = 0.f;
+                    if (decltype(masked)::value && (kj >= len || (CAUSAL && kj > qi))) p = 0.f;
                     dp[kb][r] = p * (dp[kb][r] - dsum);
                 }
             }
-            // dQ^T += K^T dS^T, 16 keys per MFMA
+        };
+        if ((k0 + DQ_BK > len) || (CAUSAL && k0 + DQ_BK - 1 > qw))
+            softmax_bwd(std::true_type{});
+        else
+            softmax_bwd(std::false_type{});
+        // dQ^T += K^T dS^T, 16 keys per MFMA
 #pragma unroll
-            for (int c = 0; c < DQ_BK / 16; ++c) {
-                const int kb = c >> 1, r0 = 8 * (c & 1);
-                const V8<T> dsb = pack8<T>(dp[kb][r0], dp[kb][r0 + 1], dp[kb][r0 + 2], dp[kb][r0 + 3], dp[kb][r0 + 4],
-                                           dp[kb][r0 + 5], dp[kb][r0 + 6], dp[kb][r0 + 7]);
+        for (int c = 0; c < DQ_BK / 16; ++c) {
+            const int kb = c >> 1, r0 = 8 * (c & 1);
+            const V8<T> dsb = pack8<T>(dp[kb][r0], dp[kb][r0 + 1], dp[kb][r0 + 2], dp[kb][r0 + 3], dp[kb][r0 + 4],
+                                       dp[kb][r0 + 5], dp[kb][r0 + 6], dp[kb][r0 + 7]);
 #pragma unroll
-                for (int db = 0; db < D / 32; ++db)
-                    dqacc[db] = Mfma<T>::mma(as_v8<T>(ld_swz_rows_tr<D>(Ks, 16 * c, 32 * db, lane)), dsb, dqacc[db]);
+            for (int db = 0; db < D / 32; ++db) {
+                const uint2 lo = ld_s8_tr(Ks + 16 * c * D + toff[db][0]);
+                const uint2 hi = ld_s8_tr(Ks + 16 * c * D + toff[db][1]);
+                dqacc[db] = Mfma<T>::mma(as_v8<T>(make_uint4(lo.x, lo.y, hi.x, hi.y)), dsb, dqacc[db]);
             }
         }
-        if (kt + 1 < nkt) swrite(stage ^ 1);
-        __syncthreads();
-    }
+    };
+
+    two_stage_loop(stA, stB, nkt, issue, compute);
 
     if (qi < len) {
         T* dQ = reinterpret_cast<T*>(a.dq) + (size_t)(row0 + qi) * ldq + (size_t)h * D;

@@ -138,6 +138,109 @@ __device__ __forceinline__ uint4 ld_swz_rows_tr(const uint16_t* tile, int row0, 
     return make_uint4(lo.x, lo.y, hi.x, hi.y);
 }
 
+// Row-major operand read from a swizzled tile: element offset of (row, col) for
+// row = 32 * blk + (lane % 32), col = 16 * kk + 8 * (lane / 32). The block
+// part is the constant 32 * blk * D because the swizzle depends on row % 16
+// only; this returns the lane part, to be kept in a register for each kk.
+template <int D>
+__device__ __forceinline__ int swz_row_off(int lane, int kk) {
+    return swz<D>(lane & 31, 16 * kk + 8 * (lane >> 5));
+}
+
+// Transposed operand read from a swizzled tile (see ld_swz_rows_tr): lane part
+// of the offset of the low (half = 0) or high (half = 1) 8-byte read for
+// columns 32 * db + ...; rows 16 * c + ... add the constant 16 * c * D.
+template <int D>
+__device__ __forceinline__ int swz_tr_off(int lane, int db, int half) {
+    const int r = lane & 15, grp = lane >> 4;
+    return swz<D>(8 * half + 4 * (grp >> 1) + (r >> 2), 32 * db + 16 * (grp & 1) + 4 * (r & 3));
+}
+
+// Direct global -> LDS staging (global_load_lds_dwordx4) of a [ROWS x D]
+// 16-bit tile into a swizzled LDS tile. Each instruction of a wave fills 1 KB
+// of LDS, lane L writing bytes 16 L .. 16 L + 15; the lane fetches from global
+// memory the 16-byte chunk that belongs at that position. Rows at or past
+// `nrows` are zero-filled with an ordinary LDS store instead. `NW` waves share
+// the tile. The loads complete asynchronously (vmcnt); callers wait and
+// barrier before reading the tile.
+template <int D, int ROWS, int NW>
+struct DmaTile {
+    static constexpr int INSTR = ROWS * D * 2 / 1024;
+    static constexpr int PER_WAVE = INSTR / NW;
+    static_assert(INSTR % NW == 0, "tile must split evenly over the waves");
+    int grow_off[PER_WAVE];  // row within the tile, per instruction
+    int gcol[PER_WAVE];      // global column (elements) of this lane's chunk
+
+    __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+        for (int i = 0; i < PER_WAVE; ++i) {
+            const int p = (wave * PER_WAVE + i) * 64 + lane;  // chunk index in LDS order
+            const int row = p / (D / 8), pos = p % (D / 8);
+            const int f = ((row & 3) * (D / 32)) ^ ((row >> 2) & 3);
+            grow_off[i] = row;
+            gcol[i] = 8 * (pos ^ f);
+        }
+    }
+
+    // `base` is the 16-bit element array (any 16-bit type viewed as uint16_t).
+    __device__ __forceinline__ void issue(uint16_t* tile, const uint16_t* base, size_t ld, int row_start, int nrows,
+                                          int wave, int lane) const {
+        typedef __attribute__((address_space(3))) void lds_void;
+        typedef __attribute__((address_space(1))) void gbl_void;  // explicit: see dma_vec64
+#pragma unroll
+        for (int i = 0; i < PER_WAVE; ++i) {
+            uint16_t* dst = tile + (wave * PER_WAVE + i) * 512;  // 1 KB per instruction
+            const int row = row_start + grow_off[i];
+            if (row < nrows) {
+                __builtin_amdgcn_global_load_lds((gbl_void*)(base + (size_t)row * ld + gcol[i]),
+                                                 (lds_void*)((__attribute__((address_space(3))) uint16_t*)dst), 16,
+                                                 0, 0);
+            } else {
+                st_s16(dst + 8 * lane, make_uint4(0, 0, 0, 0));
+            }
+        }
+    }
+};
+
+// Direct global -> LDS load of 64 consecutive fp32 values (one wave, 4 bytes per
+// lane) from `src` into `dst`; lanes whose index is at or past `n` store `fill`
+// instead.
+// The global pointer is cast to the global address space explicitly: left
+// implicit, the conversion is rejected in the host compilation pass, which
+// then silently drops the host launch stubs of every kernel that uses it.
+__device__ __forceinline__ void dma_vec64(float* dst, const float* src, int n, float fill, int lane) {
+    typedef __attribute__((address_space(3))) void lds_void;
+    typedef __attribute__((address_space(1))) void gbl_void;
+    if (lane < n)
+        __builtin_amdgcn_global_load_lds((gbl_void*)(src + lane),
+                                         (lds_void*)((__attribute__((address_space(3))) float*)dst), 4, 0, 0);
+    else
+        dst[lane] = fill;
+}
+
+// The double-buffered tile loop shared by the kernels: body(stage, i) runs for
+// i in [0, n) while issue(other stage, i + 1) prefetches the next tile. The two
+// stages are distinct __shared__ arrays so that the compiler can tell the
+// prefetch's LDS writes apart from the body's LDS reads and does not wait for
+// the prefetch before reading.
+template <class Issue, class Body>
+__device__ __forceinline__ void two_stage_loop(uint16_t* A, uint16_t* B, int n, Issue&& issue, Body&& body) {
+    issue(A, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int i = 0; i < n; i += 2) {
+        if (i + 1 < n) issue(B, i + 1);
+        body(static_cast<const uint16_t*>(A), i);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (i + 1 >= n) break;
+        if (i + 2 < n) issue(A, i + 2);
+        body(static_cast<const uint16_t*>(B), i + 1);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+}
+
 // Sequence base row and length of batch entry / packed sequence b; lengths are
 // clamped to [0, N] so a malformed cu_seqlens cannot enlarge the grid's work.
 __device__ __forceinline__ void seq_bounds(const Args& a, int b, int& row0, int& len) {

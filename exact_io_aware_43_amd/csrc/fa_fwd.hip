@@ -10,7 +10,7 @@
 // Work decomposition. One workgroup of 4 waves owns BR = 128 query rows of one
 // (sequence, query head); each wave owns 32 of them. K and V of the head's kv
 // head stream through LDS in tiles of BC = 64 keys, double buffered: the next
-// tile's global loads are in flight while the current tile is multiplied. Two
+// tile's loads are in flight while the current tile is multiplied. Two
 // workgroups share a compute unit, so each SIMD interleaves the matrix work of
 // one wave with the softmax of the other.
 //
@@ -20,8 +20,10 @@
 // in-lane reductions plus one exchange with lane l ^ 32. The output is
 // accumulated transposed as well, O^T += V^T P^T, which takes P^T straight
 // from the score accumulator as the B operand and keeps the per-query rescale
-// factor in-lane. V stays row-major in LDS; its transposed operand comes from
-// the transposing LDS read.
+// factor in-lane. K and V are staged with direct global-to-LDS loads into
+// row-major tiles whose 16-byte chunks are XOR-swizzled per row (free of bank
+// conflicts for the row-wise K reads and the transposing V reads); the
+// transposed V operand comes from the transposing LDS read.
 //
 // Softmax bookkeeping. Scores are kept in log2 units (scale * log2(e) folded
 // into one FMA before exp2). The reference maximum m is only raised when a
@@ -43,25 +45,14 @@ constexpr int BC = 64;     // keys per K/V tile
 constexpr int NT = 256;    // threads per workgroup (4 waves)
 constexpr float TAU = 8.f; // lazy-rescale threshold, log2 units
 
-template <int D>
-struct FwdLds {
-    // K: row-major, pitch = D + 8 elements (b128 reads of 16 keys hit distinct banks).
-    // V: row-major, pitch = D + 32 elements (the transposing b64 reads of 4 rows x 64 B
-    //    per half-wave hit distinct banks).
-    static constexpr int KP = D + 8;
-    static constexpr int VP = D + 32;
-    static constexpr int KT = BC * KP;
-    static constexpr int VT = BC * VP;
-    static constexpr int STAGE = KT + VT;
-    static constexpr int CHUNKS = BC * D / 8;             // 16-byte chunks per tile (each of K, V)
-    static constexpr int LOADS = CHUNKS / NT;             // per thread, per tensor
-    static_assert(CHUNKS % NT == 0, "tile must split evenly over the workgroup");
-};
-
 template <typename T, int D, bool CAUSAL, bool ALIBI>
 __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(Args a) {
-    using L = FwdLds<D>;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * L::STAGE];
+    // Two named K/V stages (swizzled [BC x D] tiles, K then V): the prefetch
+    // into one overlaps the reads of the other, which the compiler can only
+    // prove independent when they are distinct arrays.
+    constexpr int TILE = BC * D;
+    __shared__ __attribute__((aligned(16))) uint16_t stA[2 * TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t stB[2 * TILE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -100,34 +91,24 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(Args a) {
         qf[kk] = as_v8<T>(u);
     }
 
+    // lane parts of the LDS operand offsets (loop invariant)
+    int roff[D / 16], toff[D / 32][2];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) roff[kk] = swz_row_off<D>(lane, kk);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+        toff[db][0] = swz_tr_off<D>(lane, db, 0);
+        toff[db][1] = swz_tr_off<D>(lane, db, 1);
+    }
+
     const int kend = CAUSAL ? min(len, q0 + BR) : len;
     const int nkt = (kend + BC - 1) / BC;
 
-    // ---- cooperative K/V staging: global -> registers -> LDS, 16 bytes per chunk.
-    // Chunk c of a tile is (key c / (D/8), dims 8 * (c % (D/8))); consecutive
-    // threads read consecutive 16 bytes of one key row.
-    uint4 kreg[L::LOADS], vreg[L::LOADS];
-    auto gload = [&](int kt) {
-        const int k0 = kt * BC;
-#pragma unroll
-        for (int r = 0; r < L::LOADS; ++r) {
-            const int c = tid + r * NT;
-            const int key = k0 + c / (D / 8), dc = 8 * (c % (D / 8));
-            const bool ok = key < len;
-            kreg[r] = ok ? ld_g16(Kg + (size_t)key * ldk + dc) : make_uint4(0, 0, 0, 0);
-            vreg[r] = ok ? ld_g16(Vg + (size_t)key * ldk + dc) : make_uint4(0, 0, 0, 0);
-        }
-    };
-    auto swrite = [&](int stage) {
-        uint16_t* Ks = smem + stage * L::STAGE;
-        uint16_t* Vs = Ks + L::KT;
-#pragma unroll
-        for (int r = 0; r < L::LOADS; ++r) {
-            const int c = tid + r * NT;
-            const int key = c / (D / 8), dc = 8 * (c % (D / 8));
-            st_s16(Ks + key * L::KP + dc, kreg[r]);
-            st_s16(Vs + key * L::VP + dc, vreg[r]);
-        }
+    DmaTile<D, BC, NT / 64> dma;
+    dma.init(wave, lane);
+    auto issue = [&](uint16_t* st, int kt) {
+        dma.issue(st, reinterpret_cast<const uint16_t*>(Kg), ldk, kt * BC, len, wave, lane);
+        dma.issue(st + TILE, reinterpret_cast<const uint16_t*>(Vg), ldk, kt * BC, len, wave, lane);
     };
 
     f32x16 oacc[D / 32];
@@ -139,106 +120,96 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(Args a) {
     const float c2 = a.scale_log2;
     const float slope2 = ALIBI ? a.slopes[h] * kLog2e : 0.f;
 
-    gload(0);
-    swrite(0);
-    __syncthreads();
-
-    for (int kt = 0; kt < nkt; ++kt) {
-        const int stage = kt & 1;
-        if (kt + 1 < nkt) gload(kt + 1);
+    auto compute = [&](const uint16_t* Ks, int kt) {
+        const uint16_t* Vs = Ks + TILE;
         const int k0 = kt * BC;
         // wave-uniform: skip tiles that are entirely above this wave's diagonal
-        const bool active = wave_live && (!CAUSAL || k0 <= qw + 31);
-        if (active) {
-            const uint16_t* Ks = smem + stage * L::STAGE;
-            const uint16_t* Vs = Ks + L::KT;
+        if (!(wave_live && (!CAUSAL || k0 <= qw + 31))) return;
 
-            // S^T = K Q^T for BC keys x 32 queries (raw, unscaled scores)
-            f32x16 s[BC / 32];
+        // S^T = K Q^T for BC keys x 32 queries (raw, unscaled scores)
+        f32x16 s[BC / 32];
 #pragma unroll
-            for (int kb = 0; kb < BC / 32; ++kb) {
-                s[kb] = f32x16{};
+        for (int kb = 0; kb < BC / 32; ++kb) {
+            s[kb] = f32x16{};
 #pragma unroll
-                for (int kk = 0; kk < D / 16; ++kk) {
-                    const V8<T> kf = as_v8<T>(ld_s16(Ks + (32 * kb + col) * L::KP + 16 * kk + 8 * kg));
-                    s[kb] = Mfma<T>::mma(kf, qf[kk], s[kb]);
-                }
-            }
+            for (int kk = 0; kk < D / 16; ++kk)
+                s[kb] = Mfma<T>::mma(as_v8<T>(ld_s16(Ks + 32 * kb * D + roff[kk])), qf[kk], s[kb]);
+        }
 
-            // Scores in log2 units. Plain tiles keep the raw score and fold the
-            // scale into the exponent's FMA; ALiBi and edge tiles materialise
-            // t = s * c2 + bias (or -inf when masked) and use scale 1 below.
-            const bool edge = (k0 + BC > len) || (CAUSAL && k0 + BC - 1 > qw);
-            const bool materialise = ALIBI || edge;
-            float mt;
-            if (materialise) {
-                mt = -INFINITY;
-#pragma unroll
-                for (int kb = 0; kb < BC / 32; ++kb) {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * kg + (r & 3);
-                        float t = s[kb][r] * c2;
-                        if (ALIBI) {
-                            const float dist = (float)(qi - key);
-                            t -= slope2 * (CAUSAL ? dist : fabsf(dist));
-                        }
-                        if (edge && (key >= len || (CAUSAL && key > qi))) t = -INFINITY;
-                        s[kb][r] = t;
-                        mt = fmaxf(mt, t);
-                    }
-                }
-            } else {
-                float mx = s[0][0];
-#pragma unroll
-                for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-                mt = mx * c2;
-            }
-            mt = fmaxf(mt, __shfl_xor(mt, 32));
-
-            // lazy rescale: raise the reference only when the tile max exceeds it by > TAU
-            const bool raise = mt > m_ref + TAU;
-            if (__any(raise)) {
-                const float m_new = raise ? mt : m_ref;
-                const float alpha = exp2_fast(m_ref - m_new);  // 0 on the first tile
-                l_run *= alpha;
-#pragma unroll
-                for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
-                m_ref = m_new;
-            }
-            const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;  // rows with no key yet
-
-            const float sc = materialise ? 1.f : c2;
-            float ls = 0.f;
+        // Scores in log2 units. Plain tiles keep the raw score and fold the
+        // scale into the exponent's FMA; ALiBi and edge tiles materialise
+        // t = s * c2 + bias (or -inf when masked) and use scale 1 below.
+        const bool edge = (k0 + BC > len) || (CAUSAL && k0 + BC - 1 > qw);
+        const bool materialise = ALIBI || edge;
+        float mt;
+        if (materialise) {
+            mt = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < BC / 32; ++kb) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const float p = exp2_fast(fmaf(s[kb][r], sc, -m_use));
-                    s[kb][r] = p;
-                    ls += p;
+                    const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * kg + (r & 3);
+                    float t = s[kb][r] * c2;
+                    if (ALIBI) {
+                        const float dist = (float)(qi - key);
+                        t -= slope2 * (CAUSAL ? dist : fabsf(dist));
+                    }
+                    if (edge && (key >= len || (CAUSAL && key > qi))) t = -INFINITY;
+                    s[kb][r] = t;
+                    mt = fmaxf(mt, t);
                 }
             }
-            l_run += ls;
+        } else {
+            float mx = s[0][0];
+#pragma unroll
+            for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+            mt = mx * c2;
+        }
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
 
-            // O^T += V^T P^T, 16 keys per MFMA
+        // lazy rescale: raise the reference only when the tile max exceeds it by > TAU
+        const bool raise = mt > m_ref + TAU;
+        if (__any(raise)) {
+            const float m_new = raise ? mt : m_ref;
+            const float alpha = exp2_fast(m_ref - m_new);  // 0 on the first tile
+            l_run *= alpha;
 #pragma unroll
-            for (int c = 0; c < BC / 16; ++c) {
-                const int kb = c >> 1, r0 = 8 * (c & 1);
-                const V8<T> pf = pack8<T>(s[kb][r0 + 0], s[kb][r0 + 1], s[kb][r0 + 2], s[kb][r0 + 3],
-                                          s[kb][r0 + 4], s[kb][r0 + 5], s[kb][r0 + 6], s[kb][r0 + 7]);
+            for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+            m_ref = m_new;
+        }
+        const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;  // rows with no key yet
+
+        const float sc = materialise ? 1.f : c2;
+        float ls = 0.f;
 #pragma unroll
-                for (int db = 0; db < D / 32; ++db) {
-                    const V8<T> vf = as_v8<T>(ld_s16_rows_tr(Vs, L::VP, 16 * c, 32 * db, lane));
-                    oacc[db] = Mfma<T>::mma(vf, pf, oacc[db]);
-                }
+        for (int kb = 0; kb < BC / 32; ++kb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = exp2_fast(fmaf(s[kb][r], sc, -m_use));
+                s[kb][r] = p;
+                ls += p;
             }
         }
-        if (kt + 1 < nkt) swrite(stage ^ 1);
-        __syncthreads();
-    }
+        l_run += ls;
+
+        // O^T += V^T P^T, 16 keys per MFMA
+#pragma unroll
+        for (int c = 0; c < BC / 16; ++c) {
+            const int kb = c >> 1, r0 = 8 * (c & 1);
+            const V8<T> pf = pack8<T>(s[kb][r0 + 0], s[kb][r0 + 1], s[kb][r0 + 2], s[kb][r0 + 3], s[kb][r0 + 4],
+                                      s[kb][r0 + 5], s[kb][r0 + 6], s[kb][r0 + 7]);
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+                const uint2 lo = ld_s8_tr(Vs + 16 * c * D + toff[db][0]);
+                const uint2 hi = ld_s8_tr(Vs + 16 * c * D + toff[db][1]);
+                oacc[db] = Mfma<T>::mma(as_v8<T>(make_uint4(lo.x, lo.y, hi.x, hi.y)), pf, oacc[db]);
+            }
+        }
+    };
+
+    two_stage_loop(stA, stB, nkt, issue, compute);
 
     // ---- epilogue: O = O_acc / l, lse = (m + log2 l) * ln 2
     const float l_tot = l_run + __shfl_xor(l_run, 32);

@@ -22,7 +22,8 @@ struct Args {
     void* dq;
     void* dk;
     void* dv;
-    float* dsum;       // backward: D_i = dO_i . O_i, laid out like lse
+    float* dsum;       // backward workspace: D_i = dO_i . O_i, laid out like lse
+    float* lse2;       // backward workspace: lse * log2(e), laid out like lse
     const float* slopes;
     const int* cu;
     int B, H, Hkv, N, G;
