@@ -170,17 +170,33 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
         const float* lse2 = reinterpret_cast<const float*>(S + 2 * TILE);
         const float* dsv = lse2 + KV_BQ;
 
-        // S = Q K^T and dP = dO V^T: queries (rows) x keys (columns)
+        // S = Q K^T and dP = dO V^T: queries (rows) x keys (columns). The
+        // operand loads run two (qb, kk) groups ahead of the MFMAs; the
+        // scheduling barriers keep that order (left alone, the scheduler
+        // issues each load just before its MFMA and waits out its latency).
+        constexpr int NG1 = KV_BQ / 32 * D / 16;
         f32x16 s[KV_BQ / 32], dp[KV_BQ / 32];
 #pragma unroll
         for (int qb = 0; qb < KV_BQ / 32; ++qb) {
             s[qb] = f32x16{};
             dp[qb] = f32x16{};
+        }
+        uint4 fq[3], fd[3];
+        auto load1 = [&](int gi) {
+            const int qb = gi / (D / 16), kk = gi % (D / 16);
+            fq[gi % 3] = ld_s16(Qs + 32 * qb * D + roff[kk]);
+            fd[gi % 3] = ld_s16(Ds + 32 * qb * D + roff[kk]);
+        };
+        load1(0);
+        load1(1);
 #pragma unroll
-            for (int kk = 0; kk < D / 16; ++kk) {
-                s[qb] = Mfma<T>::mma(as_v8<T>(ld_s16(Qs + 32 * qb * D + roff[kk])), kf[kk], s[qb]);
-                dp[qb] = Mfma<T>::mma(as_v8<T>(ld_s16(Ds + 32 * qb * D + roff[kk])), vf[kk], dp[qb]);
-            }
+        for (int gi = 0; gi < NG1; ++gi) {
+            if (gi + 2 < NG1) load1(gi + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            const int qb = gi / (D / 16), kk = gi % (D / 16);
+            s[qb] = Mfma<T>::mma(as_v8<T>(fq[gi % 3]), kf[kk], s[qb]);
+            dp[qb] = Mfma<T>::mma(as_v8<T>(fd[gi % 3]), vf[kk], dp[qb]);
+            __builtin_amdgcn_sched_barrier(0);
         }
 
         // P = exp2(S * scale * log2(e) - L * log2(e)) [+ ALiBi], dS = P (dP - D).
@@ -217,23 +233,38 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
         else
             softmax_bwd(std::false_type{});
 
-        // dV^T += dO^T P and dK^T += Q^T dS, 16 queries per MFMA
+        // dV^T += dO^T P and dK^T += Q^T dS, 16 queries per MFMA; transposed
+        // operand loads run two (c, db) groups ahead as above.
+        constexpr int NG2 = KV_BQ / 16 * D / 32;
+        V8<T> pb[KV_BQ / 16], db8[KV_BQ / 16];
 #pragma unroll
         for (int c = 0; c < KV_BQ / 16; ++c) {
             const int qb = c >> 1, r0 = 8 * (c & 1);
-            const V8<T> pb = pack8<T>(s[qb][r0], s[qb][r0 + 1], s[qb][r0 + 2], s[qb][r0 + 3], s[qb][r0 + 4],
-                                      s[qb][r0 + 5], s[qb][r0 + 6], s[qb][r0 + 7]);
-            const V8<T> db8 = pack8<T>(dp[qb][r0], dp[qb][r0 + 1], dp[qb][r0 + 2], dp[qb][r0 + 3], dp[qb][r0 + 4],
-                                       dp[qb][r0 + 5], dp[qb][r0 + 6], dp[qb][r0 + 7]);
+            pb[c] = pack8<T>(s[qb][r0], s[qb][r0 + 1], s[qb][r0 + 2], s[qb][r0 + 3], s[qb][r0 + 4], s[qb][r0 + 5],
+                             s[qb][r0 + 6], s[qb][r0 + 7]);
+            db8[c] = pack8<T>(dp[qb][r0], dp[qb][r0 + 1], dp[qb][r0 + 2], dp[qb][r0 + 3], dp[qb][r0 + 4],
+                              dp[qb][r0 + 5], dp[qb][r0 + 6], dp[qb][r0 + 7]);
+        }
+        uint4 fo[3], fqt[3];
+        auto load2 = [&](int gi) {
+            const int c = gi / (D / 32), db = gi % (D / 32);
+            const uint2 olo = ld_s8_tr(Ds + 16 * c * D + toff[db][0]);
+            const uint2 ohi = ld_s8_tr(Ds + 16 * c * D + toff[db][1]);
+            const uint2 qlo = ld_s8_tr(Qs + 16 * c * D + toff[db][0]);
+            const uint2 qhi = ld_s8_tr(Qs + 16 * c * D + toff[db][1]);
+            fo[gi % 3] = make_uint4(olo.x, olo.y, ohi.x, ohi.y);
+            fqt[gi % 3] = make_uint4(qlo.x, qlo.y, qhi.x, qhi.y);
+        };
+        load2(0);
+        load2(1);
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-                const uint2 olo = ld_s8_tr(Ds + 16 * c * D + toff[db][0]);
-                const uint2 ohi = ld_s8_tr(Ds + 16 * c * D + toff[db][1]);
-                dvacc[db] = Mfma<T>::mma(as_v8<T>(make_uint4(olo.x, olo.y, ohi.x, ohi.y)), pb, dvacc[db]);
-                const uint2 qlo = ld_s8_tr(Qs + 16 * c * D + toff[db][0]);
-                const uint2 qhi = ld_s8_tr(Qs + 16 * c * D + toff[db][1]);
-                dkacc[db] = Mfma<T>::mma(as_v8<T>(make_uint4(qlo.x, qlo.y, qhi.x, qhi.y)), db8, dkacc[db]);
-            }
+        for (int gi = 0; gi < NG2; ++gi) {
+            if (gi + 2 < NG2) load2(gi + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            const int c = gi / (D / 32), db = gi % (D / 32);
+            dvacc[db] = Mfma<T>::mma(as_v8<T>(fo[gi % 3]), pb[c], dvacc[db]);
+            dkacc[db] = Mfma<T>::mma(as_v8<T>(fqt[gi % 3]), db8[c], dkacc[db]);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
