@@ -366,16 +366,31 @@ __global__ __launch_bounds__(NT, 1) void bwd_dq_kernel(Args a) {
         if (!(wave_live && (!CAUSAL || k0 <= qw + 31))) return;
         const uint16_t* Ks = S;
         const uint16_t* Vs = S + TILE;
+        // S^T = K Q^T and dP^T = V dO^T; operand loads two (kb, kk) groups ahead
+        // of the MFMAs, order kept by scheduling barriers.
+        constexpr int NG1 = DQ_BK / 32 * D / 16;
         f32x16 s[DQ_BK / 32], dp[DQ_BK / 32];
 #pragma unroll
         for (int kb = 0; kb < DQ_BK / 32; ++kb) {
             s[kb] = f32x16{};
             dp[kb] = f32x16{};
+        }
+        uint4 fk[3], fv[3];
+        auto load1 = [&](int gi) {
+            const int kb = gi / (D / 16), kk = gi % (D / 16);
+            fk[gi % 3] = ld_s16(Ks + 32 * kb * D + roff[kk]);
+            fv[gi % 3] = ld_s16(Vs + 32 * kb * D + roff[kk]);
+        };
+        load1(0);
+        load1(1);
 #pragma unroll
-            for (int kk = 0; kk < D / 16; ++kk) {
-                s[kb] = Mfma<T>::mma(as_v8<T>(ld_s16(Ks + 32 * kb * D + roff[kk])), qf[kk], s[kb]);
-                dp[kb] = Mfma<T>::mma(as_v8<T>(ld_s16(Vs + 32 * kb * D + roff[kk])), df[kk], dp[kb]);
-            }
+        for (int gi = 0; gi < NG1; ++gi) {
+            if (gi + 2 < NG1) load1(gi + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            const int kb = gi / (D / 16), kk = gi % (D / 16);
+            s[kb] = Mfma<T>::mma(as_v8<T>(fk[gi % 3]), qf[kk], s[kb]);
+            dp[kb] = Mfma<T>::mma(as_v8<T>(fv[gi % 3]), df[kk], dp[kb]);
+            __builtin_amdgcn_sched_barrier(0);
         }
         // dS^T = P^T (dP^T - D), P^T = exp2(S^T * scale * log2(e) - L * log2(e)) [+ ALiBi];
         // only tiles with keys past the end or across the diagonal take the masked path.
@@ -400,18 +415,31 @@ __global__ __launch_bounds__(NT, 1) void bwd_dq_kernel(Args a) {
             softmax_bwd(std::true_type{});
         else
             softmax_bwd(std::false_type{});
-        // dQ^T += K^T dS^T, 16 keys per MFMA
+        // dQ^T += K^T dS^T, 16 keys per MFMA; transposed loads two groups ahead
+        constexpr int NG2 = DQ_BK / 16 * D / 32;
+        V8<T> dsb[DQ_BK / 16];
 #pragma unroll
         for (int c = 0; c < DQ_BK / 16; ++c) {
             const int kb = c >> 1, r0 = 8 * (c & 1);
-            const V8<T> dsb = pack8<T>(dp[kb][r0], dp[kb][r0 + 1], dp[kb][r0 + 2], dp[kb][r0 + 3], dp[kb][r0 + 4],
-                                       dp[kb][r0 + 5], dp[kb][r0 + 6], dp[kb][r0 + 7]);
+            dsb[c] = pack8<T>(dp[kb][r0], dp[kb][r0 + 1], dp[kb][r0 + 2], dp[kb][r0 + 3], dp[kb][r0 + 4],
+                              dp[kb][r0 + 5], dp[kb][r0 + 6], dp[kb][r0 + 7]);
+        }
+        uint4 fkt[3];
+        auto load2 = [&](int gi) {
+            const int c = gi / (D / 32), db = gi % (D / 32);
+            const uint2 lo = ld_s8_tr(Ks + 16 * c * D + toff[db][0]);
+            const uint2 hi = ld_s8_tr(Ks + 16 * c * D + toff[db][1]);
+            fkt[gi % 3] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        };
+        load2(0);
+        load2(1);
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-                const uint2 lo = ld_s8_tr(Ks + 16 * c * D + toff[db][0]);
-                const uint2 hi = ld_s8_tr(Ks + 16 * c * D + toff[db][1]);
-                dqacc[db] = Mfma<T>::mma(as_v8<T>(make_uint4(lo.x, lo.y, hi.x, hi.y)), dsb, dqacc[db]);
-            }
+        for (int gi = 0; gi < NG2; ++gi) {
+            if (gi + 2 < NG2) load2(gi + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            const int c = gi / (D / 32), db = gi % (D / 32);
+            dqacc[db] = Mfma<T>::mma(as_v8<T>(fkt[gi % 3]), dsb[c], dqacc[db]);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 

@@ -126,14 +126,24 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(Args a) {
         // wave-uniform: skip tiles that are entirely above this wave's diagonal
         if (!(wave_live && (!CAUSAL || k0 <= qw + 31))) return;
 
-        // S^T = K Q^T for BC keys x 32 queries (raw, unscaled scores)
+        // S^T = K Q^T for BC keys x 32 queries (raw, unscaled scores). The K
+        // operand loads run two (kb, kk) groups ahead of the MFMAs; scheduling
+        // barriers keep that order.
+        constexpr int NG1 = BC / 32 * D / 16;
         f32x16 s[BC / 32];
 #pragma unroll
-        for (int kb = 0; kb < BC / 32; ++kb) {
-            s[kb] = f32x16{};
+        for (int kb = 0; kb < BC / 32; ++kb) s[kb] = f32x16{};
+        uint4 fk[3];
+        auto load1 = [&](int gi) { fk[gi % 3] = ld_s16(Ks + 32 * (gi / (D / 16)) * D + roff[gi % (D / 16)]); };
+        load1(0);
+        load1(1);
 #pragma unroll
-            for (int kk = 0; kk < D / 16; ++kk)
-                s[kb] = Mfma<T>::mma(as_v8<T>(ld_s16(Ks + 32 * kb * D + roff[kk])), qf[kk], s[kb]);
+        for (int gi = 0; gi < NG1; ++gi) {
+            if (gi + 2 < NG1) load1(gi + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            const int kb = gi / (D / 16), kk = gi % (D / 16);
+            s[kb] = Mfma<T>::mma(as_v8<T>(fk[gi % 3]), qf[kk], s[kb]);
+            __builtin_amdgcn_sched_barrier(0);
         }
 
         // Scores in log2 units. Plain tiles keep the raw score and fold the
@@ -194,18 +204,31 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(Args a) {
         }
         l_run += ls;
 
-        // O^T += V^T P^T, 16 keys per MFMA
+        // O^T += V^T P^T, 16 keys per MFMA; transposed V loads two groups ahead
+        constexpr int NG2 = BC / 16 * D / 32;
+        V8<T> pf[BC / 16];
 #pragma unroll
         for (int c = 0; c < BC / 16; ++c) {
             const int kb = c >> 1, r0 = 8 * (c & 1);
-            const V8<T> pf = pack8<T>(s[kb][r0 + 0], s[kb][r0 + 1], s[kb][r0 + 2], s[kb][r0 + 3], s[kb][r0 + 4],
-                                      s[kb][r0 + 5], s[kb][r0 + 6], s[kb][r0 + 7]);
+            pf[c] = pack8<T>(s[kb][r0 + 0], s[kb][r0 + 1], s[kb][r0 + 2], s[kb][r0 + 3], s[kb][r0 + 4],
+                             s[kb][r0 + 5], s[kb][r0 + 6], s[kb][r0 + 7]);
+        }
+        uint4 fv[3];
+        auto load2 = [&](int gi) {
+            const int c = gi / (D / 32), db = gi % (D / 32);
+            const uint2 lo = ld_s8_tr(Vs + 16 * c * D + toff[db][0]);
+            const uint2 hi = ld_s8_tr(Vs + 16 * c * D + toff[db][1]);
+            fv[gi % 3] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        };
+        load2(0);
+        load2(1);
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-                const uint2 lo = ld_s8_tr(Vs + 16 * c * D + toff[db][0]);
-                const uint2 hi = ld_s8_tr(Vs + 16 * c * D + toff[db][1]);
-                oacc[db] = Mfma<T>::mma(as_v8<T>(make_uint4(lo.x, lo.y, hi.x, hi.y)), pf, oacc[db]);
-            }
+        for (int gi = 0; gi < NG2; ++gi) {
+            if (gi + 2 < NG2) load2(gi + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            const int c = gi / (D / 32), db = gi % (D / 32);
+            oacc[db] = Mfma<T>::mma(as_v8<T>(fv[gi % 3]), pf[c], oacc[db]);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
