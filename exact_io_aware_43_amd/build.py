@@ -24,11 +24,16 @@ ARCH = "gfx950"
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # MFMA results in ordinary VGPRs: avoids AGPR<->VGPR copies around the softmax
-    "-mllvm", "-amdgpu-mfma-vgpr-form=true",
     "-I", os.path.join(ROOT, "include"),
     "-Wno-unused-command-line-argument",
 ]
+
+
+# MFMA results in ordinary VGPRs: avoids AGPR<->VGPR copies around the softmax.
+# The dK/dV kernel keeps its 128 accumulator registers per lane in AGPRs instead
+# (VGPRs are needed for its operand rings), so it uses the default AGPR form.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]
+FILE_FLAGS = {"fa_bwd_dkdv.hip": []}
 
 
 def _run(cmd):
@@ -47,7 +52,8 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
 
     def one(pair):
         src, obj = pair
-        return _run([HIPCC, *CFLAGS, "-c", src, "-o", obj])
+        extra = FILE_FLAGS.get(os.path.basename(src), VGPR_FORM)
+        return _run([HIPCC, *CFLAGS, *extra, "-c", src, "-o", obj])
 
     with ThreadPoolExecutor(max_workers=max(1, min(jobs, len(srcs)))) as ex:
         for out in ex.map(one, zip(srcs, objs)):

@@ -72,224 +72,6 @@ __global__ __launch_bounds__(NT) void bwd_dsum_kernel(Args a) {
     }
 }
 
-// ---------------------------------------------------------------- dK, dV
-constexpr int KV_BK = 128;  // keys per workgroup (32 per wave)
-constexpr int KV_BQ = 64;   // queries per step
-
-template <typename T, int D, bool CAUSAL, bool ALIBI>
-__global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
-    // stage: Q tile, dO tile (swizzled [KV_BQ x D] each), then L*log2(e) and D (fp32, KV_BQ each)
-    constexpr int TILE = KV_BQ * D;
-    constexpr int STAGE = 2 * TILE + 2 * KV_BQ * 2;
-    __shared__ __attribute__((aligned(16))) uint16_t stA[STAGE];
-    __shared__ __attribute__((aligned(16))) uint16_t stB[STAGE];
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int col = lane & 31, kg = lane >> 5;
-    const int g = blockIdx.x, b = blockIdx.y;
-    const int kt = blockIdx.z;  // low key tiles see the most queries: dispatched first
-    int row0, len;
-    seq_bounds(a, b, row0, len);
-    const int k0 = kt * KV_BK;
-    if (k0 >= len) return;
-
-    const size_t ldq = (size_t)a.H * D, ldk = (size_t)a.Hkv * D;
-    const int kw = k0 + wave * 32;   // first key of this wave
-    const int key = kw + col;        // this lane's key (column of S)
-
-    // K^T and V^T fragments as B operands: lane holds key `key`, dims 16*kk + 8*kg + 0..7.
-    V8<T> kf[D / 16], vf[D / 16];
-    {
-        const T* Kp = reinterpret_cast<const T*>(a.k) + (size_t)(row0 + key) * ldk + (size_t)g * D;
-        const T* Vp = reinterpret_cast<const T*>(a.v) + (size_t)(row0 + key) * ldk + (size_t)g * D;
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-            uint4 uk = make_uint4(0, 0, 0, 0), uv = uk;
-            if (key < len) {
-                uk = ld_g16(Kp + 16 * kk + 8 * kg);
-                uv = ld_g16(Vp + 16 * kk + 8 * kg);
-            }
-            kf[kk] = as_v8<T>(uk);
-            vf[kk] = as_v8<T>(uv);
-        }
-    }
-
-    int roff[D / 16], toff[D / 32][2];
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) roff[kk] = swz_row_off<D>(lane, kk);
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-        toff[db][0] = swz_tr_off<D>(lane, db, 0);
-        toff[db][1] = swz_tr_off<D>(lane, db, 1);
-    }
-
-    f32x16 dkacc[D / 32], dvacc[D / 32];
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-        dkacc[db] = f32x16{};
-        dvacc[db] = f32x16{};
-    }
-
-    // Query tiles that can see this key tile: all of them, or (causal) those
-    // ending at or after k0; for every query head of the kv group.
-    const int qt0 = CAUSAL ? k0 / KV_BQ : 0;
-    const int nqt = (len + KV_BQ - 1) / KV_BQ;
-    const int per_head = nqt - qt0;
-    const int steps = a.G * per_head;
-    const float c2 = a.scale_log2;
-    const T* Qb = reinterpret_cast<const T*>(a.q) + (size_t)row0 * ldq;
-    const T* Db = reinterpret_cast<const T*>(a.dout) + (size_t)row0 * ldq;
-
-    auto step_coords = [&](int st, int& h, int& q0) {
-        const int hh = st / per_head;
-        h = g * a.G + hh;
-        q0 = (qt0 + st - hh * per_head) * KV_BQ;
-    };
-
-    DmaTile<D, KV_BQ, NT / 64> dma;
-    dma.init(wave, lane);
-    auto issue = [&](uint16_t* S, int st) {
-        int h, q0;
-        step_coords(st, h, q0);
-        dma.issue(S, reinterpret_cast<const uint16_t*>(Qb + (size_t)h * D), ldq, q0, len, wave, lane);
-        dma.issue(S + TILE, reinterpret_cast<const uint16_t*>(Db + (size_t)h * D), ldq, q0, len, wave, lane);
-        // the pre-pass filled positions [len, N) with +inf / 0; stop at N
-        const size_t vbase = ((size_t)b * a.H + h) * a.N + q0;
-        if (wave == 0) dma_vec64(reinterpret_cast<float*>(S + 2 * TILE), a.lse2 + vbase, a.N - q0, INFINITY, lane);
-        if (wave == 1) dma_vec64(reinterpret_cast<float*>(S + 2 * TILE) + KV_BQ, a.dsum + vbase, a.N - q0, 0.f, lane);
-    };
-
-    auto compute = [&](const uint16_t* S, int st) {
-        int h, q0;
-        step_coords(st, h, q0);
-        // wave-uniform skips: keys past the sequence end, or (causal) a query
-        // tile entirely before this wave's first key
-        if (!((kw < len) && (!CAUSAL || q0 + KV_BQ - 1 >= kw))) return;
-        const uint16_t* Qs = S;
-        const uint16_t* Ds = S + TILE;
-        const float* lse2 = reinterpret_cast<const float*>(S + 2 * TILE);
-        const float* dsv = lse2 + KV_BQ;
-
-        // S = Q K^T and dP = dO V^T: queries (rows) x keys (columns). The
-        // operand loads run two (qb, kk) groups ahead of the MFMAs; the
-        // scheduling barriers keep that order (left alone, the scheduler
-        // issues each load just before its MFMA and waits out its latency).
-        constexpr int NG1 = KV_BQ / 32 * D / 16;
-        f32x16 s[KV_BQ / 32], dp[KV_BQ / 32];
-#pragma unroll
-        for (int qb = 0; qb < KV_BQ / 32; ++qb) {
-            s[qb] = f32x16{};
-            dp[qb] = f32x16{};
-        }
-        uint4 fq[3], fd[3];
-        auto load1 = [&](int gi) {
-            const int qb = gi / (D / 16), kk = gi % (D / 16);
-            fq[gi % 3] = ld_s16(Qs + 32 * qb * D + roff[kk]);
-            fd[gi % 3] = ld_s16(Ds + 32 * qb * D + roff[kk]);
-        };
-        load1(0);
-        load1(1);
-#pragma unroll
-        for (int gi = 0; gi < NG1; ++gi) {
-            if (gi + 2 < NG1) load1(gi + 2);
-            __builtin_amdgcn_sched_barrier(0);
-            const int qb = gi / (D / 16), kk = gi % (D / 16);
-            s[qb] = Mfma<T>::mma(as_v8<T>(fq[gi % 3]), kf[kk], s[qb]);
-            dp[qb] = Mfma<T>::mma(as_v8<T>(fd[gi % 3]), vf[kk], dp[qb]);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-
-        // P = exp2(S * scale * log2(e) - L * log2(e)) [+ ALiBi], dS = P (dP - D).
-        // Only tiles that straddle the diagonal take the masked path.
-        const float slope2 = ALIBI ? a.slopes[h] * kLog2e : 0.f;
-        auto softmax_bwd = [&](auto masked) {
-#pragma unroll
-            for (int qb = 0; qb < KV_BQ / 32; ++qb) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float4 l4 = *reinterpret_cast<const float4*>(lse2 + 32 * qb + 8 * i + 4 * kg);
-                    const float4 d4 = *reinterpret_cast<const float4*>(dsv + 32 * qb + 8 * i + 4 * kg);
-                    const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-                    const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int r = 4 * i + j;
-                        const int qi = q0 + 32 * qb + 8 * i + 4 * kg + j;
-                        float bias = -lv[j];
-                        if (ALIBI) {
-                            const float dist = (float)(qi - key);
-                            bias -= slope2 * (CAUSAL ? dist : fabsf(dist));
-                        }
-                        float p = exp2_fast(fmaf(s[qb][r], c2, bias));
-                        if (decltype(masked)::value && key > qi) p = 0.f;
-                        s[qb][r] = p;
-                        dp[qb][r] = p * (dp[qb][r] - dv4[j]);
-                    }
-                }
-            }
-        };
-        if (CAUSAL && q0 < kw + 31)
-            softmax_bwd(std::true_type{});
-        else
-            softmax_bwd(std::false_type{});
-
-        // dV^T += dO^T P and dK^T += Q^T dS, 16 queries per MFMA; transposed
-        // operand loads run two (c, db) groups ahead as above.
-        constexpr int NG2 = KV_BQ / 16 * D / 32;
-        V8<T> pb[KV_BQ / 16], db8[KV_BQ / 16];
-#pragma unroll
-        for (int c = 0; c < KV_BQ / 16; ++c) {
-            const int qb = c >> 1, r0 = 8 * (c & 1);
-            pb[c] = pack8<T>(s[qb][r0], s[qb][r0 + 1], s[qb][r0 + 2], s[qb][r0 + 3], s[qb][r0 + 4], s[qb][r0 + 5],
-                             s[qb][r0 + 6], s[qb][r0 + 7]);
-            db8[c] = pack8<T>(dp[qb][r0], dp[qb][r0 + 1], dp[qb][r0 + 2], dp[qb][r0 + 3], dp[qb][r0 + 4],
-                              dp[qb][r0 + 5], dp[qb][r0 + 6], dp[qb][r0 + 7]);
-        }
-        uint4 fo[3], fqt[3];
-        auto load2 = [&](int gi) {
-            const int c = gi / (D / 32), db = gi % (D / 32);
-            const uint2 olo = ld_s8_tr(Ds + 16 * c * D + toff[db][0]);
-            const uint2 ohi = ld_s8_tr(Ds + 16 * c * D + toff[db][1]);
-            const uint2 qlo = ld_s8_tr(Qs + 16 * c * D + toff[db][0]);
-            const uint2 qhi = ld_s8_tr(Qs + 16 * c * D + toff[db][1]);
-            fo[gi % 3] = make_uint4(olo.x, olo.y, ohi.x, ohi.y);
-            fqt[gi % 3] = make_uint4(qlo.x, qlo.y, qhi.x, qhi.y);
-        };
-        load2(0);
-        load2(1);
-#pragma unroll
-        for (int gi = 0; gi < NG2; ++gi) {
-            if (gi + 2 < NG2) load2(gi + 2);
-            __builtin_amdgcn_sched_barrier(0);
-            const int c = gi / (D / 32), db = gi % (D / 32);
-            dvacc[db] = Mfma<T>::mma(as_v8<T>(fo[gi % 3]), pb[c], dvacc[db]);
-            dkacc[db] = Mfma<T>::mma(as_v8<T>(fqt[gi % 3]), db8[c], dkacc[db]);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    };
-
-    two_stage_loop(stA, stB, steps, issue, compute);
-
-    // epilogue: lane owns key `key`; accumulator rows are dims 32*db + 8*i + 4*kg + 0..3
-    if (key < len) {
-        T* dK = reinterpret_cast<T*>(a.dk) + (size_t)(row0 + key) * ldk + (size_t)g * D;
-        T* dV = reinterpret_cast<T*>(a.dv) + (size_t)(row0 + key) * ldk + (size_t)g * D;
-        const float sc = a.scale;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int d0 = 32 * db + 8 * i + 4 * kg;
-                const int r = 4 * i;
-                *reinterpret_cast<uint2*>(dK + d0) = pack4<T>(dkacc[db][r] * sc, dkacc[db][r + 1] * sc,
-                                                              dkacc[db][r + 2] * sc, dkacc[db][r + 3] * sc);
-                *reinterpret_cast<uint2*>(dV + d0) =
-                    pack4<T>(dvacc[db][r], dvacc[db][r + 1], dvacc[db][r + 2], dvacc[db][r + 3]);
-            }
-        }
-    }
-}
-
 // ---------------------------------------------------------------- dQ
 constexpr int DQ_BQ = 128;  // queries per workgroup (32 per wave)
 constexpr int DQ_BK = 64;   // keys per K/V tile
@@ -471,9 +253,7 @@ hipError_t launch(const Args& a, unsigned stages, hipStream_t s) {
         if (e != hipSuccess) return e;
     }
     if (stages & 2u) {
-        dim3 grid(a.Hkv, a.B, (a.N + KV_BK - 1) / KV_BK);
-        hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL, ALIBI>), grid, dim3(NT), 0, s, a);
-        hipError_t e = hipGetLastError();
+        hipError_t e = launch_bwd_dkdv(a, std::is_same<T, __bf16>::value ? 2 : 1, D, CAUSAL, ALIBI, s);
         if (e != hipSuccess) return e;
     }
     if (stages & 4u) {

@@ -34,6 +34,8 @@ struct Args {
 // Each returns hipSuccess or the launch error. `dtype` follows fa_dtype.
 hipError_t launch_fwd_mfma(const Args& a, int dtype, int d, bool causal, bool alibi, hipStream_t s);
 hipError_t launch_fwd_f32(const Args& a, int d, bool causal, bool alibi, hipStream_t s);
+// The dK/dV launch alone (built in its own translation unit with its own flags).
+hipError_t launch_bwd_dkdv(const Args& a, int dtype, int d, bool causal, bool alibi, hipStream_t s);
 // `stages`: bit 0 = D pre-pass, bit 1 = dK/dV, bit 2 = dQ (enqueued in that order).
 hipError_t launch_bwd(const Args& a, int dtype, int d, bool causal, bool alibi, unsigned stages, hipStream_t s);
 
