@@ -11,6 +11,10 @@ namespace {
 
 constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
 
+// N rounded up to a multiple of 64: row pitch of the backward workspace vectors,
+// which the kernels load 64 positions at a time.
+int round64(int N) { return (N + 63) & ~63; }
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 bool valid_dtype(int dt) { return dt == FA_FP32 || dt == FA_FP16 || dt == FA_BF16; }
@@ -43,13 +47,14 @@ fa::Args make_args(const void* q, const void* k, const void* v, int B, int H, in
     a.Hkv = Hkv;
     a.N = N;
     a.G = H / Hkv;
+    a.N64 = round64(N);
     a.scale = scale;
     a.scale_log2 = scale * 1.4426950408889634f;
     return a;
 }
 
-// D and lse * log2(e), fp32 each, laid out like lse: [B, H, N].
-size_t workspace_rows(int B, int H, int N) { return (size_t)B * (size_t)H * (size_t)N; }
+// D and lse * log2(e), fp32 each, [B, H, N64] (see round64).
+size_t workspace_rows(int B, int H, int N) { return (size_t)B * (size_t)H * (size_t)round64(N); }
 size_t workspace_bytes_for(int B, int H, int N) {
     return (2 * workspace_rows(B, H, N) * sizeof(float) + 255) & ~(size_t)255;
 }

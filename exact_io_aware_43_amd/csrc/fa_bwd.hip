@@ -30,9 +30,9 @@
 // row-major LDS tiles whose 16-byte chunks are XOR-swizzled per row; the
 // transposed operands (dO^T, Q^T, K^T) come from the transposing LDS read.
 //
-// Workspace: D (fp32, laid out like lse) followed by L * log2(e) in the same
-// layout, both written by the pre-pass; positions past a packed sequence's end
-// get L * log2(e) = +inf and D = 0, so any row the later kernels read there
+// Workspace: D followed by L * log2(e), fp32 [B, H, N64] each (N64 = N rounded
+// up to 64), both written by the pre-pass; positions past a sequence's end get
+// L * log2(e) = +inf and D = 0, so any row the later kernels read there
 // contributes exactly zero.
 #include <type_traits>
 
@@ -53,7 +53,7 @@ __global__ __launch_bounds__(NT) void bwd_dsum_kernel(Args a) {
     seq_bounds(a, b, row0, len);
     const int i = blockIdx.z * RPB + threadIdx.x / LPR;
     const int part = threadIdx.x % LPR;
-    if (i >= a.N) return;
+    if (i >= a.N64) return;
     float acc = 0.f;
     if (i < len) {
         const size_t off = ((size_t)(row0 + i) * a.H + h) * D + part * 8;
@@ -66,9 +66,9 @@ __global__ __launch_bounds__(NT) void bwd_dsum_kernel(Args a) {
 #pragma unroll
     for (int w = LPR / 2; w >= 1; w >>= 1) acc += __shfl_xor(acc, w);
     if (part == 0) {
-        const size_t idx = ((size_t)b * a.H + h) * a.N + i;
+        const size_t idx = ((size_t)b * a.H + h) * a.N64 + i;
         a.dsum[idx] = (i < len) ? acc : 0.f;
-        a.lse2[idx] = (i < len) ? a.lse_in[idx] * kLog2e : INFINITY;
+        a.lse2[idx] = (i < len) ? a.lse_in[((size_t)b * a.H + h) * a.N + i] * kLog2e : INFINITY;
     }
 }
 
@@ -112,7 +112,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_dq_kernel(Args a) {
             df[kk] = as_v8<T>(ud);
         }
     }
-    const size_t vidx = ((size_t)b * a.H + h) * a.N + qi;
+    const size_t vidx = ((size_t)b * a.H + h) * a.N64 + qi;
     const float lse2 = (qi < len) ? a.lse2[vidx] : INFINITY;
     const float dsum = (qi < len) ? a.dsum[vidx] : 0.f;
     const float c2 = a.scale_log2;
@@ -247,7 +247,7 @@ template <typename T, int D, bool CAUSAL, bool ALIBI>
 hipError_t launch(const Args& a, unsigned stages, hipStream_t s) {
     if (stages & 1u) {
         constexpr int RPB = NT / (D / 8);
-        dim3 grid(a.H, a.B, (a.N + RPB - 1) / RPB);
+        dim3 grid(a.H, a.B, (a.N64 + RPB - 1) / RPB);
         hipLaunchKernelGGL((bwd_dsum_kernel<T, D>), grid, dim3(NT), 0, s, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -111,10 +111,11 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
         step_coords(st, h, q0);
         dma.issue(S, reinterpret_cast<const uint16_t*>(Qb + (size_t)h * D), ldq, q0, len, wave, lane);
         dma.issue(S + TILE, reinterpret_cast<const uint16_t*>(Db + (size_t)h * D), ldq, q0, len, wave, lane);
-        // the pre-pass filled positions [len, N) with +inf / 0; stop at N
-        const size_t vbase = ((size_t)b * a.H + h) * a.N + q0;
-        if (wave == 0) dma_vec64(reinterpret_cast<float*>(S + 2 * TILE), a.lse2 + vbase, a.N - q0, INFINITY, lane);
-        if (wave == 1) dma_vec64(reinterpret_cast<float*>(S + 2 * TILE) + KV_BQ, a.dsum + vbase, a.N - q0, 0.f, lane);
+        // the pre-pass filled positions [len, N64) with +inf / 0, so the 64
+        // values from q0 are in bounds and padding rows get P = 0
+        const size_t vbase = ((size_t)b * a.H + h) * a.N64 + q0;
+        if (wave == 0) dma_vec64(reinterpret_cast<float*>(S + 2 * TILE), a.lse2 + vbase, lane);
+        if (wave == 1) dma_vec64(reinterpret_cast<float*>(S + 2 * TILE) + KV_BQ, a.dsum + vbase, lane);
     };
 
     auto step = [&](const uint16_t* S, int h, int q0, auto masked) {

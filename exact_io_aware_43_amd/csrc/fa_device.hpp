@@ -160,9 +160,12 @@ __device__ __forceinline__ int swz_tr_off(int lane, int db, int half) {
 // 16-bit tile into a swizzled LDS tile. Each instruction of a wave fills 1 KB
 // of LDS, lane L writing bytes 16 L .. 16 L + 15; the lane fetches from global
 // memory the 16-byte chunk that belongs at that position. Rows at or past
-// `nrows` are zero-filled with an ordinary LDS store instead. `NW` waves share
-// the tile. The loads complete asynchronously (vmcnt); callers wait and
-// barrier before reading the tile.
+// `nrows` repeat row nrows - 1: every kernel masks those rows (P = 0), so a
+// finite repeated row contributes exactly zero. (An ordinary LDS store to
+// zero-fill them instead would make the compiler wait for all in-flight
+// direct loads before it, since it may alias them, serialising the prefetch.)
+// `NW` waves share the tile. The loads complete asynchronously (vmcnt);
+// callers wait and barrier before reading the tile.
 template <int D, int ROWS, int NW>
 struct DmaTile {
     static constexpr int INSTR = ROWS * D * 2 / 1024;
@@ -190,32 +193,24 @@ struct DmaTile {
 #pragma unroll
         for (int i = 0; i < PER_WAVE; ++i) {
             uint16_t* dst = tile + (wave * PER_WAVE + i) * 512;  // 1 KB per instruction
-            const int row = row_start + grow_off[i];
-            if (row < nrows) {
-                __builtin_amdgcn_global_load_lds((gbl_void*)(base + (size_t)row * ld + gcol[i]),
-                                                 (lds_void*)((__attribute__((address_space(3))) uint16_t*)dst), 16,
-                                                 0, 0);
-            } else {
-                st_s16(dst + 8 * lane, make_uint4(0, 0, 0, 0));
-            }
+            const int row = min(row_start + grow_off[i], nrows - 1);
+            __builtin_amdgcn_global_load_lds((gbl_void*)(base + (size_t)row * ld + gcol[i]),
+                                             (lds_void*)((__attribute__((address_space(3))) uint16_t*)dst), 16, 0,
+                                             0);
         }
     }
 };
 
 // Direct global -> LDS load of 64 consecutive fp32 values (one wave, 4 bytes per
-// lane) from `src` into `dst`; lanes whose index is at or past `n` store `fill`
-// instead.
+// lane) from `src` (all 64 in bounds) into `dst`.
 // The global pointer is cast to the global address space explicitly: left
 // implicit, the conversion is rejected in the host compilation pass, which
 // then silently drops the host launch stubs of every kernel that uses it.
-__device__ __forceinline__ void dma_vec64(float* dst, const float* src, int n, float fill, int lane) {
+__device__ __forceinline__ void dma_vec64(float* dst, const float* src, int lane) {
     typedef __attribute__((address_space(3))) void lds_void;
     typedef __attribute__((address_space(1))) void gbl_void;
-    if (lane < n)
-        __builtin_amdgcn_global_load_lds((gbl_void*)(src + lane),
-                                         (lds_void*)((__attribute__((address_space(3))) float*)dst), 4, 0, 0);
-    else
-        dst[lane] = fill;
+    __builtin_amdgcn_global_load_lds((gbl_void*)(src + lane),
+                                     (lds_void*)((__attribute__((address_space(3))) float*)dst), 4, 0, 0);
 }
 
 // The double-buffered tile loop shared by the kernels: body(stage, i) runs for

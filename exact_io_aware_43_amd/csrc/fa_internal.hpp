@@ -22,11 +22,12 @@ struct Args {
     void* dq;
     void* dk;
     void* dv;
-    float* dsum;       // backward workspace: D_i = dO_i . O_i, laid out like lse
-    float* lse2;       // backward workspace: lse * log2(e), laid out like lse
+    float* dsum;       // backward workspace: D_i = dO_i . O_i, [B, H, N64]
+    float* lse2;       // backward workspace: lse * log2(e), [B, H, N64]
     const float* slopes;
     const int* cu;
     int B, H, Hkv, N, G;
+    int N64;           // N rounded up to a multiple of 64: row pitch of the workspace vectors
     float scale;       // softmax scale
     float scale_log2;  // scale * log2(e)
 };

@@ -84,8 +84,9 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 /*
  * Bytes of device scratch fa_bwd needs for these sizes: the per-row
  * D_i = dO_i . O_i of Key design 3 and the row statistic rescaled to log2
- * units, both fp32 and laid out like lse (2 * 4 * B * H * N bytes, rounded up
- * to 256). Linear in N. Returns 0 for invalid sizes.
+ * units, both fp32 [B, H, N64] with N64 = N rounded up to a multiple of 64
+ * (2 * 4 * B * H * N64 bytes, rounded up to 256). Linear in N. Returns 0 for
+ * invalid sizes.
  */
 size_t fa_bwd_workspace_size(int B, int H, int Hkv, int N, int d, int causal,
                              int varlen, fa_dtype dtype);

@@ -103,10 +103,11 @@ def test_bwd_stage_mask_rejected(stages):
 
 def test_workspace_size():
     # two fp32 values (D and the log2-scaled statistic) per (sequence, head, position),
-    # rounded up to 256 bytes
+    # positions padded to a multiple of 64, total rounded up to 256 bytes
     assert fa.fa_bwd_workspace_size(2, 4, 2, 64, 64, 1, 0, fa.FA_BF16) == 2 * 2 * 4 * 64 * 4
     assert fa.fa_bwd_workspace_size(1, 32, 32, 16384, 128, 1, 0, fa.FA_BF16) == 2 * 32 * 16384 * 4
-    assert fa.fa_bwd_workspace_size(1, 1, 1, 3, 64, 0, 0, fa.FA_BF16) == 256
+    assert fa.fa_bwd_workspace_size(1, 1, 1, 3, 64, 0, 0, fa.FA_BF16) == 2 * 64 * 4
+    assert fa.fa_bwd_workspace_size(3, 2, 1, 65, 64, 0, 0, fa.FA_BF16) == 2 * 3 * 2 * 128 * 4
     assert fa.fa_bwd_workspace_size(0, 4, 2, 64, 64, 1, 0, fa.FA_BF16) == 0
     assert fa.fa_bwd_workspace_size(1, 4, 3, 64, 64, 1, 0, fa.FA_BF16) == 0
     assert fa.fa_bwd_workspace_size(1, 4, 2, 64, 80, 1, 0, fa.FA_BF16) == 0
