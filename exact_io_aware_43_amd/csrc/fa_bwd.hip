@@ -137,7 +137,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_dq_kernel(Args a) {
     const T* Vg = reinterpret_cast<const T*>(a.v) + (size_t)row0 * ldk + (size_t)g * D;
 
     DmaTile<D, DQ_BK, NT / 64> dma;
-    dma.init(wave, lane);
+    dma.init(wave, lane, ldk);
     auto issue = [&](uint16_t* S, int kt) {
         dma.issue(S, reinterpret_cast<const uint16_t*>(Kg), ldk, kt * DQ_BK, len, wave, lane);
         dma.issue(S + TILE, reinterpret_cast<const uint16_t*>(Vg), ldk, kt * DQ_BK, len, wave, lane);

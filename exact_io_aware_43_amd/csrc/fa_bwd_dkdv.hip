@@ -105,7 +105,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
     };
 
     DmaTile<D, KV_BQ, NT / 64> dma;
-    dma.init(wave, lane);
+    dma.init(wave, lane, ldq);
     auto issue = [&](uint16_t* S, int st) {
         int h, q0;
         step_coords(st, h, q0);

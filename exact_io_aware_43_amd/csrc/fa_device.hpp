@@ -173,8 +173,9 @@ struct DmaTile {
     static_assert(INSTR % NW == 0, "tile must split evenly over the waves");
     int grow_off[PER_WAVE];  // row within the tile, per instruction
     int gcol[PER_WAVE];      // global column (elements) of this lane's chunk
+    uint32_t boff[PER_WAVE]; // byte offset of that chunk from the tile's first row, for row stride `ld`
 
-    __device__ __forceinline__ void init(int wave, int lane) {
+    __device__ __forceinline__ void init(int wave, int lane, size_t ld) {
 #pragma unroll
         for (int i = 0; i < PER_WAVE; ++i) {
             const int p = (wave * PER_WAVE + i) * 64 + lane;  // chunk index in LDS order
@@ -182,22 +183,38 @@ struct DmaTile {
             const int f = ((row & 3) * (D / 32)) ^ ((row >> 2) & 3);
             grow_off[i] = row;
             gcol[i] = 8 * (pos ^ f);
+            boff[i] = (uint32_t)(((size_t)row * ld + gcol[i]) * 2);
         }
     }
 
     // `base` is the 16-bit element array (any 16-bit type viewed as uint16_t).
+    // Full tiles (the common case) address every chunk as a uniform base plus
+    // the precomputed 32-bit lane offset; only a tile that runs past `nrows`
+    // recomputes clamped rows.
     __device__ __forceinline__ void issue(uint16_t* tile, const uint16_t* base, size_t ld, int row_start, int nrows,
                                           int wave, int lane) const {
         typedef __attribute__((address_space(3))) void lds_void;
         typedef __attribute__((address_space(1))) void gbl_void;  // explicit: see dma_vec64
+        if (row_start + ROWS <= nrows) {
+            const char* b = reinterpret_cast<const char*>(base + (size_t)row_start * ld);
 #pragma unroll
-        for (int i = 0; i < PER_WAVE; ++i) {
-            uint16_t* dst = tile + (wave * PER_WAVE + i) * 512;  // 1 KB per instruction
-            const int row = min(row_start + grow_off[i], nrows - 1);
-            __builtin_amdgcn_global_load_lds((gbl_void*)(base + (size_t)row * ld + gcol[i]),
-                                             (lds_void*)((__attribute__((address_space(3))) uint16_t*)dst), 16, 0,
-                                             0);
+            for (int i = 0; i < PER_WAVE; ++i) {
+                uint16_t* dst = tile + (wave * PER_WAVE + i) * 512;  // 1 KB per instruction
+                __builtin_amdgcn_global_load_lds((gbl_void*)(b + boff[i]),
+                                                 (lds_void*)((__attribute__((address_space(3))) uint16_t*)dst), 16,
+                                                 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < PER_WAVE; ++i) {
+                uint16_t* dst = tile + (wave * PER_WAVE + i) * 512;
+                const int row = min(row_start + grow_off[i], nrows - 1);
+                __builtin_amdgcn_global_load_lds((gbl_void*)(base + (size_t)row * ld + gcol[i]),
+                                                 (lds_void*)((__attribute__((address_space(3))) uint16_t*)dst), 16,
+                                                 0, 0);
+            }
         }
+        (void)lane;
     }
 };
 

@@ -105,7 +105,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(Args a) {
     const int nkt = (kend + BC - 1) / BC;
 
     DmaTile<D, BC, NT / 64> dma;
-    dma.init(wave, lane);
+    dma.init(wave, lane, ldk);
     auto issue = [&](uint16_t* st, int kt) {
         dma.issue(st, reinterpret_cast<const uint16_t*>(Kg), ldk, kt * BC, len, wave, lane);
         dma.issue(st + TILE, reinterpret_cast<const uint16_t*>(Vg), ldk, kt * BC, len, wave, lane);
