@@ -139,8 +139,8 @@ __global__ __launch_bounds__(NT, 1) void bwd_dq_kernel(Args a) {
     DmaTile<D, DQ_BK, NT / 64> dma;
     dma.init(wave, lane, ldk);
     auto issue = [&](uint16_t* S, int kt) {
-        dma.issue(S, reinterpret_cast<const uint16_t*>(Kg), ldk, kt * DQ_BK, len, wave, lane);
-        dma.issue(S + TILE, reinterpret_cast<const uint16_t*>(Vg), ldk, kt * DQ_BK, len, wave, lane);
+        dma.issue(S, reinterpret_cast<const uint16_t*>(Kg), kt * DQ_BK, len, wave);
+        dma.issue(S + TILE, reinterpret_cast<const uint16_t*>(Vg), kt * DQ_BK, len, wave);
     };
 
     auto compute = [&](const uint16_t* S, int kt) {

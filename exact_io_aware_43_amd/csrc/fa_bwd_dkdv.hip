@@ -109,8 +109,8 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
     auto issue = [&](uint16_t* S, int st) {
         int h, q0;
         step_coords(st, h, q0);
-        dma.issue(S, reinterpret_cast<const uint16_t*>(Qb + (size_t)h * D), ldq, q0, len, wave, lane);
-        dma.issue(S + TILE, reinterpret_cast<const uint16_t*>(Db + (size_t)h * D), ldq, q0, len, wave, lane);
+        dma.issue(S, reinterpret_cast<const uint16_t*>(Qb + (size_t)h * D), q0, len, wave);
+        dma.issue(S + TILE, reinterpret_cast<const uint16_t*>(Db + (size_t)h * D), q0, len, wave);
         // the pre-pass filled positions [len, N64) with +inf / 0, so the 64
         // values from q0 are in bounds and padding rows get P = 0
         const size_t vbase = ((size_t)b * a.H + h) * a.N64 + q0;

@@ -26,6 +26,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// Last word of a raw buffer descriptor (no stride, no swizzle; 32-bit data
+// format) as the CDNA3/CDNA4 buffer instructions expect it.
+constexpr int kBufferWord3 = 0x00020000;
 
 template <typename T>
 struct Mfma;
@@ -156,67 +159,58 @@ __device__ __forceinline__ int swz_tr_off(int lane, int db, int half) {
     return swz<D>(8 * half + 4 * (grp >> 1) + (r >> 2), 32 * db + 16 * (grp & 1) + 4 * (r & 3));
 }
 
-// Direct global -> LDS staging (global_load_lds_dwordx4) of a [ROWS x D]
+// Direct global -> LDS staging (buffer_load_dwordx4 ... lds) of a [ROWS x D]
 // 16-bit tile into a swizzled LDS tile. Each instruction of a wave fills 1 KB
 // of LDS, lane L writing bytes 16 L .. 16 L + 15; the lane fetches from global
-// memory the 16-byte chunk that belongs at that position. Rows at or past
-// `nrows` repeat row nrows - 1: every kernel masks those rows (P = 0), so a
-// finite repeated row contributes exactly zero. (An ordinary LDS store to
-// zero-fill them instead would make the compiler wait for all in-flight
-// direct loads before it, since it may alias them, serialising the prefetch.)
-// `NW` waves share the tile. The loads complete asynchronously (vmcnt);
-// callers wait and barrier before reading the tile.
+// memory the 16-byte chunk that belongs at that position, at a byte offset
+// from the tile's first row that is fixed for the kernel (precomputed once).
+// Per tile only a buffer descriptor is built (scalar code): its base is the
+// tile's first row and its size ends with row `nrows` - 1, so the hardware
+// range check turns the chunks of rows at or past `nrows` into zeros. Every
+// kernel masks such rows (P = 0), and zero rows contribute exactly zero. `NW`
+// waves share the tile. The loads complete asynchronously (vmcnt); callers
+// wait and barrier before reading the tile.
 template <int D, int ROWS, int NW>
 struct DmaTile {
     static constexpr int INSTR = ROWS * D * 2 / 1024;
     static constexpr int PER_WAVE = INSTR / NW;
     static_assert(INSTR % NW == 0, "tile must split evenly over the waves");
-    int grow_off[PER_WAVE];  // row within the tile, per instruction
-    int gcol[PER_WAVE];      // global column (elements) of this lane's chunk
-    uint32_t boff[PER_WAVE]; // byte offset of that chunk from the tile's first row, for row stride `ld`
+    uint32_t boff[PER_WAVE];  // byte offset of this lane's chunk from the tile's first row (row stride `ld`)
+    uint32_t ld2;             // row stride in bytes
 
     __device__ __forceinline__ void init(int wave, int lane, size_t ld) {
+        ld2 = (uint32_t)(ld * 2);
 #pragma unroll
         for (int i = 0; i < PER_WAVE; ++i) {
             const int p = (wave * PER_WAVE + i) * 64 + lane;  // chunk index in LDS order
             const int row = p / (D / 8), pos = p % (D / 8);
             const int f = ((row & 3) * (D / 32)) ^ ((row >> 2) & 3);
-            grow_off[i] = row;
-            gcol[i] = 8 * (pos ^ f);
-            boff[i] = (uint32_t)(((size_t)row * ld + gcol[i]) * 2);
+            boff[i] = (uint32_t)row * ld2 + 16u * (uint32_t)(pos ^ f);
         }
     }
 
-    // `base` is the 16-bit element array (any 16-bit type viewed as uint16_t).
-    // Full tiles (the common case) address every chunk as a uniform base plus
-    // the precomputed 32-bit lane offset; only a tile that runs past `nrows`
-    // recomputes clamped rows.
-    __device__ __forceinline__ void issue(uint16_t* tile, const uint16_t* base, size_t ld, int row_start, int nrows,
-                                          int wave, int lane) const {
-        typedef __attribute__((address_space(3))) void lds_void;
-        typedef __attribute__((address_space(1))) void gbl_void;  // explicit: see dma_vec64
-        if (row_start + ROWS <= nrows) {
-            const char* b = reinterpret_cast<const char*>(base + (size_t)row_start * ld);
+    // Rows [row_start, row_start + ROWS) of `base` (16-bit elements, any
+    // 16-bit type viewed as uint16_t); rows at or past `nrows` read as zero.
+    __device__ __forceinline__ void issue(uint16_t* tile, const uint16_t* base, int row_start, int nrows,
+                                          int wave) const {
+#if defined(__HIP_DEVICE_COMPILE__)  // the buffer descriptor type exists for the GPU target only
+        const int valid = min(nrows - row_start, ROWS);
+        const uint32_t bytes = valid > 0 ? (uint32_t)(valid - 1) * ld2 + D * 2 : 0u;
+        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(base) + (size_t)row_start * (ld2 / 2), (short)0, (int)bytes, kBufferWord3);
 #pragma unroll
-            for (int i = 0; i < PER_WAVE; ++i) {
-                uint16_t* dst = tile + (wave * PER_WAVE + i) * 512;  // 1 KB per instruction
-                __builtin_amdgcn_global_load_lds((gbl_void*)(b + boff[i]),
-                                                 (lds_void*)((__attribute__((address_space(3))) uint16_t*)dst), 16,
-                                                 0, 0);
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < PER_WAVE; ++i) {
-                uint16_t* dst = tile + (wave * PER_WAVE + i) * 512;
-                const int row = min(row_start + grow_off[i], nrows - 1);
-                __builtin_amdgcn_global_load_lds((gbl_void*)(base + (size_t)row * ld + gcol[i]),
-                                                 (lds_void*)((__attribute__((address_space(3))) uint16_t*)dst), 16,
-                                                 0, 0);
-            }
+        for (int i = 0; i < PER_WAVE; ++i) {
+            uint16_t* dst = tile + (wave * PER_WAVE + i) * 512;  // 1 KB per instruction
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc, (__attribute__((address_space(3))) void*)((__attribute__((address_space(3))) uint16_t*)dst), 16,
+                boff[i], 0, 0, 0);
         }
-        (void)lane;
+#else
+        (void)tile, (void)base, (void)row_start, (void)nrows, (void)wave;
+#endif
     }
 };
+
 
 // Direct global -> LDS load of 64 consecutive fp32 values (one wave, 4 bytes per
 // lane) from `src` (all 64 in bounds) into `dst`.

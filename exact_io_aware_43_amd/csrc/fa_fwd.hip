@@ -107,8 +107,8 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(Args a) {
     DmaTile<D, BC, NT / 64> dma;
     dma.init(wave, lane, ldk);
     auto issue = [&](uint16_t* st, int kt) {
-        dma.issue(st, reinterpret_cast<const uint16_t*>(Kg), ldk, kt * BC, len, wave, lane);
-        dma.issue(st + TILE, reinterpret_cast<const uint16_t*>(Vg), ldk, kt * BC, len, wave, lane);
+        dma.issue(st, reinterpret_cast<const uint16_t*>(Kg), kt * BC, len, wave);
+        dma.issue(st + TILE, reinterpret_cast<const uint16_t*>(Vg), kt * BC, len, wave);
     };
 
     f32x16 oacc[D / 32];
