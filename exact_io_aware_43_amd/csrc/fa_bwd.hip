@@ -116,7 +116,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_dq_kernel(Args a) {
     const float lse2 = (qi < len) ? a.lse2[vidx] : INFINITY;
     const float dsum = (qi < len) ? a.dsum[vidx] : 0.f;
     const float c2 = a.scale_log2;
-    const float slope2 = ALIBI ? a.slopes[h] * kLog2e : 0.f;
+    const float slope2 = ALIBI ? ld_uniform(a.slopes + h) * kLog2e : 0.f;
 
     int roff[D / 16], toff[D / 32][2];
 #pragma unroll

@@ -124,7 +124,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
         const uint16_t* Ds = S + TILE;
         const float* lse2 = reinterpret_cast<const float*>(S + 2 * TILE);
         const float* dsv = lse2 + KV_BQ;
-        const float slope2 = ALIBI ? a.slopes[h] * kLog2e : 0.f;
+        const float slope2 = ALIBI ? ld_uniform(a.slopes + h) * kLog2e : 0.f;
 
         f32x16 sc[2], dpc[2];  // S and dP of blocks 0, 1
 #pragma unroll
@@ -136,40 +136,43 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
         float pv[16], dsr[16];
         V8<T> pb[4], db8[4];  // packed P and dS per 16-query chunk c
 
-        auto load_vec = [&](int qb) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                l4[i] = *reinterpret_cast<const float4*>(lse2 + 32 * qb + 8 * i + 4 * kg);
-                d4[i] = *reinterpret_cast<const float4*>(dsv + 32 * qb + 8 * i + 4 * kg);
-            }
+        // L*log2(e) and D of rows 8i + 4kg + 0..3 of block qb (one row group)
+        auto load_vec = [&](int qb, int i) {
+            l4[i] = *reinterpret_cast<const float4*>(lse2 + 32 * qb + 8 * i + 4 * kg);
+            d4[i] = *reinterpret_cast<const float4*>(dsv + 32 * qb + 8 * i + 4 * kg);
         };
-        // softmax backward of row group i (4 accumulator rows) of block qb
-        auto smax = [&](int qb, int i) {
-            const float lv[4] = {l4[i].x, l4[i].y, l4[i].z, l4[i].w};
-            const float dv[4] = {d4[i].x, d4[i].y, d4[i].z, d4[i].w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 4 * i + j;
-                const int qi = q0 + 32 * qb + 8 * i + 4 * kg + j;
-                float bias = -lv[j];
-                if (ALIBI) {
-                    const float dist = (float)(qi - key);
-                    bias -= slope2 * (CAUSAL ? dist : fabsf(dist));
-                }
-                float p = exp2_fast(fmaf(sc[qb][r], c2, bias));
-                if (MASKED && key > qi) p = 0.f;
-                pv[r] = p;
-                dsr[r] = p * (dpc[qb][r] - dv[j]);
+        // softmax backward of accumulator row r of block qb: P and dS
+        auto elem = [&](int qb, int r) {
+            const int i = r >> 2, j = r & 3;
+            const float lv = j == 0 ? l4[i].x : j == 1 ? l4[i].y : j == 2 ? l4[i].z : l4[i].w;
+            const float dv = j == 0 ? d4[i].x : j == 1 ? d4[i].y : j == 2 ? d4[i].z : d4[i].w;
+            const int qi = q0 + 32 * qb + 8 * i + 4 * kg + j;
+            float bias = -lv;
+            if (ALIBI) {
+                const float dist = (float)(qi - key);
+                bias -= slope2 * (CAUSAL ? dist : fabsf(dist));
             }
+            float p = exp2_fast(fmaf(sc[qb][r], c2, bias));
+            if (MASKED && key > qi) p = 0.f;
+            pv[r] = p;
+            dsr[r] = p * (dpc[qb][r] - dv);
         };
-        auto pack_block = [&](int qb) {
+        // P and dS of rows 8 h2 .. 8 h2 + 7 of block qb as bf16/f16 B operands
+        auto pack_half = [&](int qb, int h2) {
+            const int r0 = 8 * h2;
+            pb[2 * qb + h2] = pack8<T>(pv[r0], pv[r0 + 1], pv[r0 + 2], pv[r0 + 3], pv[r0 + 4], pv[r0 + 5], pv[r0 + 6],
+                                       pv[r0 + 7]);
+            db8[2 * qb + h2] = pack8<T>(dsr[r0], dsr[r0 + 1], dsr[r0 + 2], dsr[r0 + 3], dsr[r0 + 4], dsr[r0 + 5],
+                                        dsr[r0 + 6], dsr[r0 + 7]);
+        };
+        // elements [r0, r0 + n) of block qb, each followed by what it frees or completes:
+        // the row group's vectors for block `nxt` (if >= 0) and the packed half
+        auto elems = [&](int qb, int r0, int n, int nxt) {
 #pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-                const int r0 = 8 * h2;
-                pb[2 * qb + h2] = pack8<T>(pv[r0], pv[r0 + 1], pv[r0 + 2], pv[r0 + 3], pv[r0 + 4], pv[r0 + 5],
-                                           pv[r0 + 6], pv[r0 + 7]);
-                db8[2 * qb + h2] = pack8<T>(dsr[r0], dsr[r0 + 1], dsr[r0 + 2], dsr[r0 + 3], dsr[r0 + 4], dsr[r0 + 5],
-                                            dsr[r0 + 6], dsr[r0 + 7]);
+            for (int r = r0; r < r0 + n; ++r) {
+                elem(qb, r);
+                if ((r & 3) == 3 && nxt >= 0) load_vec(nxt, r >> 2);
+                if ((r & 7) == 7) pack_half(qb, r >> 3);
             }
         };
 
@@ -181,10 +184,17 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
             fq[g1 % 3] = ld_s16(Qs + 32 * qb * D + roff[kk]);
             fd[g1 % 3] = ld_s16(Ds + 32 * qb * D + roff[kk]);
         };
-        auto mma1 = [&](int g1) {
+        auto mma1s = [&](int g1) {
             const int qb = g1 / NK, kk = g1 % NK;
             sc[qb] = Mfma<T>::mma(as_v8<T>(fq[g1 % 3]), kf[kk], sc[qb]);
+        };
+        auto mma1d = [&](int g1) {
+            const int qb = g1 / NK, kk = g1 % NK;
             dpc[qb] = Mfma<T>::mma(as_v8<T>(fd[g1 % 3]), vf[kk], dpc[qb]);
+        };
+        auto mma1 = [&](int g1) {
+            mma1s(g1);
+            mma1d(g1);
         };
         // ---- dV/dK operand ring: group g2 in [0, 4 * D/32): chunk c = g2 / (D/32), db = g2 % (D/32)
         constexpr int ND = D / 32;
@@ -198,14 +208,28 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
             fo[g2 % 3] = make_uint4(olo.x, olo.y, ohi.x, ohi.y);
             fqt[g2 % 3] = make_uint4(qlo.x, qlo.y, qhi.x, qhi.y);
         };
-        auto mma2 = [&](int g2) {
+        auto mma2v = [&](int g2) {
             const int c = g2 / ND, db = g2 % ND;
             dvacc[db] = Mfma<T>::mma(as_v8<T>(fo[g2 % 3]), pb[c], dvacc[db]);
+        };
+        auto mma2k = [&](int g2) {
+            const int c = g2 / ND, db = g2 % ND;
             dkacc[db] = Mfma<T>::mma(as_v8<T>(fqt[g2 % 3]), db8[c], dkacc[db]);
         };
+        auto mma2 = [&](int g2) {
+            mma2v(g2);
+            mma2k(g2);
+        };
+
+        // One softmax element after every MFMA of phases B and C (two for
+        // D = 64): with one wave per SIMD issue is in order, and a VALU run
+        // only overlaps the MFMA issued just before it.
+        constexpr int EB = 16 / (2 * NK);  // elements per MFMA in phase B
+        constexpr int EC = 16 / (4 * ND);  // and in phase C
 
         // phase A: S/dP of block 0
-        load_vec(0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) load_vec(0, i);
         load1(0);
         load1(1);
 #pragma unroll
@@ -215,35 +239,39 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
             mma1(g1);
             FA_SB();
         }
-        // phase B: S/dP of block 1, softmax of block 0 (row group after every NK/4 groups)
+        // phase B: S/dP of block 1, softmax of block 0 (its row-group vectors
+        // are replaced by block 1's as they are used up)
 #pragma unroll
         for (int g1 = NK; g1 < 2 * NK; ++g1) {
+            const int e = 2 * (g1 - NK) * EB;
             if (g1 + 2 < 2 * NK) load1(g1 + 2);
             FA_SB();
-            mma1(g1);
+            mma1s(g1);
             FA_SB();
-            if ((g1 - NK) % (NK / 4) == NK / 4 - 1) {
-                smax(0, (g1 - NK) / (NK / 4));
-                FA_SB();
-            }
+            elems(0, e, EB, 1);
+            FA_SB();
+            mma1d(g1);
+            FA_SB();
+            elems(0, e + EB, EB, 1);
+            FA_SB();
         }
-        pack_block(0);
-        load_vec(1);
         // phase C: dV/dK of block 0 (chunks 0, 1), softmax of block 1
         load2(0);
         load2(1);
 #pragma unroll
         for (int g2 = 0; g2 < 2 * ND; ++g2) {
+            const int e = 2 * g2 * EC;
             load2(g2 + 2);
             FA_SB();
-            mma2(g2);
+            mma2v(g2);
             FA_SB();
-            if (g2 % (2 * ND / 4) == 2 * ND / 4 - 1) {
-                smax(1, g2 / (2 * ND / 4));
-                FA_SB();
-            }
+            elems(1, e, EC, -1);
+            FA_SB();
+            mma2k(g2);
+            FA_SB();
+            elems(1, e + EC, EC, -1);
+            FA_SB();
         }
-        pack_block(1);
         // phase D: dV/dK of block 1 (chunks 2, 3)
 #pragma unroll
         for (int g2 = 2 * ND; g2 < 4 * ND; ++g2) {

@@ -117,6 +117,17 @@ __device__ __forceinline__ uint4 ld_s16_rows_tr(const uint16_t* tile, int pitch,
     return make_uint4(lo.x, lo.y, hi.x, hi.y);
 }
 
+// Load of a wave-uniform, kernel-invariant value through the scalar cache
+// (s_load): unlike a vector load it is not counted by vmcnt, so waiting for it
+// does not also wait for the direct loads in flight.
+__device__ __forceinline__ float ld_uniform(const float* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return *(const __attribute__((address_space(4))) float*)p;
+#else
+    return *p;
+#endif
+}
+
 // Swizzled 16-bit tile in LDS: rows of exactly D elements, and the 16-byte chunk
 // c of row r stored at chunk position c ^ f(r), f(r) = ((r & 3) * D / 32) ^ ((r >> 2) & 3).
 // With it, three access patterns are free of bank conflicts: 16-byte reads of

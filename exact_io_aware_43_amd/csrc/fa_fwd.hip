@@ -118,7 +118,7 @@ __global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(Args a) {
     float l_run = 0.f;        // this lane's share of the running sum
 
     const float c2 = a.scale_log2;
-    const float slope2 = ALIBI ? a.slopes[h] * kLog2e : 0.f;
+    const float slope2 = ALIBI ? ld_uniform(a.slopes + h) * kLog2e : 0.f;
 
     auto compute = [&](const uint16_t* Ks, int kt) {
         const uint16_t* Vs = Ks + TILE;

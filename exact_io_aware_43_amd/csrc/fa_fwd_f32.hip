@@ -48,7 +48,7 @@ __global__ __launch_bounds__(F_NT) void fwd_f32_kernel(Args a) {
         o[c] = 0.f;
     }
     const float c2 = a.scale_log2;
-    const float slope2 = ALIBI ? a.slopes[h] * kLog2e : 0.f;
+    const float slope2 = ALIBI ? ld_uniform(a.slopes + h) * kLog2e : 0.f;
     float m_run = -INFINITY, l_run = 0.f;
 
     const int kend = CAUSAL ? min(len, q0 + F_ROWS) : len;
