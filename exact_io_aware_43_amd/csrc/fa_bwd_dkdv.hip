@@ -154,8 +154,10 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
             }
             float p = exp2_fast(fmaf(sc[qb][r], c2, bias));
             if (MASKED && key > qi) p = 0.f;
+            float ds = p * (dpc[qb][r] - dv);
+            asm volatile("" : "+v"(p), "+v"(ds));  // materialise here: keeps the VALU work in its MFMA slot
             pv[r] = p;
-            dsr[r] = p * (dpc[qb][r] - dv);
+            dsr[r] = ds;
         };
         // P and dS of rows 8 h2 .. 8 h2 + 7 of block qb as bf16/f16 B operands
         auto pack_half = [&](int qb, int h2) {

@@ -222,17 +222,21 @@ struct DmaTile {
     }
 };
 
-
 // Direct global -> LDS load of 64 consecutive fp32 values (one wave, 4 bytes per
-// lane) from `src` (all 64 in bounds) into `dst`.
-// The global pointer is cast to the global address space explicitly: left
-// implicit, the conversion is rejected in the host compilation pass, which
-// then silently drops the host launch stubs of every kernel that uses it.
+// lane) from `src` (all 64 in bounds) into `dst`. Buffer form, like the tiles:
+// the FLAT-encoded global_load_lds would also count against lgkmcnt, after
+// which the compiler can no longer count LDS reads exactly and waits for all
+// of them before every MFMA, defeating the operand prefetch rings.
 __device__ __forceinline__ void dma_vec64(float* dst, const float* src, int lane) {
-    typedef __attribute__((address_space(3))) void lds_void;
-    typedef __attribute__((address_space(1))) void gbl_void;
-    __builtin_amdgcn_global_load_lds((gbl_void*)(src + lane),
-                                     (lds_void*)((__attribute__((address_space(3))) float*)dst), 4, 0, 0);
+#if defined(__HIP_DEVICE_COMPILE__)  // the buffer descriptor type exists for the GPU target only
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(src), (short)0, 64 * 4, kBufferWord3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsrc, (__attribute__((address_space(3))) void*)((__attribute__((address_space(3))) float*)dst), 4,
+        (uint32_t)lane * 4u, 0, 0, 0);
+#else
+    (void)dst, (void)src, (void)lane;
+#endif
 }
 
 // The double-buffered tile loop shared by the kernels: body(stage, i) runs for
