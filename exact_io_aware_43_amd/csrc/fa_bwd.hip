@@ -148,81 +148,137 @@ __global__ __launch_bounds__(NT, 1) void bwd_dq_kernel(Args a) {
         if (!(wave_live && (!CAUSAL || k0 <= qw + 31))) return;
         const uint16_t* Ks = S;
         const uint16_t* Vs = S + TILE;
-        // S^T = K Q^T and dP^T = V dO^T; operand loads two (kb, kk) groups ahead
-        // of the MFMAs, order kept by scheduling barriers.
-        constexpr int NG1 = DQ_BK / 32 * D / 16;
-        f32x16 s[DQ_BK / 32], dp[DQ_BK / 32];
+        // S^T = K Q^T and dP^T = V dO^T per 32-key block kb, then
+        // dQ^T += K^T dS^T per 16-key chunk c. With one wave per SIMD issue is
+        // in order, so the softmax backward of each element is placed right
+        // after an MFMA it does not depend on:
+        //   A: S/dP of block 0
+        //   B: S/dP of block 1      + softmax of block 0 (one element per MFMA)
+        //   C: dQ of chunks 0, 1    + softmax of block 1, rows 0..7
+        //   D: dQ of chunks 2, 3    + softmax of block 1, rows 8..15 (during chunk 2)
+        // Operand loads run two MFMA groups ahead through register rings;
+        // scheduling barriers keep the order.
+        static_assert(DQ_BK == 64, "two 32-key blocks per tile");
+        constexpr int NK = D / 16, ND = D / 32;
+        f32x16 s[2], dp[2];
 #pragma unroll
-        for (int kb = 0; kb < DQ_BK / 32; ++kb) {
+        for (int kb = 0; kb < 2; ++kb) {
             s[kb] = f32x16{};
             dp[kb] = f32x16{};
         }
-        uint4 fk[3], fv[3];
-        auto load1 = [&](int gi) {
-            const int kb = gi / (D / 16), kk = gi % (D / 16);
-            fk[gi % 3] = ld_s16(Ks + 32 * kb * D + roff[kk]);
-            fv[gi % 3] = ld_s16(Vs + 32 * kb * D + roff[kk]);
-        };
-        load1(0);
-        load1(1);
-#pragma unroll
-        for (int gi = 0; gi < NG1; ++gi) {
-            if (gi + 2 < NG1) load1(gi + 2);
-            __builtin_amdgcn_sched_barrier(0);
-            const int kb = gi / (D / 16), kk = gi % (D / 16);
-            s[kb] = Mfma<T>::mma(as_v8<T>(fk[gi % 3]), qf[kk], s[kb]);
-            dp[kb] = Mfma<T>::mma(as_v8<T>(fv[gi % 3]), df[kk], dp[kb]);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        // dS^T = P^T (dP^T - D), P^T = exp2(S^T * scale * log2(e) - L * log2(e)) [+ ALiBi];
-        // only tiles with keys past the end or across the diagonal take the masked path.
-        auto softmax_bwd = [&](auto masked) {
-#pragma unroll
-            for (int kb = 0; kb < DQ_BK / 32; ++kb) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int kj = k0 + 32 * kb + 8 * (r >> 2) + 4 * kg + (r & 3);
-                    float bias = -lse2;
-                    if (ALIBI) {
-                        const float dist = (float)(qi - kj);
-                        bias -= slope2 * (CAUSAL ? dist : fabsf(dist));
-                    }
-                    float p = exp2_fast(fmaf(s[kb][r], c2, bias));
-                    if (decltype(masked)::value && (kj >= len || (CAUSAL && kj > qi))) p = 0.f;
-                    dp[kb][r] = p * (dp[kb][r] - dsum);
-                }
+      // masked: a compile-time flag, true for tiles with keys past the end or
+      // across the diagonal
+      auto body = [&](auto masked_t) {
+        constexpr bool masked = decltype(masked_t)::value;
+        // softmax backward of element r of block kb: dS^T = P^T (dP^T - D),
+        // P^T = exp2(S^T * scale * log2(e) - L * log2(e)) [+ ALiBi].
+        auto elem = [&](int kb, int r) {
+            const int kj = k0 + 32 * kb + 8 * (r >> 2) + 4 * kg + (r & 3);
+            float bias = -lse2;
+            if (ALIBI) {
+                const float dist = (float)(qi - kj);
+                bias -= slope2 * (CAUSAL ? dist : fabsf(dist));
             }
+            float p = exp2_fast(fmaf(s[kb][r], c2, bias));
+            if (masked && (kj >= len || (CAUSAL && kj > qi))) p = 0.f;
+            float ds = p * (dp[kb][r] - dsum);
+            asm volatile("" : "+v"(ds));  // materialise here: keeps the VALU work in its MFMA slot
+            dp[kb][r] = ds;
         };
-        if ((k0 + DQ_BK > len) || (CAUSAL && k0 + DQ_BK - 1 > qw))
-            softmax_bwd(std::true_type{});
-        else
-            softmax_bwd(std::false_type{});
-        // dQ^T += K^T dS^T, 16 keys per MFMA; transposed loads two groups ahead
-        constexpr int NG2 = DQ_BK / 16 * D / 32;
-        V8<T> dsb[DQ_BK / 16];
-#pragma unroll
-        for (int c = 0; c < DQ_BK / 16; ++c) {
+        V8<T> dsb[4];
+        auto pack_chunk = [&](int c) {
             const int kb = c >> 1, r0 = 8 * (c & 1);
             dsb[c] = pack8<T>(dp[kb][r0], dp[kb][r0 + 1], dp[kb][r0 + 2], dp[kb][r0 + 3], dp[kb][r0 + 4],
                               dp[kb][r0 + 5], dp[kb][r0 + 6], dp[kb][r0 + 7]);
-        }
+        };
+
+        uint4 fk[3], fv[3];
+        auto load1 = [&](int gi) {
+            const int kb = gi / NK, kk = gi % NK;
+            fk[gi % 3] = ld_s16(Ks + 32 * kb * D + roff[kk]);
+            fv[gi % 3] = ld_s16(Vs + 32 * kb * D + roff[kk]);
+        };
+        auto mmaS = [&](int gi) {
+            const int kb = gi / NK, kk = gi % NK;
+            s[kb] = Mfma<T>::mma(as_v8<T>(fk[gi % 3]), qf[kk], s[kb]);
+        };
+        auto mmaP = [&](int gi) {
+            const int kb = gi / NK, kk = gi % NK;
+            dp[kb] = Mfma<T>::mma(as_v8<T>(fv[gi % 3]), df[kk], dp[kb]);
+        };
         uint4 fkt[3];
         auto load2 = [&](int gi) {
-            const int c = gi / (D / 32), db = gi % (D / 32);
+            const int c = gi / ND, db = gi % ND;
             const uint2 lo = ld_s8_tr(Ks + 16 * c * D + toff[db][0]);
             const uint2 hi = ld_s8_tr(Ks + 16 * c * D + toff[db][1]);
             fkt[gi % 3] = make_uint4(lo.x, lo.y, hi.x, hi.y);
         };
+        auto mma2 = [&](int gi) {
+            const int c = gi / ND, db = gi % ND;
+            dqacc[db] = Mfma<T>::mma(as_v8<T>(fkt[gi % 3]), dsb[c], dqacc[db]);
+        };
+        constexpr int EB = 16 / (2 * NK);  // block-0 elements per MFMA in phase B
+
+        // phase A
+        load1(0);
+        load1(1);
+#pragma unroll
+        for (int gi = 0; gi < NK; ++gi) {
+            load1(gi + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            mmaS(gi);
+            mmaP(gi);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // phase B
+#pragma unroll
+        for (int gi = NK; gi < 2 * NK; ++gi) {
+            const int e = 2 * (gi - NK) * EB;
+            if (gi + 2 < 2 * NK) load1(gi + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            mmaS(gi);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int r = e; r < e + EB; ++r) elem(0, r);
+            __builtin_amdgcn_sched_barrier(0);
+            mmaP(gi);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int r = e + EB; r < e + 2 * EB; ++r) elem(0, r);
+            if (e + 2 * EB == 8) pack_chunk(0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        pack_chunk(1);
+        // phases C and D: 4 ND MFMAs over chunks 0..3; block-1 rows 0..7 spread
+        // over chunks 0 and 1, rows 8..15 over chunk 2
         load2(0);
         load2(1);
 #pragma unroll
-        for (int gi = 0; gi < NG2; ++gi) {
-            if (gi + 2 < NG2) load2(gi + 2);
+        for (int gi = 0; gi < 4 * ND; ++gi) {
+            const int c = gi / ND;
+            if (gi + 2 < 4 * ND) load2(gi + 2);
             __builtin_amdgcn_sched_barrier(0);
-            const int c = gi / (D / 32), db = gi % (D / 32);
-            dqacc[db] = Mfma<T>::mma(as_v8<T>(fkt[gi % 3]), dsb[c], dqacc[db]);
+            mma2(gi);
+            __builtin_amdgcn_sched_barrier(0);
+            if (c < 2) {
+                constexpr int E = 8 / (2 * ND);
+#pragma unroll
+                for (int r = gi * E; r < gi * E + E; ++r) elem(1, r);
+                if (gi == 2 * ND - 1) pack_chunk(2);
+            } else if (c == 2) {
+                constexpr int E = 8 / ND;
+                const int g = gi - 2 * ND;
+#pragma unroll
+                for (int r = 8 + g * E; r < 8 + g * E + E; ++r) elem(1, r);
+                if (gi == 3 * ND - 1) pack_chunk(3);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
+      };
+        if ((k0 + DQ_BK > len) || (CAUSAL && k0 + DQ_BK - 1 > qw))
+            body(std::true_type{});
+        else
+            body(std::false_type{});
     };
 
     two_stage_loop(stA, stB, nkt, issue, compute);
