@@ -186,7 +186,10 @@ struct DmaTile {
     static constexpr int INSTR = ROWS * D * 2 / 1024;
     static constexpr int PER_WAVE = INSTR / NW;
     static_assert(INSTR % NW == 0, "tile must split evenly over the waves");
-    uint32_t boff[PER_WAVE];  // byte offset of this lane's chunk from the tile's first row (row stride `ld`)
+    static_assert(PER_WAVE <= 4, "the immediate offset field reaches 4 KB");
+    // byte offset of this lane's chunk of instruction i from the tile's first
+    // row (row stride `ld`), less the instruction's immediate offset 1024 i
+    uint32_t boff[PER_WAVE];
     uint32_t ld2;             // row stride in bytes
 
     __device__ __forceinline__ void init(int wave, int lane, size_t ld) {
@@ -196,7 +199,7 @@ struct DmaTile {
             const int p = (wave * PER_WAVE + i) * 64 + lane;  // chunk index in LDS order
             const int row = p / (D / 8), pos = p % (D / 8);
             const int f = ((row & 3) * (D / 32)) ^ ((row >> 2) & 3);
-            boff[i] = (uint32_t)row * ld2 + 16u * (uint32_t)(pos ^ f);
+            boff[i] = (uint32_t)row * ld2 + 16u * (uint32_t)(pos ^ f) - 1024u * (uint32_t)i;
         }
     }
 
@@ -209,13 +212,15 @@ struct DmaTile {
         const uint32_t bytes = valid > 0 ? (uint32_t)(valid - 1) * ld2 + D * 2 : 0u;
         const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint16_t*>(base) + (size_t)row_start * (ld2 / 2), (short)0, (int)bytes, kBufferWord3);
-#pragma unroll
-        for (int i = 0; i < PER_WAVE; ++i) {
-            uint16_t* dst = tile + (wave * PER_WAVE + i) * 512;  // 1 KB per instruction
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rsrc, (__attribute__((address_space(3))) void*)((__attribute__((address_space(3))) uint16_t*)dst), 16,
-                boff[i], 0, 0, 0);
-        }
+        // One LDS base (M0) per wave and tile: the immediate offset 1024 i of
+        // instruction i moves both the global and the LDS address, so M0 is
+        // set once instead of once per instruction from a vector register.
+        typedef __attribute__((address_space(3))) void lds_void;
+        lds_void* dst = (lds_void*)((__attribute__((address_space(3))) uint16_t*)(tile + wave * PER_WAVE * 512));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, boff[0], 0, 0, 0);
+        if constexpr (PER_WAVE > 1) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, boff[1], 0, 1024, 0);
+        if constexpr (PER_WAVE > 2) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, boff[2], 0, 2048, 0);
+        if constexpr (PER_WAVE > 3) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, boff[3], 0, 3072, 0);
 #else
         (void)tile, (void)base, (void)row_start, (void)nrows, (void)wave;
 #endif
