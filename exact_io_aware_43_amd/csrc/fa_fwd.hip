@@ -7,12 +7,14 @@
 // one of Key design 4 (one workgroup per query tile, parallel over the
 // sequence), and only O and L = m + ln(l) are written.
 //
-// Work decomposition. One workgroup of 4 waves owns BR = 128 query rows of one
+// Work decomposition. One workgroup of 8 waves owns BR = 256 query rows of one
 // (sequence, query head); each wave owns 32 of them. K and V of the head's kv
 // head stream through LDS in tiles of BC = 64 keys, double buffered: the next
-// tile's loads are in flight while the current tile is multiplied. Two
-// workgroups share a compute unit, so each SIMD interleaves the matrix work of
-// one wave with the softmax of the other.
+// tile's loads are in flight while the current tile is multiplied. The 8 waves
+// share every tile (the direct loads that stage it cost issue time per wave,
+// so sharing halves that cost against two 4-wave groups), and two waves run
+// on each SIMD, which interleaves the matrix work of one with the softmax of
+// the other.
 //
 // Register orientation. Each wave computes the transposed score tile
 // S^T = K Q^T (keys x queries) so that in the MFMA accumulator every lane holds
@@ -40,13 +42,13 @@
 namespace fa {
 namespace {
 
-constexpr int BR = 128;    // query rows per workgroup
+constexpr int BR = 256;    // query rows per workgroup
 constexpr int BC = 64;     // keys per K/V tile
-constexpr int NT = 256;    // threads per workgroup (4 waves)
+constexpr int NT = 512;    // threads per workgroup (8 waves, two per SIMD)
 constexpr float TAU = 8.f; // lazy-rescale threshold, log2 units
 
 template <typename T, int D, bool CAUSAL, bool ALIBI>
-__global__ __launch_bounds__(NT, 2) void fwd_mfma_kernel(Args a) {
+__global__ __launch_bounds__(NT, 1) void fwd_mfma_kernel(Args a) {
     // Two named K/V stages (swizzled [BC x D] tiles, K then V): the prefetch
     // into one overlaps the reads of the other, which the compiler can only
     // prove independent when they are distinct arrays.
