@@ -43,7 +43,7 @@ namespace fa {
 namespace {
 
 constexpr int BR = 256;    // query rows per workgroup
-constexpr int BC = 64;     // keys per K/V tile
+constexpr int BC = 128;    // keys per K/V tile
 constexpr int NT = 512;    // threads per workgroup (8 waves, two per SIMD)
 constexpr float TAU = 8.f; // lazy-rescale threshold, log2 units
 
