@@ -15,8 +15,8 @@ Besides the step rate the line carries:
     dense bf16 MFMA peak (or HBM bandwidth for the memory-bound pre-pass), with
     HBM traffic from the committed rocprofv3 counter summary when that summary
     was taken on the current kernel sources (else null);
-  * ``cpu_baseline``: the fp64 CPU oracle timed on this host on one
-    (batch, head) slice of the same workload (forward + backward);
+  * ``cpu_baseline``: the fp64 CPU oracle timed on this host on the first
+    heads of the same workload (forward + backward, about ten seconds);
   * ``memory``: device bytes the step allocates versus a materialised-score
     baseline that stores S and P.
 """
@@ -39,18 +39,25 @@ PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 4096 dense bf16 FLOP/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = os.path.join(ROOT, "exact_io_aware_43_amd", "csrc")
-KERNEL_SOURCES = {
-    "fwd": ["fa_fwd.hip", "fa_device.hpp", "fa_internal.hpp"],
-    "bwd_dsum": ["fa_bwd.hip", "fa_device.hpp", "fa_internal.hpp"],
-    "bwd_dkdv": ["fa_bwd.hip", "fa_device.hpp", "fa_internal.hpp"],
-    "bwd_dq": ["fa_bwd.hip", "fa_device.hpp", "fa_internal.hpp"],
+KERNEL_SOURCES = {  # what each kernel's machine code depends on (the build flags included)
+    "fwd": ["fa_fwd.hip", "fa_device.hpp", "fa_internal.hpp", "../build.py"],
+    "bwd_dsum": ["fa_bwd.hip", "fa_device.hpp", "fa_internal.hpp", "../build.py"],
+    "bwd_dkdv": ["fa_bwd_dkdv.hip", "fa_device.hpp", "fa_internal.hpp", "../build.py"],
+    "bwd_dq": ["fa_bwd.hip", "fa_device.hpp", "fa_internal.hpp", "../build.py"],
 }
+# rocprofv3 kernel-name fragments of the four kernels
+KERNEL_SYMBOLS = {"fwd": "fwd_mfma_kernel", "bwd_dsum": "bwd_dsum_kernel", "bwd_dkdv": "bwd_dkdv_kernel",
+                  "bwd_dq": "bwd_dq_kernel"}
+# plain elementwise copy used to calibrate the HBM byte counters: fp32 negation
+# of COPY_BYTES into a second buffer reads and writes COPY_BYTES once each
+COPY_BYTES = 1 << 30
+COPY_SYMBOL = "neg_kernel"
 
 
 def source_hash(kernel: str) -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(CSRC, f), "rb") as fh:
+        with open(os.path.normpath(os.path.join(CSRC, f)), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
@@ -64,11 +71,19 @@ def parse():
     ap.add_argument("--kernel-reps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the measurement run a plain 1 GiB fp32 copy (negation) for counter calibration")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, both "
+                         "with --copy-calibration) into profiles/traffic.json and exit; needs no GPU")
     return ap.parse_args()
 
 
 def main():
     args = parse()
+    if args.traffic_from:
+        summarise_traffic(args.workload, *args.traffic_from)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the attention kernels run on a single device and this "
@@ -244,9 +259,82 @@ def main():
     out["bwd_frac_of_peak"] = round(out["bwd_tflops"] / PEAK_BF16_TFLOPS, 4)
     print(json.dumps(out), flush=True)
 
+    if args.copy_calibration:
+        x = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        torch.neg(x, out=y)
+        torch.cuda.synchronize()
+        print(f"[bench] copy calibration: neg of {COPY_BYTES} bytes", file=sys.stderr, flush=True)
+
+
+def _counter_rows(d):
+    """(kernel name, dispatch id, counter, value) from a rocprofv3 --output-format csv directory."""
+    import csv
+    import glob
+
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *counter_collection.csv under {d}")
+    for fn in files:
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                yield r["Kernel_Name"], (fn, r["Dispatch_Id"]), r["Counter_Name"], float(r["Counter_Value"])
+
+
+def _per_dispatch(d, counter):
+    """Mean counter value (KiB) per dispatch for each kernel of interest and the copy kernel."""
+    acc = {}
+    for name, disp, cname, val in _counter_rows(d):
+        if cname != counter:
+            continue
+        key = next((k for k, sym in KERNEL_SYMBOLS.items() if sym in name), None)
+        if key is None and COPY_SYMBOL in name:
+            key = "copy"
+        if key is None:
+            continue
+        acc.setdefault(key, {}).setdefault(disp, 0.0)
+        acc[key][disp] += val
+    return {k: (sum(v.values()) / len(v), len(v)) for k, v in acc.items()}
+
+
+def summarise_traffic(workload, fetch_dir, write_dir):
+    """HBM bytes per launch of each kernel from FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch), each scaled by what the same counter reads for the 1 GiB copy."""
+    fetch = _per_dispatch(fetch_dir, "FETCH_SIZE")
+    write = _per_dispatch(write_dir, "WRITE_SIZE")
+    if "copy" not in fetch or "copy" not in write:
+        raise SystemExit("the counter runs hold no copy-calibration dispatch (run bench.py with --copy-calibration)")
+    f_fetch = COPY_BYTES / (fetch["copy"][0] * 1024.0)
+    f_write = COPY_BYTES / (write["copy"][0] * 1024.0)
+    res = {}
+    for k in KERNEL_SYMBOLS:
+        if k in fetch and k in write:
+            fb = fetch[k][0] * 1024.0 * f_fetch
+            wb = write[k][0] * 1024.0 * f_write
+            res[k] = {"fetch_bytes": round(fb), "write_bytes": round(wb), "bytes_per_launch": round(fb + wb),
+                      "fetch_kib_raw": fetch[k][0], "write_kib_raw": write[k][0],
+                      "dispatches": [fetch[k][1], write[k][1]], "source_hash": source_hash(k)}
+    allw = {}
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            allw = json.load(f)
+    allw[workload] = res
+    allw.setdefault("_calibration", {})[workload] = {
+        "copy_bytes": COPY_BYTES, "copy_fetch_kib": fetch["copy"][0], "copy_write_kib": write["copy"][0],
+        "fetch_factor": f_fetch, "write_factor": f_write}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(allw, f, indent=1, sort_keys=True)
+    print(json.dumps({workload: res, "fetch_factor": f_fetch, "write_factor": f_write}, indent=1))
+
+
+CPU_SAMPLE_SECONDS = 10.0  # heads are added to the sample until this much CPU time is spent
+CPU_SAMPLE_MAX_HEADS = 8
+
 
 def cpu_baseline(w, inp, lens):
-    """The fp64 oracle, as it is, on one (sequence 0, head 0) slice: forward + backward."""
+    """The fp64 oracle, as it is, on the first heads of sequence 0: forward + backward,
+    one head at a time, until CPU_SAMPLE_SECONDS have passed (at most
+    CPU_SAMPLE_MAX_HEADS heads)."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -256,25 +344,30 @@ def cpu_baseline(w, inp, lens):
     n = lens[0]
     G = w.H // w.Hkv
     sl = (0, slice(0, n)) if inp["cu_seqlens"] is None else (slice(0, n),)
-    q = OA._f64(inp["q"][sl][:, 0])
-    k = OA._f64(inp["k"][sl][:, 0 // G])
-    v = OA._f64(inp["v"][sl][:, 0 // G])
-    do = OA._f64(inp["do"][sl][:, 0])
-    slope = None if inp["alibi_slopes"] is None else float(inp["alibi_slopes"][0])
-    print(f"[bench] cpu baseline: oracle fwd+bwd on one head, n={n}", file=sys.stderr, flush=True)
-    t0 = time.perf_counter()
-    OA.head_fwd(q, k, v, inp["scale"], w.causal, slope)
-    OA.head_bwd(q, k, v, do, inp["scale"], w.causal, slope)
-    t = time.perf_counter() - t0
+    print(f"[bench] cpu baseline: oracle fwd+bwd per head, n={n}", file=sys.stderr, flush=True)
+    t = 0.0
+    heads = 0
+    while heads < min(w.H, CPU_SAMPLE_MAX_HEADS) and t < CPU_SAMPLE_SECONDS:
+        h = heads
+        q = OA._f64(inp["q"][sl][:, h])
+        k = OA._f64(inp["k"][sl][:, h // G])
+        v = OA._f64(inp["v"][sl][:, h // G])
+        do = OA._f64(inp["do"][sl][:, h])
+        slope = None if inp["alibi_slopes"] is None else float(inp["alibi_slopes"][h])
+        t0 = time.perf_counter()
+        OA.head_fwd(q, k, v, inp["scale"], w.causal, slope)
+        OA.head_bwd(q, k, v, do, inp["scale"], w.causal, slope)
+        t += time.perf_counter() - t0
+        heads += 1
     one = w.with_(B=1, H=1, Hkv=1)
-    work = flops(one, [n]) + flops(one, [n], backward=True)
+    work = heads * (flops(one, [n]) + flops(one, [n], backward=True))
     blas = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
     return {
         "value": round(work / t / 1e12, 5),
         "unit": "TFLOP/s",
         "cores": int(max(blas) if blas else 1),
         "kind": "oracle",
-        "sample": f"one (batch 0, head 0) slice of {w.name}: N={n}, d={w.d}, causal={w.causal}; "
+        "sample": f"heads 0..{heads - 1} of sequence 0 of {w.name}: N={n}, d={w.d}, causal={w.causal}; "
                   f"fp64 numpy forward + backward, {t:.1f} s",
         "host_cpus_available": len(os.sched_getaffinity(0)),
         "seconds": round(t, 2),

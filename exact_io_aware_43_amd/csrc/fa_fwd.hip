@@ -149,10 +149,12 @@ __global__ __launch_bounds__(NT, 1) void fwd_mfma_kernel(Args a) {
         }
 
         // Scores in log2 units. Plain tiles keep the raw score and fold the
-        // scale into the exponent's FMA; ALiBi and edge tiles materialise
+        // scale into the exponent's FMA; ALiBi, edge and negative-scale tiles materialise
         // t = s * c2 + bias (or -inf when masked) and use scale 1 below.
         const bool edge = (k0 + BC > len) || (CAUSAL && k0 + BC - 1 > qw);
-        const bool materialise = ALIBI || edge;
+        // a negative scale reverses the score order: the max of raw scores
+        // would be the wrong end, so such tiles materialise too
+        const bool materialise = ALIBI || edge || !(c2 >= 0.f);
         float mt;
         if (materialise) {
             mt = -INFINITY;

@@ -1,7 +1,7 @@
 """GPU parity: libfa (through the C ABI) against the fp64 oracle on identical seeded inputs.
 
 Small shapes are compared element by element over whole tensors; they span
-several 64-key and 128-query tiles with ragged tails. The named full-size
+several key and query tiles with ragged tails. The named full-size
 workloads run in the same launch configuration the benchmark times and are
 compared on sampled rows (forward) or whole kv-head groups (backward), which
 the oracle computes exactly.
@@ -114,6 +114,21 @@ def _bwd_case(w, seed=0, lengths=None):
     o, lse = gpu_fwd(w, dinp)
     grads = gpu_bwd(w, dinp, o, lse)
     return check_bwd_full(w, inp, grads)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("alibi", [False, True])
+def test_negative_scale(causal, alibi):
+    """Any finite scale is a valid argument; a negative one reverses the score
+    order, which a maximum taken on raw scores would get wrong."""
+    w = Workload(f"negscale_c{int(causal)}_a{int(alibi)}", "bf16", 1, 2, 1, 200, 128, causal=causal, alibi=alibi)
+    _banner(f"negative scale {w}")
+    inp = make_inputs(w, 11, with_grad=True)
+    inp["scale"] = -inp["scale"]
+    dinp = to_dev(inp)
+    o, lse = gpu_fwd(w, dinp)
+    check_fwd_full(w, inp, o, lse)
+    check_bwd_full(w, inp, gpu_bwd(w, dinp, o, lse))
 
 
 BWD_SMALL = []
