@@ -14,9 +14,11 @@
 //                 see the keys, accumulating dV = P^T dO and dK = dS^T Q in
 //                 registers. No atomics: each dK / dV row has one owner, and
 //                 the GQA group sum happens in the accumulators.
-//   3. bwd_dq:    one workgroup per (128-query tile, query head, sequence); Q
-//                 and dO stay in registers and 64-key K, V tiles stream through
-//                 LDS; dQ = dS K is accumulated in registers.
+//   3. bwd_dq:    one workgroup of 8 waves per (256-query tile, query head,
+//                 sequence); Q and dO stay in registers and 64-key K, V tiles
+//                 stream through LDS, shared by all 8 waves; dQ = dS K is
+//                 accumulated in registers. Two waves run on each SIMD (one
+//                 workgroup of 4 waves for d = 128 without causal mask).
 // Splitting dQ from dK/dV recomputes S and dP twice but needs no atomic
 // reduction, so the result is bitwise reproducible (the deterministic option
 // the page's Limitations section discusses).
@@ -73,11 +75,20 @@ __global__ __launch_bounds__(NT) void bwd_dsum_kernel(Args a) {
 }
 
 // ---------------------------------------------------------------- dQ
-constexpr int DQ_BQ = 128;  // queries per workgroup (32 per wave)
-constexpr int DQ_BK = 64;   // keys per K/V tile
+constexpr int DQ_BK = 64;  // keys per K/V tile
+
+// NW waves per workgroup, 32 queries each: 8 (two per SIMD) where the kernel
+// fits in 256 registers per lane. The d = 128 non-causal instance does not
+// (the compiler spills it there) and runs 4 waves, one per SIMD.
+template <int D, bool CAUSAL>
+constexpr int dq_waves() {
+    return (D == 128 && !CAUSAL) ? 4 : 8;
+}
 
 template <typename T, int D, bool CAUSAL, bool ALIBI>
-__global__ __launch_bounds__(NT, 1) void bwd_dq_kernel(Args a) {
+__global__ __launch_bounds__((64 * dq_waves<D, CAUSAL>()), 1) void bwd_dq_kernel(Args a) {
+    constexpr int DQ_NT = 64 * dq_waves<D, CAUSAL>();
+    constexpr int DQ_BQ = 32 * dq_waves<D, CAUSAL>();
     constexpr int TILE = DQ_BK * D;  // stage: K tile then V tile, swizzled
     __shared__ __attribute__((aligned(16))) uint16_t stA[2 * TILE];
     __shared__ __attribute__((aligned(16))) uint16_t stB[2 * TILE];
@@ -136,7 +147,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_dq_kernel(Args a) {
     const T* Kg = reinterpret_cast<const T*>(a.k) + (size_t)row0 * ldk + (size_t)g * D;
     const T* Vg = reinterpret_cast<const T*>(a.v) + (size_t)row0 * ldk + (size_t)g * D;
 
-    DmaTile<D, DQ_BK, NT / 64> dma;
+    DmaTile<D, DQ_BK, DQ_NT / 64> dma;
     dma.init(wave, lane, ldk);
     auto issue = [&](uint16_t* S, int kt) {
         dma.issue(S, reinterpret_cast<const uint16_t*>(Kg), kt * DQ_BK, len, wave);
@@ -148,133 +159,74 @@ __global__ __launch_bounds__(NT, 1) void bwd_dq_kernel(Args a) {
         if (!(wave_live && (!CAUSAL || k0 <= qw + 31))) return;
         const uint16_t* Ks = S;
         const uint16_t* Vs = S + TILE;
-        // S^T = K Q^T and dP^T = V dO^T per 32-key block kb, then
-        // dQ^T += K^T dS^T per 16-key chunk c. With one wave per SIMD issue is
-        // in order, so the softmax backward of each element is placed right
-        // after an MFMA it does not depend on:
-        //   A: S/dP of block 0
-        //   B: S/dP of block 1      + softmax of block 0 (one element per MFMA)
-        //   C: dQ of chunks 0, 1    + softmax of block 1, rows 0..7
-        //   D: dQ of chunks 2, 3    + softmax of block 1, rows 8..15 (during chunk 2)
-        // Operand loads run two MFMA groups ahead through register rings;
-        // scheduling barriers keep the order.
-        static_assert(DQ_BK == 64, "two 32-key blocks per tile");
+        // Per 32-key block kb: S^T = K Q^T and dP^T = V dO^T, the softmax
+        // backward, then dQ^T += K^T dS^T over the block's two 16-key chunks.
+        // One block's scores at a time keep the wave within the register
+        // budget of two waves per SIMD; the other wave on the SIMD fills the
+        // MFMA pipe during this one's softmax. Operand loads run two MFMA
+        // groups ahead through register rings; scheduling barriers keep the
+        // order.
         constexpr int NK = D / 16, ND = D / 32;
-        f32x16 s[2], dp[2];
+        // masked: a compile-time flag, true for tiles with keys past the end or
+        // across the diagonal
+        auto body = [&](auto masked_t) {
+            constexpr bool masked = decltype(masked_t)::value;
+            uint4 fk[3], fv[3], fkt[3];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            s[kb] = f32x16{};
-            dp[kb] = f32x16{};
-        }
-      // masked: a compile-time flag, true for tiles with keys past the end or
-      // across the diagonal
-      auto body = [&](auto masked_t) {
-        constexpr bool masked = decltype(masked_t)::value;
-        // softmax backward of element r of block kb: dS^T = P^T (dP^T - D),
-        // P^T = exp2(S^T * scale * log2(e) - L * log2(e)) [+ ALiBi].
-        auto elem = [&](int kb, int r) {
-            const int kj = k0 + 32 * kb + 8 * (r >> 2) + 4 * kg + (r & 3);
-            float bias = -lse2;
-            if (ALIBI) {
-                const float dist = (float)(qi - kj);
-                bias -= slope2 * (CAUSAL ? dist : fabsf(dist));
+            for (int kb = 0; kb < DQ_BK / 32; ++kb) {
+                f32x16 s = f32x16{}, dp = f32x16{};
+                auto load1 = [&](int kk) {
+                    fk[kk % 3] = ld_s16(Ks + 32 * kb * D + roff[kk]);
+                    fv[kk % 3] = ld_s16(Vs + 32 * kb * D + roff[kk]);
+                };
+                load1(0);
+                load1(1);
+#pragma unroll
+                for (int kk = 0; kk < NK; ++kk) {
+                    if (kk + 2 < NK) load1(kk + 2);
+                    __builtin_amdgcn_sched_barrier(0);
+                    s = Mfma<T>::mma(as_v8<T>(fk[kk % 3]), qf[kk], s);
+                    dp = Mfma<T>::mma(as_v8<T>(fv[kk % 3]), df[kk], dp);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                // dS^T = P^T (dP^T - D), P^T = exp2(S^T * scale * log2(e) - L * log2(e)) [+ ALiBi]
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int kj = k0 + 32 * kb + 8 * (r >> 2) + 4 * kg + (r & 3);
+                    float bias = -lse2;
+                    if (ALIBI) {
+                        const float dist = (float)(qi - kj);
+                        bias -= slope2 * (CAUSAL ? dist : fabsf(dist));
+                    }
+                    float p = exp2_fast(fmaf(s[r], c2, bias));
+                    if (masked && (kj >= len || (CAUSAL && kj > qi))) p = 0.f;
+                    dp[r] = p * (dp[r] - dsum);
+                }
+                V8<T> dsb[2];
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    const int r0 = 8 * h2;
+                    dsb[h2] = pack8<T>(dp[r0], dp[r0 + 1], dp[r0 + 2], dp[r0 + 3], dp[r0 + 4], dp[r0 + 5], dp[r0 + 6],
+                                       dp[r0 + 7]);
+                }
+                // dQ^T += K^T dS^T for chunks c = 2 kb, 2 kb + 1
+                auto load2 = [&](int gi) {
+                    const int c = 2 * kb + gi / ND, db = gi % ND;
+                    const uint2 lo = ld_s8_tr(Ks + 16 * c * D + toff[db][0]);
+                    const uint2 hi = ld_s8_tr(Ks + 16 * c * D + toff[db][1]);
+                    fkt[gi % 3] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                };
+                load2(0);
+                load2(1);
+#pragma unroll
+                for (int gi = 0; gi < 2 * ND; ++gi) {
+                    if (gi + 2 < 2 * ND) load2(gi + 2);
+                    __builtin_amdgcn_sched_barrier(0);
+                    dqacc[gi % ND] = Mfma<T>::mma(as_v8<T>(fkt[gi % 3]), dsb[gi / ND], dqacc[gi % ND]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
-            float p = exp2_fast(fmaf(s[kb][r], c2, bias));
-            if (masked && (kj >= len || (CAUSAL && kj > qi))) p = 0.f;
-            float ds = p * (dp[kb][r] - dsum);
-            asm volatile("" : "+v"(ds));  // materialise here: keeps the VALU work in its MFMA slot
-            dp[kb][r] = ds;
         };
-        V8<T> dsb[4];
-        auto pack_chunk = [&](int c) {
-            const int kb = c >> 1, r0 = 8 * (c & 1);
-            dsb[c] = pack8<T>(dp[kb][r0], dp[kb][r0 + 1], dp[kb][r0 + 2], dp[kb][r0 + 3], dp[kb][r0 + 4],
-                              dp[kb][r0 + 5], dp[kb][r0 + 6], dp[kb][r0 + 7]);
-        };
-
-        uint4 fk[3], fv[3];
-        auto load1 = [&](int gi) {
-            const int kb = gi / NK, kk = gi % NK;
-            fk[gi % 3] = ld_s16(Ks + 32 * kb * D + roff[kk]);
-            fv[gi % 3] = ld_s16(Vs + 32 * kb * D + roff[kk]);
-        };
-        auto mmaS = [&](int gi) {
-            const int kb = gi / NK, kk = gi % NK;
-            s[kb] = Mfma<T>::mma(as_v8<T>(fk[gi % 3]), qf[kk], s[kb]);
-        };
-        auto mmaP = [&](int gi) {
-            const int kb = gi / NK, kk = gi % NK;
-            dp[kb] = Mfma<T>::mma(as_v8<T>(fv[gi % 3]), df[kk], dp[kb]);
-        };
-        uint4 fkt[3];
-        auto load2 = [&](int gi) {
-            const int c = gi / ND, db = gi % ND;
-            const uint2 lo = ld_s8_tr(Ks + 16 * c * D + toff[db][0]);
-            const uint2 hi = ld_s8_tr(Ks + 16 * c * D + toff[db][1]);
-            fkt[gi % 3] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        };
-        auto mma2 = [&](int gi) {
-            const int c = gi / ND, db = gi % ND;
-            dqacc[db] = Mfma<T>::mma(as_v8<T>(fkt[gi % 3]), dsb[c], dqacc[db]);
-        };
-        constexpr int EB = 16 / (2 * NK);  // block-0 elements per MFMA in phase B
-
-        // phase A
-        load1(0);
-        load1(1);
-#pragma unroll
-        for (int gi = 0; gi < NK; ++gi) {
-            load1(gi + 2);
-            __builtin_amdgcn_sched_barrier(0);
-            mmaS(gi);
-            mmaP(gi);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        // phase B
-#pragma unroll
-        for (int gi = NK; gi < 2 * NK; ++gi) {
-            const int e = 2 * (gi - NK) * EB;
-            if (gi + 2 < 2 * NK) load1(gi + 2);
-            __builtin_amdgcn_sched_barrier(0);
-            mmaS(gi);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int r = e; r < e + EB; ++r) elem(0, r);
-            __builtin_amdgcn_sched_barrier(0);
-            mmaP(gi);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int r = e + EB; r < e + 2 * EB; ++r) elem(0, r);
-            if (e + 2 * EB == 8) pack_chunk(0);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        pack_chunk(1);
-        // phases C and D: 4 ND MFMAs over chunks 0..3; block-1 rows 0..7 spread
-        // over chunks 0 and 1, rows 8..15 over chunk 2
-        load2(0);
-        load2(1);
-#pragma unroll
-        for (int gi = 0; gi < 4 * ND; ++gi) {
-            const int c = gi / ND;
-            if (gi + 2 < 4 * ND) load2(gi + 2);
-            __builtin_amdgcn_sched_barrier(0);
-            mma2(gi);
-            __builtin_amdgcn_sched_barrier(0);
-            if (c < 2) {
-                constexpr int E = 8 / (2 * ND);
-#pragma unroll
-                for (int r = gi * E; r < gi * E + E; ++r) elem(1, r);
-                if (gi == 2 * ND - 1) pack_chunk(2);
-            } else if (c == 2) {
-                constexpr int E = 8 / ND;
-                const int g = gi - 2 * ND;
-#pragma unroll
-                for (int r = 8 + g * E; r < 8 + g * E + E; ++r) elem(1, r);
-                if (gi == 3 * ND - 1) pack_chunk(3);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-      };
         if ((k0 + DQ_BK > len) || (CAUSAL && k0 + DQ_BK - 1 > qw))
             body(std::true_type{});
         else
@@ -313,8 +265,9 @@ hipError_t launch(const Args& a, unsigned stages, hipStream_t s) {
         if (e != hipSuccess) return e;
     }
     if (stages & 4u) {
-        dim3 grid(a.H, a.B, (a.N + DQ_BQ - 1) / DQ_BQ);
-        hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL, ALIBI>), grid, dim3(NT), 0, s, a);
+        constexpr int nw = dq_waves<D, CAUSAL>();
+        dim3 grid(a.H, a.B, (a.N + 32 * nw - 1) / (32 * nw));
+        hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL, ALIBI>), grid, dim3(64 * nw), 0, s, a);
         return hipGetLastError();
     }
     return hipSuccess;
