@@ -2,24 +2,22 @@
 // are described in fa_bwd.hip; "FlashAttention: Faster Attention Without
 // Dropping a Single Interaction", Method Deep Dive, Key design 3).
 //
-// One workgroup of 4 waves per (128-key tile, kv head, sequence); each wave
-// owns 32 keys and keeps their K and V rows in registers as MFMA operands and
-// their dK, dV accumulators in AGPRs. The workgroup walks every query head of
-// the kv group and every 64-query tile that can see the keys. Per 64-query
-// step, with query blocks qb = 0, 1 of 32 rows:
+// One workgroup of 8 waves (two per SIMD) per (256-key tile, kv head,
+// sequence); each wave owns 32 keys. K of the wave's keys is held in registers
+// as an MFMA operand; V of the workgroup's keys sits in LDS for the whole
+// kernel (it is read once per query block), which keeps a wave within the 256
+// registers per lane that two waves per SIMD allow next to the dK, dV
+// accumulators. The workgroup walks every query head of the kv group and every
+// 64-query tile that can see the keys; all 8 waves share each staged Q / dO
+// tile, so a direct load feeds twice the MFMA work it would with 4 waves. Per
+// 32-query block qb of a step:
 //
 //   S  = Q K^T, dP = dO V^T            (scores: one key column per lane)
 //   P  = exp2(S * scale * log2 e - L * log2 e), dS = P o (dP - D)
 //   dV^T += dO^T P,  dK^T += Q^T dS    (transposed operands via ds_read_b64_tr_b16)
 //
-// At one wave per SIMD nothing else hides the softmax, so the step is laid out
-// by hand as four phases whose VALU and MFMA work are independent and
-// interleaved:
-//   A: S/dP of block 0
-//   B: S/dP of block 1        + softmax of block 0
-//   C: dV/dK of block 0       + softmax of block 1
-//   D: dV/dK of block 1
-// LDS operand loads run two MFMA groups ahead through small register rings,
+// The other wave on the SIMD fills the MFMA pipe during this one's softmax.
+// LDS operand loads run one MFMA group ahead through two-slot register rings,
 // and scheduling barriers pin the order.
 #include <type_traits>
 
@@ -28,19 +26,26 @@
 namespace fa {
 namespace {
 
-constexpr int NT = 256;
-constexpr int KV_BK = 128;  // keys per workgroup (32 per wave)
-constexpr int KV_BQ = 64;   // queries per step (two blocks of 32)
+constexpr int NW = 8;           // waves per workgroup, two per SIMD
+constexpr int NT = 64 * NW;
+constexpr int KV_BK = 32 * NW;  // keys per workgroup (32 per wave)
+constexpr int KV_BQ = 64;       // queries per step (two blocks of 32)
 
 #define FA_SB() __builtin_amdgcn_sched_barrier(0)
 
 template <typename T, int D, bool CAUSAL, bool ALIBI>
 __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
-    // stage: Q tile, dO tile (swizzled [KV_BQ x D] each), then L*log2(e) and D (fp32, KV_BQ each)
+    // stage: Q tile, dO tile (swizzled [KV_BQ x D] each), with L*log2(e) and D
+    // (fp32, KV_BQ each) in a small array of their own: the two tile stages
+    // then span 64 KB, and every operand read reaches them from one set of
+    // per-lane offset registers through the 16-bit immediate offset.
     constexpr int TILE = KV_BQ * D;
-    constexpr int STAGE = 2 * TILE + 2 * KV_BQ * 2;
+    constexpr int STAGE = 2 * TILE;
     __shared__ __attribute__((aligned(16))) uint16_t stA[STAGE];
     __shared__ __attribute__((aligned(16))) uint16_t stB[STAGE];
+    __shared__ __attribute__((aligned(16))) float vecA[2 * KV_BQ];
+    __shared__ __attribute__((aligned(16))) float vecB[2 * KV_BQ];
+    __shared__ __attribute__((aligned(16))) uint16_t vt[KV_BK * D];  // V rows k0 .. k0 + KV_BK, swizzled
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int kg = lane >> 5;
@@ -55,31 +60,30 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
     const int kw = k0 + wave * 32;     // first key of this wave
     const int key = kw + (lane & 31);  // this lane's key (column of S)
 
-    // K^T and V^T fragments as B operands: lane holds key `key`, dims 16*kk + 8*kg + 0..7.
-    V8<T> kf[D / 16], vf[D / 16];
+    // K^T fragments as B operands: lane holds key `key`, dims 16*kk + 8*kg + 0..7.
+    V8<T> kf[D / 16];
     {
         const T* Kp = reinterpret_cast<const T*>(a.k) + (size_t)(row0 + key) * ldk + (size_t)g * D;
-        const T* Vp = reinterpret_cast<const T*>(a.v) + (size_t)(row0 + key) * ldk + (size_t)g * D;
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
-            uint4 uk = make_uint4(0, 0, 0, 0), uv = uk;
-            if (key < len) {
-                uk = ld_g16(Kp + 16 * kk + 8 * kg);
-                uv = ld_g16(Vp + 16 * kk + 8 * kg);
-            }
+            uint4 uk = make_uint4(0, 0, 0, 0);
+            if (key < len) uk = ld_g16(Kp + 16 * kk + 8 * kg);
             kf[kk] = as_v8<T>(uk);
-            vf[kk] = as_v8<T>(uv);
         }
     }
-
-    int roff[D / 16], toff[D / 32][2];
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) roff[kk] = swz_row_off<D>(lane, kk);
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-        toff[db][0] = swz_tr_off<D>(lane, db, 0);
-        toff[db][1] = swz_tr_off<D>(lane, db, 1);
+    // V of the workgroup's keys into LDS (rows past the end read as zero), in
+    // two halves of KV_BK / 2 rows; the swizzle repeats every 16 rows, so the
+    // halves form one swizzled [KV_BK x D] tile. The first wait of the loop
+    // below covers these loads.
+    {
+        DmaTile<D, KV_BK / 2, NW> vdma;
+        vdma.init(wave, lane, ldk);
+        const uint16_t* Vg = reinterpret_cast<const uint16_t*>(a.v) + (size_t)row0 * ldk + (size_t)g * D;
+        vdma.issue(vt, Vg, k0, len, wave);
+        vdma.issue(vt + (KV_BK / 2) * D, Vg, k0 + KV_BK / 2, len, wave);
     }
+
+    const int vrow = wave * 32 * D;  // element offset of this wave's 32 rows of V
 
     f32x16 dkacc[D / 32], dvacc[D / 32];
 #pragma unroll
@@ -104,7 +108,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
         q0 = (qt0 + st - hh * per_head) * KV_BQ;
     };
 
-    DmaTile<D, KV_BQ, NT / 64> dma;
+    DmaTile<D, KV_BQ, NW> dma;
     dma.init(wave, lane, ldq);
     auto issue = [&](uint16_t* S, int st) {
         int h, q0;
@@ -114,173 +118,111 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
         // the pre-pass filled positions [len, N64) with +inf / 0, so the 64
         // values from q0 are in bounds and padding rows get P = 0
         const size_t vbase = ((size_t)b * a.H + h) * a.N64 + q0;
-        if (wave == 0) dma_vec64(reinterpret_cast<float*>(S + 2 * TILE), a.lse2 + vbase, lane);
-        if (wave == 1) dma_vec64(reinterpret_cast<float*>(S + 2 * TILE) + KV_BQ, a.dsum + vbase, lane);
+        float* vec = S == stA ? vecA : vecB;
+        if (wave == 0) dma_vec64(vec, a.lse2 + vbase, lane);
+        if (wave == 1) dma_vec64(vec + KV_BQ, a.dsum + vbase, lane);
     };
 
     auto step = [&](const uint16_t* S, int h, int q0, auto masked) {
         constexpr bool MASKED = decltype(masked)::value;
         const uint16_t* Qs = S;
         const uint16_t* Ds = S + TILE;
-        const float* lse2 = reinterpret_cast<const float*>(S + 2 * TILE);
+        const float* lse2 = S == stA ? vecA : vecB;
         const float* dsv = lse2 + KV_BQ;
         const float slope2 = ALIBI ? ld_uniform(a.slopes + h) * kLog2e : 0.f;
+        constexpr int NK = D / 16, ND = D / 32;
+        // Lane parts of the LDS operand offsets, computed in every step from an
+        // opaque copy of the lane index: kept live across the loop instead,
+        // they would cost 16 registers per lane (more, once the compiler adds
+        // the stage bases to them), which two waves per SIMD cannot afford;
+        // formed here, the stage and tile bases fold into the instructions'
+        // immediate offsets.
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        int ro[NK], to[ND][2];
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) ro[kk] = swz_row_off<D>(ln, kk);
+#pragma unroll
+        for (int db = 0; db < ND; ++db) {
+            to[db][0] = swz_tr_off<D>(ln, db, 0);
+            to[db][1] = swz_tr_off<D>(ln, db, 1);
+        }
+        const uint16_t* Vw = vt + vrow;  // this wave's 32 rows of V
 
-        f32x16 sc[2], dpc[2];  // S and dP of blocks 0, 1
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-            sc[qb] = f32x16{};
-            dpc[qb] = f32x16{};
-        }
-        float4 l4[4], d4[4];  // L*log2(e) and D of the block being softmaxed, per row group i
-        float pv[16], dsr[16];
-        V8<T> pb[4], db8[4];  // packed P and dS per 16-query chunk c
-
-        // L*log2(e) and D of rows 8i + 4kg + 0..3 of block qb (one row group)
-        auto load_vec = [&](int qb, int i) {
-            l4[i] = *reinterpret_cast<const float4*>(lse2 + 32 * qb + 8 * i + 4 * kg);
-            d4[i] = *reinterpret_cast<const float4*>(dsv + 32 * qb + 8 * i + 4 * kg);
-        };
-        // softmax backward of accumulator row r of block qb: P and dS
-        auto elem = [&](int qb, int r) {
-            const int i = r >> 2, j = r & 3;
-            const float lv = j == 0 ? l4[i].x : j == 1 ? l4[i].y : j == 2 ? l4[i].z : l4[i].w;
-            const float dv = j == 0 ? d4[i].x : j == 1 ? d4[i].y : j == 2 ? d4[i].z : d4[i].w;
-            const int qi = q0 + 32 * qb + 8 * i + 4 * kg + j;
-            float bias = -lv;
-            if (ALIBI) {
-                const float dist = (float)(qi - key);
-                bias -= slope2 * (CAUSAL ? dist : fabsf(dist));
+            // ---- S = Q K^T and dP = dO V^T: operand groups kk = 0 .. NK - 1
+            f32x16 sc = f32x16{}, dpc = f32x16{};
+            uint4 fq[2], fd[2], fv[2];  // one group ahead: three operands per group
+            auto load1 = [&](int kk) {
+                fq[kk % 2] = ld_s16(Qs + 32 * qb * D + ro[kk]);
+                fd[kk % 2] = ld_s16(Ds + 32 * qb * D + ro[kk]);
+                fv[kk % 2] = ld_s16(Vw + ro[kk]);
+            };
+            load1(0);
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk) {
+                if (kk + 1 < NK) load1(kk + 1);
+                FA_SB();
+                sc = Mfma<T>::mma(as_v8<T>(fq[kk % 2]), kf[kk], sc);
+                dpc = Mfma<T>::mma(as_v8<T>(fd[kk % 2]), as_v8<T>(fv[kk % 2]), dpc);
+                FA_SB();
             }
-            float p = exp2_fast(fmaf(sc[qb][r], c2, bias));
-            if (MASKED && key > qi) p = 0.f;
-            float ds = p * (dpc[qb][r] - dv);
-            asm volatile("" : "+v"(p), "+v"(ds));  // materialise here: keeps the VALU work in its MFMA slot
-            pv[r] = p;
-            dsr[r] = ds;
-        };
-        // P and dS of rows 8 h2 .. 8 h2 + 7 of block qb as bf16/f16 B operands
-        auto pack_half = [&](int qb, int h2) {
-            const int r0 = 8 * h2;
-            pb[2 * qb + h2] = pack8<T>(pv[r0], pv[r0 + 1], pv[r0 + 2], pv[r0 + 3], pv[r0 + 4], pv[r0 + 5], pv[r0 + 6],
-                                       pv[r0 + 7]);
-            db8[2 * qb + h2] = pack8<T>(dsr[r0], dsr[r0 + 1], dsr[r0 + 2], dsr[r0 + 3], dsr[r0 + 4], dsr[r0 + 5],
-                                        dsr[r0 + 6], dsr[r0 + 7]);
-        };
-        // elements [r0, r0 + n) of block qb, each followed by what it frees or completes:
-        // the row group's vectors for block `nxt` (if >= 0) and the packed half
-        auto elems = [&](int qb, int r0, int n, int nxt) {
+
+            // ---- softmax backward, row group i = accumulator rows 4i .. 4i + 3
+            float pv[16], dsr[16];
 #pragma unroll
-            for (int r = r0; r < r0 + n; ++r) {
-                elem(qb, r);
-                if ((r & 3) == 3 && nxt >= 0) load_vec(nxt, r >> 2);
-                if ((r & 7) == 7) pack_half(qb, r >> 3);
+            for (int i = 0; i < 4; ++i) {
+                const float4 l4 = *reinterpret_cast<const float4*>(lse2 + 32 * qb + 8 * i + 4 * kg);
+                const float4 d4 = *reinterpret_cast<const float4*>(dsv + 32 * qb + 8 * i + 4 * kg);
+                const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+                const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 4 * i + j;
+                    const int qi = q0 + 32 * qb + 8 * i + 4 * kg + j;
+                    float bias = -lv[j];
+                    if (ALIBI) {
+                        const float dist = (float)(qi - key);
+                        bias -= slope2 * (CAUSAL ? dist : fabsf(dist));
+                    }
+                    float p = exp2_fast(fmaf(sc[r], c2, bias));
+                    if (MASKED && key > qi) p = 0.f;
+                    pv[r] = p;
+                    dsr[r] = p * (dpc[r] - dv[j]);
+                }
             }
-        };
+            V8<T> pb[2], db8[2];  // P and dS per 16-query chunk, as B operands
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const int r0 = 8 * h2;
+                pb[h2] = pack8<T>(pv[r0], pv[r0 + 1], pv[r0 + 2], pv[r0 + 3], pv[r0 + 4], pv[r0 + 5], pv[r0 + 6],
+                                  pv[r0 + 7]);
+                db8[h2] = pack8<T>(dsr[r0], dsr[r0 + 1], dsr[r0 + 2], dsr[r0 + 3], dsr[r0 + 4], dsr[r0 + 5],
+                                   dsr[r0 + 6], dsr[r0 + 7]);
+            }
 
-        // ---- S/dP operand ring: group g1 in [0, 2 * D/16): block g1 / (D/16), kk = g1 % (D/16)
-        constexpr int NK = D / 16;
-        uint4 fq[3], fd[3];
-        auto load1 = [&](int g1) {
-            const int qb = g1 / NK, kk = g1 % NK;
-            fq[g1 % 3] = ld_s16(Qs + 32 * qb * D + roff[kk]);
-            fd[g1 % 3] = ld_s16(Ds + 32 * qb * D + roff[kk]);
-        };
-        auto mma1s = [&](int g1) {
-            const int qb = g1 / NK, kk = g1 % NK;
-            sc[qb] = Mfma<T>::mma(as_v8<T>(fq[g1 % 3]), kf[kk], sc[qb]);
-        };
-        auto mma1d = [&](int g1) {
-            const int qb = g1 / NK, kk = g1 % NK;
-            dpc[qb] = Mfma<T>::mma(as_v8<T>(fd[g1 % 3]), vf[kk], dpc[qb]);
-        };
-        auto mma1 = [&](int g1) {
-            mma1s(g1);
-            mma1d(g1);
-        };
-        // ---- dV/dK operand ring: group g2 in [0, 4 * D/32): chunk c = g2 / (D/32), db = g2 % (D/32)
-        constexpr int ND = D / 32;
-        uint4 fo[3], fqt[3];
-        auto load2 = [&](int g2) {
-            const int c = g2 / ND, db = g2 % ND;
-            const uint2 olo = ld_s8_tr(Ds + 16 * c * D + toff[db][0]);
-            const uint2 ohi = ld_s8_tr(Ds + 16 * c * D + toff[db][1]);
-            const uint2 qlo = ld_s8_tr(Qs + 16 * c * D + toff[db][0]);
-            const uint2 qhi = ld_s8_tr(Qs + 16 * c * D + toff[db][1]);
-            fo[g2 % 3] = make_uint4(olo.x, olo.y, ohi.x, ohi.y);
-            fqt[g2 % 3] = make_uint4(qlo.x, qlo.y, qhi.x, qhi.y);
-        };
-        auto mma2v = [&](int g2) {
-            const int c = g2 / ND, db = g2 % ND;
-            dvacc[db] = Mfma<T>::mma(as_v8<T>(fo[g2 % 3]), pb[c], dvacc[db]);
-        };
-        auto mma2k = [&](int g2) {
-            const int c = g2 / ND, db = g2 % ND;
-            dkacc[db] = Mfma<T>::mma(as_v8<T>(fqt[g2 % 3]), db8[c], dkacc[db]);
-        };
-        auto mma2 = [&](int g2) {
-            mma2v(g2);
-            mma2k(g2);
-        };
-
-        // One softmax element after every MFMA of phases B and C (two for
-        // D = 64): with one wave per SIMD issue is in order, and a VALU run
-        // only overlaps the MFMA issued just before it.
-        constexpr int EB = 16 / (2 * NK);  // elements per MFMA in phase B
-        constexpr int EC = 16 / (4 * ND);  // and in phase C
-
-        // phase A: S/dP of block 0
+            // ---- dV^T += dO^T P, dK^T += Q^T dS: groups (chunk c of the block, db)
+            uint4 fo[2], fqt[2];
+            auto load2 = [&](int gi) {
+                const int c = 2 * qb + gi / ND, db = gi % ND;
+                const uint2 olo = ld_s8_tr(Ds + 16 * c * D + to[db][0]);
+                const uint2 ohi = ld_s8_tr(Ds + 16 * c * D + to[db][1]);
+                const uint2 qlo = ld_s8_tr(Qs + 16 * c * D + to[db][0]);
+                const uint2 qhi = ld_s8_tr(Qs + 16 * c * D + to[db][1]);
+                fo[gi % 2] = make_uint4(olo.x, olo.y, ohi.x, ohi.y);
+                fqt[gi % 2] = make_uint4(qlo.x, qlo.y, qhi.x, qhi.y);
+            };
+            load2(0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) load_vec(0, i);
-        load1(0);
-        load1(1);
-#pragma unroll
-        for (int g1 = 0; g1 < NK; ++g1) {
-            load1(g1 + 2);
-            FA_SB();
-            mma1(g1);
-            FA_SB();
-        }
-        // phase B: S/dP of block 1, softmax of block 0 (its row-group vectors
-        // are replaced by block 1's as they are used up)
-#pragma unroll
-        for (int g1 = NK; g1 < 2 * NK; ++g1) {
-            const int e = 2 * (g1 - NK) * EB;
-            if (g1 + 2 < 2 * NK) load1(g1 + 2);
-            FA_SB();
-            mma1s(g1);
-            FA_SB();
-            elems(0, e, EB, 1);
-            FA_SB();
-            mma1d(g1);
-            FA_SB();
-            elems(0, e + EB, EB, 1);
-            FA_SB();
-        }
-        // phase C: dV/dK of block 0 (chunks 0, 1), softmax of block 1
-        load2(0);
-        load2(1);
-#pragma unroll
-        for (int g2 = 0; g2 < 2 * ND; ++g2) {
-            const int e = 2 * g2 * EC;
-            load2(g2 + 2);
-            FA_SB();
-            mma2v(g2);
-            FA_SB();
-            elems(1, e, EC, -1);
-            FA_SB();
-            mma2k(g2);
-            FA_SB();
-            elems(1, e + EC, EC, -1);
-            FA_SB();
-        }
-        // phase D: dV/dK of block 1 (chunks 2, 3)
-#pragma unroll
-        for (int g2 = 2 * ND; g2 < 4 * ND; ++g2) {
-            if (g2 + 2 < 4 * ND) load2(g2 + 2);
-            FA_SB();
-            mma2(g2);
-            FA_SB();
+            for (int gi = 0; gi < 2 * ND; ++gi) {
+                if (gi + 1 < 2 * ND) load2(gi + 1);
+                FA_SB();
+                const int db = gi % ND;
+                dvacc[db] = Mfma<T>::mma(as_v8<T>(fo[gi % 2]), pb[gi / ND], dvacc[db]);
+                dkacc[db] = Mfma<T>::mma(as_v8<T>(fqt[gi % 2]), db8[gi / ND], dkacc[db]);
+                FA_SB();
+            }
         }
     };
 
