@@ -84,6 +84,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
     }
 
     const int vrow = wave * 32 * D;  // element offset of this wave's 32 rows of V
+    const int rbase = swz_row_off<D>(lane, 0), tbase = swz_tr_off<D>(lane, 0, 0);
 
     f32x16 dkacc[D / 32], dvacc[D / 32];
 #pragma unroll
@@ -131,33 +132,25 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
         const float* dsv = lse2 + KV_BQ;
         const float slope2 = ALIBI ? ld_uniform(a.slopes + h) * kLog2e : 0.f;
         constexpr int NK = D / 16, ND = D / 32;
-        // Lane parts of the LDS operand offsets, computed in every step from an
-        // opaque copy of the lane index: kept live across the loop instead,
-        // they would cost 16 registers per lane (more, once the compiler adds
-        // the stage bases to them), which two waves per SIMD cannot afford;
-        // formed here, the stage and tile bases fold into the instructions'
-        // immediate offsets.
-        int ln = lane;
-        asm volatile("" : "+v"(ln));
-        int ro[NK], to[ND][2];
-#pragma unroll
-        for (int kk = 0; kk < NK; ++kk) ro[kk] = swz_row_off<D>(ln, kk);
-#pragma unroll
-        for (int db = 0; db < ND; ++db) {
-            to[db][0] = swz_tr_off<D>(ln, db, 0);
-            to[db][1] = swz_tr_off<D>(ln, db, 1);
-        }
+        // Lane parts of the LDS operand offsets in XOR form: a base per lane,
+        // passed through an empty asm in every block so that the compiler cannot
+        // hoist the per-group offsets out of the loop as 16 registers per lane,
+        // which two waves per SIMD cannot afford. Formed here, each is one
+        // v_xor, and the stage and tile bases fold into the immediate offsets.
         const uint16_t* Vw = vt + vrow;  // this wave's 32 rows of V
 
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
+            int rb = rbase, tb = tbase;
+            asm volatile("" : "+v"(rb), "+v"(tb));
             // ---- S = Q K^T and dP = dO V^T: operand groups kk = 0 .. NK - 1
             f32x16 sc = f32x16{}, dpc = f32x16{};
             uint4 fq[2], fd[2], fv[2];  // one group ahead: three operands per group
             auto load1 = [&](int kk) {
-                fq[kk % 2] = ld_s16(Qs + 32 * qb * D + ro[kk]);
-                fd[kk % 2] = ld_s16(Ds + 32 * qb * D + ro[kk]);
-                fv[kk % 2] = ld_s16(Vw + ro[kk]);
+                const int o = swz_row_x<D>(rb, kk);
+                fq[kk % 2] = ld_s16(Qs + 32 * qb * D + o);
+                fd[kk % 2] = ld_s16(Ds + 32 * qb * D + o);
+                fv[kk % 2] = ld_s16(Vw + o);
             };
             load1(0);
 #pragma unroll
@@ -206,10 +199,11 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
             uint4 fo[2], fqt[2];
             auto load2 = [&](int gi) {
                 const int c = 2 * qb + gi / ND, db = gi % ND;
-                const uint2 olo = ld_s8_tr(Ds + 16 * c * D + to[db][0]);
-                const uint2 ohi = ld_s8_tr(Ds + 16 * c * D + to[db][1]);
-                const uint2 qlo = ld_s8_tr(Qs + 16 * c * D + to[db][0]);
-                const uint2 qhi = ld_s8_tr(Qs + 16 * c * D + to[db][1]);
+                const int o0 = swz_tr_x<D>(tb, db, 0), o1 = swz_tr_x<D>(tb, db, 1);
+                const uint2 olo = ld_s8_tr(Ds + 16 * c * D + o0);
+                const uint2 ohi = ld_s8_tr(Ds + 16 * c * D + o1);
+                const uint2 qlo = ld_s8_tr(Qs + 16 * c * D + o0);
+                const uint2 qhi = ld_s8_tr(Qs + 16 * c * D + o1);
                 fo[gi % 2] = make_uint4(olo.x, olo.y, ohi.x, ohi.y);
                 fqt[gi % 2] = make_uint4(qlo.x, qlo.y, qhi.x, qhi.y);
             };

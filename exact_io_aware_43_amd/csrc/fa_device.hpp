@@ -135,7 +135,7 @@ __device__ __forceinline__ float ld_uniform(const float* p) {
 // 8-byte reads of 4 rows x 64 bytes per half-wave (transposed operands), and
 // 16-byte writes of whole rows by consecutive lanes. `col` is a multiple of 4.
 template <int D>
-__device__ __forceinline__ int swz(int row, int col) {
+__host__ __device__ constexpr int swz(int row, int col) {
     const int f = ((row & 3) * (D / 32)) ^ ((row >> 2) & 3);
     return row * D + (((col >> 3) ^ f) << 3) + (col & 7);
 }
@@ -157,7 +157,7 @@ __device__ __forceinline__ uint4 ld_swz_rows_tr(const uint16_t* tile, int row0, 
 // part is the constant 32 * blk * D because the swizzle depends on row % 16
 // only; this returns the lane part, to be kept in a register for each kk.
 template <int D>
-__device__ __forceinline__ int swz_row_off(int lane, int kk) {
+__host__ __device__ constexpr int swz_row_off(int lane, int kk) {
     return swz<D>(lane & 31, 16 * kk + 8 * (lane >> 5));
 }
 
@@ -165,10 +165,36 @@ __device__ __forceinline__ int swz_row_off(int lane, int kk) {
 // of the offset of the low (half = 0) or high (half = 1) 8-byte read for
 // columns 32 * db + ...; rows 16 * c + ... add the constant 16 * c * D.
 template <int D>
-__device__ __forceinline__ int swz_tr_off(int lane, int db, int half) {
+__host__ __device__ constexpr int swz_tr_off(int lane, int db, int half) {
     const int r = lane & 15, grp = lane >> 4;
     return swz<D>(8 * half + 4 * (grp >> 1) + (r >> 2), 32 * db + 16 * (grp & 1) + 4 * (r & 3));
 }
+
+// XOR forms of the two lane offsets. A row starts at a multiple of D elements
+// and the swizzled chunk bits sit below D, so the kk (or db, half) part of an
+// offset enters as an XOR with a constant of the lane's base offset (kk = 0,
+// db = half = 0), plus 8 D per half. One v_xor per read then replaces a
+// register per operand group.
+template <int D>
+__host__ __device__ constexpr int swz_row_x(int rbase, int kk) {
+    return rbase ^ (16 * kk);
+}
+template <int D>
+__host__ __device__ constexpr int swz_tr_x(int tbase, int db, int half) {
+    return (tbase ^ (32 * db + 16 * half)) + 8 * half * D;
+}
+template <int D>
+constexpr bool swz_xor_forms_hold() {
+    for (int lane = 0; lane < 64; ++lane) {
+        for (int kk = 0; kk < D / 16; ++kk)
+            if (swz_row_x<D>(swz_row_off<D>(lane, 0), kk) != swz_row_off<D>(lane, kk)) return false;
+        for (int db = 0; db < D / 32; ++db)
+            for (int half = 0; half < 2; ++half)
+                if (swz_tr_x<D>(swz_tr_off<D>(lane, 0, 0), db, half) != swz_tr_off<D>(lane, db, half)) return false;
+    }
+    return true;
+}
+static_assert(swz_xor_forms_hold<64>() && swz_xor_forms_hold<128>(), "XOR forms of the swizzled offsets");
 
 // Direct global -> LDS staging (buffer_load_dwordx4 ... lds) of a [ROWS x D]
 // 16-bit tile into a swizzled LDS tile. Each instruction of a wave fills 1 KB
