@@ -90,6 +90,18 @@ __device__ __forceinline__ uint32_t half_of(const uint4& u, int e) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Maximum / sum of x over lanes l and l ^ 32 with v_permlane32_swap (a
+// register exchange between the two halves of the wave, no LDS round trip).
+// Both lanes get the same value, with the same rounding.
+__device__ __forceinline__ float max_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Transposing LDS read (ds_read_b64_tr_b16). Within each group of 16 lanes,
 // lane 4a + c receives element c of the 8-byte chunks addressed by lanes
 // a, a + 4, a + 8 and a + 12 of the group, in that order. If lane r of a group

@@ -9,7 +9,7 @@
 //
 // Work decomposition. One workgroup of 8 waves owns BR = 256 query rows of one
 // (sequence, query head); each wave owns 32 of them. K and V of the head's kv
-// head stream through LDS in tiles of BC = 64 keys, double buffered: the next
+// head stream through LDS in tiles of BC = 128 keys, double buffered: the next
 // tile's loads are in flight while the current tile is multiplied. The 8 waves
 // share every tile (the direct loads that stage it cost issue time per wave,
 // so sharing halves that cost against two 4-wave groups), and two waves run
@@ -19,7 +19,7 @@
 // Register orientation. Each wave computes the transposed score tile
 // S^T = K Q^T (keys x queries) so that in the MFMA accumulator every lane holds
 // scores of ONE query (its column) for 16 keys; the row max and row sum are
-// in-lane reductions plus one exchange with lane l ^ 32. The output is
+// in-lane reductions plus one register exchange with lane l ^ 32. The output is
 // accumulated transposed as well, O^T += V^T P^T, which takes P^T straight
 // from the score accumulator as the B operand and keeps the per-query rescale
 // factor in-lane. K and V are staged with direct global-to-LDS loads into
@@ -181,7 +181,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_mfma_kernel(Args a) {
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
             mt = mx * c2;
         }
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        mt = max_xor32(mt);
 
         // lazy rescale: raise the reference only when the tile max exceeds it by > TAU
         const bool raise = mt > m_ref + TAU;
@@ -239,7 +239,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_mfma_kernel(Args a) {
     two_stage_loop(stA, stB, nkt, issue, compute);
 
     // ---- epilogue: O = O_acc / l, lse = (m + log2 l) * ln 2
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float l_tot = sum_xor32(l_run);
     if (qi < len) {
         const float inv = 1.f / l_tot;
         T* O = reinterpret_cast<T*>(a.out) + (size_t)row0 * ldq + (size_t)h * D + (size_t)qi * ldq;
