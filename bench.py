@@ -10,7 +10,10 @@ for causal, and 2.5x that for backward.
 
 Besides the step rate the line carries:
   * ``kernels``: each kernel timed alone with HIP events on the launch stream
-    (average over --kernel-reps launches) against its algorithmic work;
+    (average over --kernel-reps launches) against its algorithmic work, and
+    the HBM rate its algorithmic bytes imply (every input read once, every
+    output written once), the figure that matters for short sequences
+    (``--workload gpt2m``);
   * ``roofline``: the kernel that takes longest per step, against the MI355X
     dense bf16 MFMA peak (or HBM bandwidth for the memory-bound pre-pass), with
     HBM traffic from the committed rocprofv3 counter summary when that summary
@@ -180,7 +183,16 @@ def main():
 
     row_bytes = 2 if w.dtype in ("bf16", "fp16") else 4
     T = sum(lens)
-    dsum_bytes = 2 * T * H * d * row_bytes + 4 * T * H
+    # algorithmic HBM bytes per launch: every input read once, every output
+    # written once (q-side rows T*H*d, kv-side rows T*Hkv*d, fp32 row vectors T*H)
+    qb, kvb, vec = T * H * d * row_bytes, T * Hkv * d * row_bytes, 4 * T * H
+    dsum_bytes = 2 * qb + 3 * vec
+    alg_bytes = {
+        "fwd": 2 * qb + 2 * kvb + vec,                # Q, K, V in; O, lse out
+        "bwd_dsum": dsum_bytes,                       # O, dO, lse in; D and L*log2(e) out
+        "bwd_dkdv": 2 * qb + 4 * kvb + 2 * vec,       # Q, dO, K, V, D, L in; dK, dV out
+        "bwd_dq": 3 * qb + 2 * kvb + 2 * vec,         # Q, dO, K, V, D, L in; dQ out
+    }
     kernels = {
         "fwd": dict(ms=time_launches(fwd), work=f_fwd, bound="mfma"),
         "bwd_dsum": dict(ms=time_launches(lambda: bwd(fa.FA_BWD_PREP)), work=dsum_bytes, bound="hbm"),
@@ -250,7 +262,10 @@ def main():
         "bwd_tflops": round(f_bwd / (sum(kernels[n]["ms"] for n in ("bwd_dsum", "bwd_dkdv", "bwd_dq")) * 1e-3)
                             / 1e12, 2),
         "kernels": {n: {"ms": round(kr["ms"], 4), "achieved": round(kr["achieved"], 2), "unit": kr["unit"],
-                        "frac": round(kr["frac"], 4)} for n, kr in kernels.items()},
+                        "frac": round(kr["frac"], 4),
+                        "hbm_alg_bytes": int(alg_bytes[n]),
+                        "hbm_alg_gbs": round(alg_bytes[n] / (kr["ms"] * 1e-3) / 1e9, 1)}
+                    for n, kr in kernels.items()},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "memory": memory,
