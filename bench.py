@@ -21,7 +21,12 @@ Besides the step rate the line carries:
   * ``cpu_baseline``: the fp64 CPU oracle timed on this host on the first
     heads of the same workload (forward + backward, about ten seconds);
   * ``memory``: device bytes the step allocates versus a materialised-score
-    baseline that stores S and P.
+    baseline that stores S and P;
+  * ``env``: ROCm, compiler and torch versions, and the power and clock
+    readings of amd-smi (or rocm-smi) taken while steps keep the GPU busy.
+Per kernel, ``ms`` is the average over --kernel-reps back-to-back launches
+(the figure the roofline uses, comparable with a rocprofv3 trace average);
+``median_ms`` and ``min_ms`` come from as many launches timed one by one.
 """
 
 from __future__ import annotations
@@ -31,6 +36,7 @@ import hashlib
 import json
 import math
 import os
+import subprocess
 import sys
 import time
 
@@ -71,7 +77,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="long_causal")
-    ap.add_argument("--kernel-reps", type=int, default=10)
+    ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -170,7 +176,11 @@ def main():
     value = (f_fwd + f_bwd) / (ms * 1e-3) / 1e12
 
     # ---- each kernel alone, HIP events on the launch stream
-    def time_launches(fn):
+    launch_stats = {}
+
+    def time_launches(fn, name):
+        """Average over back-to-back launches (one event pair around all of them),
+        then median and minimum of the same number of launches timed one by one."""
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         fn()
         torch.cuda.synchronize()
@@ -179,6 +189,15 @@ def main():
             fn()
         e1.record(stream)
         torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.kernel_reps)]
+        for a_, b_ in evs:
+            a_.record(stream)
+            fn()
+            b_.record(stream)
+        torch.cuda.synchronize()
+        one = sorted(a_.elapsed_time(b_) for a_, b_ in evs)
+        launch_stats[name] = (one[len(one) // 2], one[0])
         return e0.elapsed_time(e1) / args.kernel_reps
 
     row_bytes = 2 if w.dtype in ("bf16", "fp16") else 4
@@ -194,10 +213,10 @@ def main():
         "bwd_dq": 3 * qb + 2 * kvb + 2 * vec,         # Q, dO, K, V, D, L in; dQ out
     }
     kernels = {
-        "fwd": dict(ms=time_launches(fwd), work=f_fwd, bound="mfma"),
-        "bwd_dsum": dict(ms=time_launches(lambda: bwd(fa.FA_BWD_PREP)), work=dsum_bytes, bound="hbm"),
-        "bwd_dkdv": dict(ms=time_launches(lambda: bwd(fa.FA_BWD_DKDV)), work=2.0 * f_fwd, bound="mfma"),
-        "bwd_dq": dict(ms=time_launches(lambda: bwd(fa.FA_BWD_DQ)), work=0.5 * f_fwd, bound="mfma"),
+        "fwd": dict(ms=time_launches(fwd, "fwd"), work=f_fwd, bound="mfma"),
+        "bwd_dsum": dict(ms=time_launches(lambda: bwd(fa.FA_BWD_PREP), "bwd_dsum"), work=dsum_bytes, bound="hbm"),
+        "bwd_dkdv": dict(ms=time_launches(lambda: bwd(fa.FA_BWD_DKDV), "bwd_dkdv"), work=2.0 * f_fwd, bound="mfma"),
+        "bwd_dq": dict(ms=time_launches(lambda: bwd(fa.FA_BWD_DQ), "bwd_dq"), work=0.5 * f_fwd, bound="mfma"),
     }
     for name, kr in kernels.items():
         if kr["bound"] == "mfma":
@@ -238,6 +257,22 @@ def main():
         "ratio": round(2 * nn * row_bytes / max(lib_bytes, 1), 1),
     }
 
+    # clock and power under load: the query runs on another thread while this
+    # one keeps the launch queue full for six seconds of wall time
+    import threading
+
+    tel = {}
+    th = threading.Thread(target=lambda: tel.update(r=gpu_telemetry()))
+    th.start()
+    t_end = time.perf_counter() + 6.0
+    while time.perf_counter() < t_end or th.is_alive():
+        step()
+        if time.perf_counter() > t_end + 30.0:
+            break
+    th.join()
+    torch.cuda.synchronize()
+    telemetry = tel.get("r")
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, inp, lens)
@@ -263,12 +298,15 @@ def main():
                             / 1e12, 2),
         "kernels": {n: {"ms": round(kr["ms"], 4), "achieved": round(kr["achieved"], 2), "unit": kr["unit"],
                         "frac": round(kr["frac"], 4),
+                        "median_ms": round(launch_stats[n][0], 4), "min_ms": round(launch_stats[n][1], 4),
                         "hbm_alg_bytes": int(alg_bytes[n]),
                         "hbm_alg_gbs": round(alg_bytes[n] / (kr["ms"] * 1e-3) / 1e9, 1)}
                     for n, kr in kernels.items()},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "memory": memory,
+        "env": {"rocm": _read_first("/opt/rocm/.info/version"), "hipcc": _hipcc_version(), "torch": torch.__version__,
+                "gpu": torch.cuda.get_device_properties(0).gcnArchName, "telemetry_under_load": telemetry},
     }
     out["fwd_frac_of_peak"] = round(out["fwd_tflops"] / PEAK_BF16_TFLOPS, 4)
     out["bwd_frac_of_peak"] = round(out["bwd_tflops"] / PEAK_BF16_TFLOPS, 4)
@@ -280,6 +318,57 @@ def main():
         torch.neg(x, out=y)
         torch.cuda.synchronize()
         print(f"[bench] copy calibration: neg of {COPY_BYTES} bytes", file=sys.stderr, flush=True)
+
+
+def _read_first(path):
+    try:
+        with open(path) as f:
+            return f.readline().strip()
+    except OSError:
+        return None
+
+
+def _hipcc_version():
+    try:
+        r = subprocess.run(["/opt/rocm/bin/hipcc", "--version"], capture_output=True, text=True, timeout=30)
+    except (OSError, subprocess.SubprocessError):
+        return None
+    return next((ln.strip() for ln in r.stdout.splitlines() if "HIP version" in ln), None)
+
+
+def gpu_telemetry():
+    """Power and clock readings of GPU 0 from amd-smi (else rocm-smi), as flat key/value pairs; read-only queries."""
+    cmds = (["/opt/rocm/bin/amd-smi", "metric", "-g", "0", "-p", "-c", "--json"],
+            ["/opt/rocm/bin/rocm-smi", "-d", "0", "--showpower", "--showclocks", "--json"])
+    for cmd in cmds:
+        try:
+            r = subprocess.run(cmd, capture_output=True, text=True, timeout=30)
+            data = json.loads(r.stdout) if r.returncode == 0 and r.stdout.strip() else None
+        except (OSError, subprocess.SubprocessError, ValueError):
+            data = None
+        if data is None:
+            continue
+        flat = {}
+
+        def walk(x, key):
+            if isinstance(x, dict):
+                for k2, v2 in x.items():
+                    walk(v2, f"{key}.{k2}" if key else str(k2))
+            elif isinstance(x, list):
+                for i, v2 in enumerate(x):
+                    walk(v2, f"{key}[{i}]")
+            elif any(t in key.lower() for t in ("power", "clk", "clock")) and len(flat) < 200:
+                flat[key] = x
+
+        walk(data, "")
+        # amd-smi: socket power and the current gfx clock of each XCD; other tools: the raw entries
+        power = [v for k, v in flat.items() if k.endswith("socket_power.value")]
+        clks = [v for k, v in flat.items() if ".clock.gfx_" in k and k.endswith(".clk.value")]
+        if power or clks:
+            return {"tool": os.path.basename(cmd[0]), "socket_power_w": power[0] if power else None,
+                    "gfx_clk_mhz": clks}
+        return {"tool": os.path.basename(cmd[0]), "readings": flat}
+    return {"tool": None, "readings": "unavailable"}
 
 
 def _counter_rows(d):
