@@ -95,7 +95,7 @@ __global__ __launch_bounds__((64 * dq_waves<D, CAUSAL>()), 1) void bwd_dq_kernel
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int col = lane & 31, kg = lane >> 5;
-    const int h = blockIdx.x, b = blockIdx.y;
+    const int h = query_head(a, blockIdx.x), b = blockIdx.y;  // kv-head-major columns
     const int qt = CAUSAL ? (int)(gridDim.z - 1 - blockIdx.z) : (int)blockIdx.z;
     int row0, len;
     seq_bounds(a, b, row0, len);

@@ -305,6 +305,14 @@ __device__ __forceinline__ void two_stage_loop(uint16_t* A, uint16_t* B, int n, 
     }
 }
 
+// Query head of grid column x. Workgroups are dealt to the eight XCDs (each
+// with its own L2) in turn, so with H a multiple of 8 column x runs on XCD
+// x % 8. Numbering the columns kv-head-major (x = g + Hkv * i for query head
+// G g + i) puts the G query heads that read one kv head's K and V on the same
+// XCD whenever Hkv divides 8 or is a multiple of it; with G = 1 it is the
+// identity.
+__device__ __forceinline__ int query_head(const Args& a, int x) { return (x % a.Hkv) * a.G + x / a.Hkv; }
+
 // Sequence base row and length of batch entry / packed sequence b; lengths are
 // clamped to [0, N] so a malformed cu_seqlens cannot enlarge the grid's work.
 __device__ __forceinline__ void seq_bounds(const Args& a, int b, int& row0, int& len) {

@@ -62,9 +62,10 @@ __global__ __launch_bounds__(NT, 1) void fwd_mfma_kernel(Args a) {
     const int col = lane & 31;
     const int kg = lane >> 5;
 
-    // Grid: x = query head, y = batch / sequence, z = query tile. Causal
-    // launches the longest tiles (highest index) first.
-    const int h = blockIdx.x;
+    // Grid: x = query head (kv-head-major, see query_head), y = batch /
+    // sequence, z = query tile. Causal launches the longest tiles (highest
+    // index) first.
+    const int h = query_head(a, blockIdx.x);
     const int b = blockIdx.y;
     const int qt = CAUSAL ? (int)(gridDim.z - 1 - blockIdx.z) : (int)blockIdx.z;
 
