@@ -78,15 +78,6 @@ __device__ __forceinline__ V8<T> as_v8(uint4 u) {
 
 __device__ __forceinline__ uint4 ld_g16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ uint4 ld_s16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
-__device__ __forceinline__ uint2 ld_s8(const uint16_t* p) { return *reinterpret_cast<const uint2*>(p); }
-__device__ __forceinline__ void st_s16(uint16_t* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
-__device__ __forceinline__ void st_s8(uint16_t* p, uint2 v) { *reinterpret_cast<uint2*>(p) = v; }
-
-// 16-bit element `e` (0..7) of a 16-byte chunk.
-__device__ __forceinline__ uint32_t half_of(const uint4& u, int e) {
-    const uint32_t w = (e < 2) ? u.x : (e < 4) ? u.y : (e < 6) ? u.z : u.w;
-    return (e & 1) ? (w >> 16) : (w & 0xffffu);
-}
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -116,19 +107,6 @@ __device__ __forceinline__ uint2 ld_s8_tr(const uint16_t* p) {
     return __builtin_bit_cast(uint2, v);
 }
 
-// MFMA A operand for a product whose contraction index runs along the ROWS of
-// a row-major LDS tile (for example V^T from V[key][d]): lane l gets column
-// (col0 + l % 32) and rows row0 + {4*kg .. 4*kg+3, 8+4*kg .. 8+4*kg+3},
-// kg = l / 32, which is the k order the score accumulator hands to its
-// transposed operand (see the layout notes above).
-__device__ __forceinline__ uint4 ld_s16_rows_tr(const uint16_t* tile, int pitch, int row0, int col0, int lane) {
-    const int r = lane & 15, grp = lane >> 4;
-    const uint16_t* p = tile + (row0 + 4 * (grp >> 1) + (r >> 2)) * pitch + col0 + 16 * (grp & 1) + 4 * (r & 3);
-    const uint2 lo = ld_s8_tr(p);
-    const uint2 hi = ld_s8_tr(p + 8 * pitch);
-    return make_uint4(lo.x, lo.y, hi.x, hi.y);
-}
-
 // Load of a wave-uniform, kernel-invariant value through the scalar cache
 // (s_load): unlike a vector load it is not counted by vmcnt, so waiting for it
 // does not also wait for the direct loads in flight.
@@ -152,18 +130,6 @@ __host__ __device__ constexpr int swz(int row, int col) {
     return row * D + (((col >> 3) ^ f) << 3) + (col & 7);
 }
 
-// Swizzled-tile variant of ld_s16_rows_tr: the MFMA A operand whose contraction
-// index runs along the rows, columns col0 + (lane % 32).
-template <int D>
-__device__ __forceinline__ uint4 ld_swz_rows_tr(const uint16_t* tile, int row0, int col0, int lane) {
-    const int r = lane & 15, grp = lane >> 4;
-    const int row = row0 + 4 * (grp >> 1) + (r >> 2);
-    const int col = col0 + 16 * (grp & 1) + 4 * (r & 3);
-    const uint2 lo = ld_s8_tr(tile + swz<D>(row, col));
-    const uint2 hi = ld_s8_tr(tile + swz<D>(row + 8, col));
-    return make_uint4(lo.x, lo.y, hi.x, hi.y);
-}
-
 // Row-major operand read from a swizzled tile: element offset of (row, col) for
 // row = 32 * blk + (lane % 32), col = 16 * kk + 8 * (lane / 32). The block
 // part is the constant 32 * blk * D because the swizzle depends on row % 16
@@ -173,9 +139,13 @@ __host__ __device__ constexpr int swz_row_off(int lane, int kk) {
     return swz<D>(lane & 31, 16 * kk + 8 * (lane >> 5));
 }
 
-// Transposed operand read from a swizzled tile (see ld_swz_rows_tr): lane part
-// of the offset of the low (half = 0) or high (half = 1) 8-byte read for
-// columns 32 * db + ...; rows 16 * c + ... add the constant 16 * c * D.
+// Transposed operand read from a swizzled tile: the MFMA A operand whose
+// contraction index runs along the rows (for example V^T from V[key][d]),
+// built from two transposing reads (ld_s8_tr). Lane l gets column
+// 32 * db + (l % 32) of rows {4 kg .. 4 kg + 3} (half = 0) and
+// {8 + 4 kg .. 8 + 4 kg + 3} (half = 1) of a 16-row chunk, kg = l / 32: the k
+// order the score accumulator hands to its transposed operand. This returns
+// the lane part of each read's offset; chunk c adds the constant 16 * c * D.
 template <int D>
 __host__ __device__ constexpr int swz_tr_off(int lane, int db, int half) {
     const int r = lane & 15, grp = lane >> 4;
