@@ -161,6 +161,16 @@ def test_bwd_varlen_small():
     _bwd_case(w, lengths=[200, 17, 128])
 
 
+@pytest.mark.parametrize("H,Hkv", [(8, 8), (8, 2), (8, 1)])
+def test_gqa_group_sizes(H, Hkv):
+    """Query-head groups of 1, 4 and 8 per kv head (the grid numbers query heads
+    kv-head-major, so every group size must still reach each head once)."""
+    for causal in (False, True):
+        w = Workload(f"gqa_h{H}_kv{Hkv}_c{int(causal)}", "bf16", 1, H, Hkv, 200, 128, causal=causal)
+        _fwd_case(w, seed=H * 10 + Hkv)
+        _bwd_case(w, seed=H * 10 + Hkv)
+
+
 def test_bwd_gpt2m_full():
     """GPT-2-medium shape at full size, whole-tensor comparison of dQ, dK, dV."""
     _banner(str(_bwd_case(WORKLOADS["gpt2m"])))
