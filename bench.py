@@ -79,6 +79,8 @@ def parse():
     ap.add_argument("--workload", default="long_causal")
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-telemetry", action="store_true",
+                    help="skip the amd-smi reading under load (profiling runs: keeps the trace to the timed work)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the measurement run a plain 1 GiB fp32 copy (negation) for counter calibration")
@@ -262,15 +264,16 @@ def main():
     import threading
 
     tel = {}
-    th = threading.Thread(target=lambda: tel.update(r=gpu_telemetry()))
-    th.start()
-    t_end = time.perf_counter() + 6.0
-    while time.perf_counter() < t_end or th.is_alive():
-        step()
-        if time.perf_counter() > t_end + 30.0:
-            break
-    th.join()
-    torch.cuda.synchronize()
+    if not args.no_telemetry:
+        th = threading.Thread(target=lambda: tel.update(r=gpu_telemetry()))
+        th.start()
+        t_end = time.perf_counter() + 6.0
+        while time.perf_counter() < t_end or th.is_alive():
+            step()
+            if time.perf_counter() > t_end + 30.0:
+                break
+        th.join()
+        torch.cuda.synchronize()
     telemetry = tel.get("r")
 
     cpu = None
