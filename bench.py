@@ -107,14 +107,18 @@ def main():
     from exact_io_aware_43_amd.workloads import WORKLOADS, flops, make_inputs, seq_lengths
 
     w = WORKLOADS[args.workload]
-    if not w.backward:
-        raise SystemExit(f"workload {w.name} has no backward pass; the step is forward+backward")
+    if w.dtype == "fp32":
+        raise SystemExit(f"workload {w.name} is the fp32 latency case (one or two workgroups); it is a parity "
+                         "case, not a throughput workload")
+    has_bwd = bool(w.backward)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"[bench] workload {w}", file=sys.stderr, flush=True)
 
     inp = make_inputs(w, args.seed, with_grad=True)
     q, k, v, do = (inp[x].to(dev) for x in ("q", "k", "v", "do"))
+    if not has_bwd:
+        do = None
     cu = inp["cu_seqlens"].to(dev) if inp["cu_seqlens"] is not None else None
     slopes = inp["alibi_slopes"].to(dev) if inp["alibi_slopes"] is not None else None
     lens = seq_lengths(inp, w)
@@ -130,9 +134,10 @@ def main():
     torch.cuda.reset_peak_memory_stats()
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws_bytes = fa.fa_bwd_workspace_size(B, H, Hkv, N, d, causal, int(cu is not None), dt)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    if has_bwd:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws_bytes = fa.fa_bwd_workspace_size(B, H, Hkv, N, d, causal, int(cu is not None), dt)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     P = lambda t: None if t is None else t.data_ptr()  # noqa: E731
 
     def fwd():
@@ -150,7 +155,8 @@ def main():
 
     def step():
         fwd()
-        bwd()
+        if has_bwd:
+            bwd()
 
     step()
     torch.cuda.synchronize()
@@ -174,7 +180,7 @@ def main():
     print(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step (wall {wall:.2f} s)", file=sys.stderr, flush=True)
 
     f_fwd = flops(w, lens)
-    f_bwd = flops(w, lens, backward=True)
+    f_bwd = flops(w, lens, backward=True) if has_bwd else 0.0
     value = (f_fwd + f_bwd) / (ms * 1e-3) / 1e12
 
     # ---- each kernel alone, HIP events on the launch stream
@@ -214,12 +220,15 @@ def main():
         "bwd_dkdv": 2 * qb + 4 * kvb + 2 * vec,       # Q, dO, K, V, D, L in; dK, dV out
         "bwd_dq": 3 * qb + 2 * kvb + 2 * vec,         # Q, dO, K, V, D, L in; dQ out
     }
-    kernels = {
-        "fwd": dict(ms=time_launches(fwd, "fwd"), work=f_fwd, bound="mfma"),
-        "bwd_dsum": dict(ms=time_launches(lambda: bwd(fa.FA_BWD_PREP), "bwd_dsum"), work=dsum_bytes, bound="hbm"),
-        "bwd_dkdv": dict(ms=time_launches(lambda: bwd(fa.FA_BWD_DKDV), "bwd_dkdv"), work=2.0 * f_fwd, bound="mfma"),
-        "bwd_dq": dict(ms=time_launches(lambda: bwd(fa.FA_BWD_DQ), "bwd_dq"), work=0.5 * f_fwd, bound="mfma"),
-    }
+    kernels = {"fwd": dict(ms=time_launches(fwd, "fwd"), work=f_fwd, bound="mfma")}
+    if has_bwd:
+        kernels.update({
+            "bwd_dsum": dict(ms=time_launches(lambda: bwd(fa.FA_BWD_PREP), "bwd_dsum"), work=dsum_bytes,
+                             bound="hbm"),
+            "bwd_dkdv": dict(ms=time_launches(lambda: bwd(fa.FA_BWD_DKDV), "bwd_dkdv"), work=2.0 * f_fwd,
+                             bound="mfma"),
+            "bwd_dq": dict(ms=time_launches(lambda: bwd(fa.FA_BWD_DQ), "bwd_dq"), work=0.5 * f_fwd, bound="mfma"),
+        })
     for name, kr in kernels.items():
         if kr["bound"] == "mfma":
             kr["achieved"] = kr["work"] / (kr["ms"] * 1e-3) / 1e12
@@ -294,11 +303,12 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "H": H, "Hkv": Hkv, "N": N, "d": d, "causal": bool(w.causal),
-                   "alibi": bool(w.alibi), "pass": "forward+backward"},
+                   "alibi": bool(w.alibi), "pass": "forward+backward" if has_bwd else "forward",
+                   **({"sequences": len(lens), "tokens": int(T)} if cu is not None else {})},
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "fwd_tflops": round(f_fwd / (kernels["fwd"]["ms"] * 1e-3) / 1e12, 2),
-        "bwd_tflops": round(f_bwd / (sum(kernels[n]["ms"] for n in ("bwd_dsum", "bwd_dkdv", "bwd_dq")) * 1e-3)
-                            / 1e12, 2),
+        "bwd_tflops": (round(f_bwd / (sum(kernels[n]["ms"] for n in ("bwd_dsum", "bwd_dkdv", "bwd_dq")) * 1e-3)
+                             / 1e12, 2) if has_bwd else None),
         "kernels": {n: {"ms": round(kr["ms"], 4), "achieved": round(kr["achieved"], 2), "unit": kr["unit"],
                         "frac": round(kr["frac"], 4),
                         "median_ms": round(launch_stats[n][0], 4), "min_ms": round(launch_stats[n][1], 4),
@@ -312,7 +322,7 @@ def main():
                 "gpu": torch.cuda.get_device_properties(0).gcnArchName, "telemetry_under_load": telemetry},
     }
     out["fwd_frac_of_peak"] = round(out["fwd_tflops"] / PEAK_BF16_TFLOPS, 4)
-    out["bwd_frac_of_peak"] = round(out["bwd_tflops"] / PEAK_BF16_TFLOPS, 4)
+    out["bwd_frac_of_peak"] = round(out["bwd_tflops"] / PEAK_BF16_TFLOPS, 4) if has_bwd else None
     print(json.dumps(out), flush=True)
 
     if args.copy_calibration:
@@ -321,6 +331,18 @@ def main():
         torch.neg(x, out=y)
         torch.cuda.synchronize()
         print(f"[bench] copy calibration: neg of {COPY_BYTES} bytes", file=sys.stderr, flush=True)
+
+
+def _cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None where it is not readable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.lower().startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def _read_first(path):
@@ -459,15 +481,15 @@ def cpu_baseline(w, inp, lens):
         q = OA._f64(inp["q"][sl][:, h])
         k = OA._f64(inp["k"][sl][:, h // G])
         v = OA._f64(inp["v"][sl][:, h // G])
-        do = OA._f64(inp["do"][sl][:, h])
         slope = None if inp["alibi_slopes"] is None else float(inp["alibi_slopes"][h])
         t0 = time.perf_counter()
         OA.head_fwd(q, k, v, inp["scale"], w.causal, slope)
-        OA.head_bwd(q, k, v, do, inp["scale"], w.causal, slope)
+        if w.backward:
+            OA.head_bwd(q, k, v, OA._f64(inp["do"][sl][:, h]), inp["scale"], w.causal, slope)
         t += time.perf_counter() - t0
         heads += 1
     one = w.with_(B=1, H=1, Hkv=1)
-    work = heads * (flops(one, [n]) + flops(one, [n], backward=True))
+    work = heads * (flops(one, [n]) + (flops(one, [n], backward=True) if w.backward else 0.0))
     blas = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
     return {
         "value": round(work / t / 1e12, 5),
@@ -475,8 +497,9 @@ def cpu_baseline(w, inp, lens):
         "cores": int(max(blas) if blas else 1),
         "kind": "oracle",
         "sample": f"heads 0..{heads - 1} of sequence 0 of {w.name}: N={n}, d={w.d}, causal={w.causal}; "
-                  f"fp64 numpy forward + backward, {t:.1f} s",
+                  f"fp64 numpy forward{' + backward' if w.backward else ''}, {t:.1f} s",
         "host_cpus_available": len(os.sched_getaffinity(0)),
+        "cpu_model": _cpu_model(),
         "seconds": round(t, 2),
     }
 

@@ -103,6 +103,7 @@ def _stream_handle() -> int:
 
 
 def _shape(q: torch.Tensor, k: torch.Tensor, cu_seqlens, max_seqlen):
+    """(B, H, Hkv, N, d) of a call, from q and k (dense) or q, k and cu_seqlens (packed)."""
     if cu_seqlens is None:
         if q.dim() != 4 or k.dim() != 4:
             raise ValueError("dense inputs are q [B, N, H, d], k/v [B, N, Hkv, d]")
@@ -111,6 +112,8 @@ def _shape(q: torch.Tensor, k: torch.Tensor, cu_seqlens, max_seqlen):
     else:
         if q.dim() != 3 or k.dim() != 3:
             raise ValueError("packed inputs are q [total, H, d], k/v [total, Hkv, d]")
+        if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+            raise ValueError("cu_seqlens must be a 1-D tensor of B + 1 offsets")
         if max_seqlen is None:
             raise ValueError("packed inputs need max_seqlen")
         _, H, d = q.shape
@@ -119,10 +122,62 @@ def _shape(q: torch.Tensor, k: torch.Tensor, cu_seqlens, max_seqlen):
     return B, H, Hkv, N, d
 
 
-def _check_tensors(*ts):
-    for t in ts:
-        if t is not None and (not t.is_cuda or not t.is_contiguous()):
-            raise ValueError("libfa takes contiguous device tensors")
+def _expect(t: Optional[torch.Tensor], name: str, shape, dtype, device) -> None:
+    """Raise ValueError unless ``t`` is a contiguous tensor of exactly this shape,
+    dtype and device (the layouts the C ABI documents)."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def validate(q, k, v, *, cu_seqlens=None, max_seqlen=None, alibi_slopes=None, q_like=(), lse=None,
+             require_device: bool = True):
+    """Check every tensor of a call against the sizes (B, H, Hkv, N, d) that q, k and
+    cu_seqlens imply, and return those sizes.
+
+    q_like: (name, tensor) pairs that must match q exactly (o, dout, out). Packed
+    inputs need int32 cu_seqlens [B + 1]; alibi_slopes is fp32 [H]; lse is fp32
+    [B, H, N]. Every tensor must be contiguous and on q's device, which must be a
+    GPU unless ``require_device`` is False (host-side tests of this function).
+    Lengths inside cu_seqlens live in device memory and are not read here: the
+    library treats N as the caller's bound on every length.
+    """
+    if not isinstance(q, torch.Tensor):
+        raise ValueError("q must be a torch.Tensor")
+    if require_device and not q.is_cuda:
+        raise ValueError("libfa takes device tensors (q is on the host)")
+    if q.dtype not in _DTYPE:
+        raise ValueError(f"q has dtype {q.dtype}; libfa takes float32, float16 or bfloat16")
+    B, H, Hkv, N, d = _shape(q, k, cu_seqlens, max_seqlen)
+    dev, dt = q.device, q.dtype
+    _expect(q, "q", q.shape, dt, dev)
+    if cu_seqlens is None:
+        kv_shape = (B, N, Hkv, d)
+    else:
+        kv_shape = (q.shape[0], Hkv, d)
+        _expect(cu_seqlens, "cu_seqlens", (B + 1,), torch.int32, dev)
+        if N <= 0:
+            raise ValueError("max_seqlen must be positive")
+    _expect(k, "k", kv_shape, dt, dev)
+    _expect(v, "v", kv_shape, dt, dev)
+    if H % Hkv != 0:
+        raise ValueError(f"query heads ({H}) must be a multiple of kv heads ({Hkv})")
+    if alibi_slopes is not None:
+        _expect(alibi_slopes, "alibi_slopes", (H,), torch.float32, dev)
+    for name, t in q_like:
+        _expect(t, name, q.shape, dt, dev)
+    if lse is not None:
+        _expect(lse, "lse", (B, H, N), torch.float32, dev)
+    return B, H, Hkv, N, d
 
 
 def attention(q, k, v, causal: bool = False, softmax_scale: Optional[float] = None,
@@ -133,12 +188,11 @@ def attention(q, k, v, causal: bool = False, softmax_scale: Optional[float] = No
 
     Mirrors ``flash_attn_func(q, k, v, softmax_scale=None, causal=...)`` (no
     dropout). ``lse`` is fp32 [B, H, N] (N = max_seqlen for packed inputs).
+    Every tensor is validated against the layouts of the C ABI before the call.
     """
-    _check_tensors(q, k, v, alibi_slopes, cu_seqlens)
-    B, H, Hkv, N, d = _shape(q, k, cu_seqlens, max_seqlen)
+    B, H, Hkv, N, d = validate(q, k, v, cu_seqlens=cu_seqlens, max_seqlen=max_seqlen, alibi_slopes=alibi_slopes,
+                               q_like=(() if out is None else (("out", out),)), lse=lse)
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
-    if q.dtype not in _DTYPE or k.dtype != q.dtype or v.dtype != q.dtype:
-        raise ValueError("q, k, v must share one of fp32 / fp16 / bf16")
     o = torch.empty_like(q) if out is None else out
     l = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
     st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(), B, H, Hkv, N, d, scale,
@@ -152,18 +206,20 @@ def attention_bwd(dout, q, k, v, o, lse, causal: bool = False, softmax_scale: Op
                   alibi_slopes: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None,
                   max_seqlen: Optional[int] = None, workspace: Optional[torch.Tensor] = None):
     """Exact attention backward through ``fa_bwd``: returns (dq, dk, dv)."""
-    _check_tensors(dout, q, k, v, o, lse, alibi_slopes, cu_seqlens)
-    B, H, Hkv, N, d = _shape(q, k, cu_seqlens, max_seqlen)
+    B, H, Hkv, N, d = validate(q, k, v, cu_seqlens=cu_seqlens, max_seqlen=max_seqlen, alibi_slopes=alibi_slopes,
+                               q_like=(("o", o), ("dout", dout)), lse=lse)
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     dt = _DTYPE[q.dtype]
     ws_bytes = fa_bwd_workspace_size(B, H, Hkv, N, d, int(bool(causal)), int(cu_seqlens is not None), dt)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    elif not (workspace.is_contiguous() and workspace.device == q.device):
+        raise ValueError("workspace must be a contiguous tensor on q's device")
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
                 dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, N, d, scale, int(bool(causal)),
-                _ptr(alibi_slopes), _ptr(cu_seqlens), dt, workspace.data_ptr(), workspace.numel(),
-                _stream_handle())
+                _ptr(alibi_slopes), _ptr(cu_seqlens), dt, workspace.data_ptr(),
+                workspace.numel() * workspace.element_size(), _stream_handle())
     if st != FA_OK:
         raise FaError(st)
     return dq, dk, dv

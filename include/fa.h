@@ -24,6 +24,11 @@
  *   cu_seqlens             : int32 [B + 1], device memory, cu_seqlens[0] = 0,
  *                            non-decreasing; every length must be <= N (N is
  *                            the maximum sequence length in packed mode).
+ *                            The lengths live in device memory and are not
+ *                            checked on the host: a length above N is
+ *                            truncated to N (its rows past N are neither read
+ *                            nor written) and a negative one is treated as
+ *                            empty, and the call still returns FA_OK.
  *   alibi_slopes           : float [H], device memory, or NULL for no bias.
  *
  * Element types (fa_dtype): FA_BF16 and FA_FP16 store q, k, v, o, dout, dq, dk,

@@ -63,6 +63,8 @@ __all__ = [
     "head_bwd",
     "head_rows_fwd",
     "online_head_fwd",
+    "tile_state",
+    "merge_states",
     "brute_fwd",
 ]
 
@@ -208,49 +210,66 @@ def attention_bwd(q, k, v, do, scale=None, causal=False, alibi_slopes=None, cu_s
     return dq, dk, dv
 
 
-def online_head_fwd(qh, kh, vh, scale, bounds, causal=False, slope=None):
-    """The blockwise online-softmax recurrence for one (sequence, head), in fp64.
+def tile_state(qh, kh, vh, lo, hi, scale, causal=False, slope=None):
+    """Softmax state of one query block against the keys [lo, hi) alone ([PN] Key design 2).
 
-    Follows the merge of [PN] Key design 2 (also the per-tile loop of [RX]): keys
-    are visited in the tiles [bounds[t], bounds[t+1]); each tile's scores give a
-    tile maximum and local exponential sum, and the running (m, l, O) is rescaled
-    to the common maximum m' = max(m, m~):
-
-        l' = e^(m - m') l + e^(m~ - m') l~
-        O' = (e^(m - m') l O + e^(m~ - m') P~ V_j) / l'
-
-    State starts at m = -inf, l = 0, O = 0. A row whose tile is entirely masked
-    keeps its state unchanged (its tile contributes exactly zero). Returns (O, lse)
-    with lse = m + ln l. This is a second, independent route to the same values
-    as :func:`head_fwd`; by Theorem 1 the two agree up to rounding.
+    For each query row i the state is (m_i, l_i, U_i): the largest score of the
+    row within these keys, the sum of exp(S_ij - m_i) over them, and the
+    unnormalised output sum_j exp(S_ij - m_i) V_j. A row that sees none of
+    these keys (all masked) has the empty state (-inf, 0, 0).
     """
     n_q = qh.shape[0]
     rows = np.arange(n_q)
+    s = _scores(qh, kh[:hi], scale, causal, slope, rows=rows)[:, lo:hi]
+    seen = np.isfinite(s).any(axis=1)
     m = np.full(n_q, -np.inf)
-    ell = np.zeros(n_q)
-    o = np.zeros((n_q, vh.shape[1]))
-    for lo, hi in zip(bounds[:-1], bounds[1:]):
-        if hi <= lo:
-            continue
-        cols = np.arange(lo, hi)
-        s = scale * (qh @ kh[lo:hi].T)
-        if slope is not None:
-            s = s - slope * np.abs(rows[:, None] - cols[None, :]).astype(np.float64)
-        if causal:
-            s = np.where(cols[None, :] > rows[:, None], -np.inf, s)
-        live = np.isfinite(s).any(axis=1)
-        m_t = np.where(live, s.max(axis=1), -np.inf)
-        p_t = np.where(live[:, None], np.exp(s - np.where(live, m_t, 0.0)[:, None]), 0.0)
-        l_t = p_t.sum(axis=1)
-        m_new = np.maximum(m, m_t)
-        a_old = np.where(np.isfinite(m), np.exp(m - m_new), 0.0)
-        a_new = np.where(live, np.exp(m_t - m_new), 0.0)
-        l_new = a_old * ell + a_new * l_t
-        upd = l_new > 0
-        num = (a_old * ell)[:, None] * o + a_new[:, None] * (p_t @ vh[lo:hi])
-        o = np.where(upd[:, None], num / np.where(upd, l_new, 1.0)[:, None], o)
-        m, ell = np.where(upd, m_new, m), np.where(upd, l_new, ell)
-    return o, m + np.log(ell)
+    m[seen] = s[seen].max(axis=1)
+    w = np.zeros_like(s)
+    w[seen] = np.exp(s[seen] - m[seen][:, None])
+    return m, w.sum(axis=1), w @ vh[lo:hi]
+
+
+def merge_states(a, b):
+    """State of the union of two disjoint key sets from the states of each ([PN] Key design 2).
+
+    With m = max(m_a, m_b) every term of a is re-referenced by exp(m_a - m) and
+    every term of b by exp(m_b - m); an empty side has weight 0.
+    """
+    (ma, la, ua), (mb, lb, ub) = a, b
+    m = np.maximum(ma, mb)
+    wa = np.zeros_like(m)
+    wb = np.zeros_like(m)
+    fa, fb = np.isfinite(ma), np.isfinite(mb)
+    wa[fa] = np.exp(ma[fa] - m[fa])
+    wb[fb] = np.exp(mb[fb] - m[fb])
+    return m, wa * la + wb * lb, wa[:, None] * ua + wb[:, None] * ub
+
+
+def online_head_fwd(qh, kh, vh, scale, bounds, causal=False, slope=None, order="stream"):
+    """O and lse of one (sequence, head) from per-tile states, combined with :func:`merge_states`.
+
+    Keys are split into the tiles [bounds[t], bounds[t+1]). ``order`` is
+    "stream" (fold the tiles left to right, the order in which a kernel
+    visits them) or "tree" (merge neighbouring pairs until one state is left).
+    Normalisation happens once at the end: O = U / l, lse = m + ln l. By the
+    page's Theorem 1 this equals :func:`head_fwd` up to rounding for any split
+    and any merge order.
+    """
+    states = [tile_state(qh, kh, vh, lo, hi, scale, causal, slope)
+              for lo, hi in zip(bounds[:-1], bounds[1:]) if hi > lo]
+    if order == "stream":
+        acc = states[0]
+        for st in states[1:]:
+            acc = merge_states(acc, st)
+    elif order == "tree":
+        while len(states) > 1:
+            states = [merge_states(states[i], states[i + 1]) if i + 1 < len(states) else states[i]
+                      for i in range(0, len(states), 2)]
+        acc = states[0]
+    else:
+        raise ValueError(order)
+    m, ell, u = acc
+    return u / ell[:, None], m + np.log(ell)
 
 
 def brute_fwd(q, k, v, scale=None, causal=False, alibi_slopes=None, cu_seqlens=None):

@@ -4,12 +4,15 @@ Tolerances (fixed for this path): fp32 forward O max-abs <= 1e-5; 16-bit
 forward O max-abs <= 1e-2 and relative RMS <= 5e-3, lse max-abs <= 1e-3;
 16-bit backward relative RMS <= 1e-2 on each of dQ, dK, dV.
 
-A 16-bit O is stored in its own type, and no value of that type is closer to
-the exact result than half a unit in the last place (ulp): 0.0078 for
-|O| in [2, 4) and 0.0156 for |O| in [4, 8) in bf16. The O max-abs gate is
-therefore applied to the error beyond that unavoidable rounding,
-max(|o - o_ref| - ulp(o_ref)/2) <= 1e-2; the plain max-abs is reported next
-to it.
+A 16-bit O is stored in its own type. Where half a unit in the last place of
+that type at |O_ref| is below 1e-2 (|O_ref| < 4 in bf16, < 32 in fp16) a
+correctly rounded output meets the 1e-2 bound, and the raw max-abs
+|o - o_ref| is gated there. Only where half an ulp is 1e-2 or more can no
+value of the type meet it; on those elements the gate is the error beyond that
+rounding, |o - o_ref| - ulp(o_ref)/2 <= 1e-2. Both maxima are recorded.
+
+Every comparison is appended to RECORDS (test id, workload, metrics); the test
+session writes them out when FA_PARITY_REPORT names a file (see conftest.py).
 """
 
 from __future__ import annotations
@@ -69,7 +72,7 @@ def check_fwd_full(w: Workload, inp: dict, o, lse):
     mask = np.zeros(lg.shape, dtype=bool)
     for b, n in enumerate(lens):
         mask[b, :, :n] = True
-    return _compare_fwd(w, og, o_ref, lg[mask], lse_ref[mask])
+    return _compare_fwd(w, og, o_ref, lg[mask], lse_ref[mask], note="whole tensors")
 
 
 _SIG_BITS = {"bf16": 8, "fp16": 11, "fp32": 24}
@@ -85,20 +88,36 @@ def half_ulp(x: np.ndarray, dtype: str) -> np.ndarray:
     return 0.5 * ulp
 
 
-def _compare_fwd(w, og, o_ref, lg, lref):
+RECORDS: list = []
+CURRENT_TEST = {"id": None}
+
+
+def record(kind: str, w: Workload, metrics: dict, **extra) -> None:
+    RECORDS.append(dict(test=CURRENT_TEST["id"], kind=kind, workload=w.name, dtype=w.dtype, B=w.B, H=w.H,
+                        Hkv=w.Hkv, N=w.N, d=w.d, causal=bool(w.causal), alibi=bool(w.alibi), **extra, **metrics))
+
+
+def _compare_fwd(w, og, o_ref, lg, lref, note=""):
+    assert np.isfinite(og).all() and np.isfinite(lg).all(), "non-finite output"
     diff = np.abs(og - o_ref)
+    hu = half_ulp(o_ref, w.dtype)
+    reach = hu < TOL_O_MAX  # a correctly rounded output can meet the bound here
     err_o = float(diff.max()) if og.size else 0.0
-    excess = float((diff - half_ulp(o_ref, w.dtype)).max()) if og.size else 0.0
+    err_reach = float(diff[reach].max()) if reach.any() else 0.0
+    excess = float((diff - hu)[~reach].max()) if (~reach).any() else 0.0
     err_l = float(np.abs(lg - lref).max()) if lg.size else 0.0
     rms = rel_rms(og, o_ref) if og.size else 0.0
-    assert np.isfinite(og).all() and np.isfinite(lg).all(), "non-finite output"
+    out = dict(o_maxabs=err_o, o_maxabs_gated=err_reach, o_beyond_rounding=excess, n_beyond=int((~reach).sum()),
+               o_relrms=rms, lse_maxabs=err_l, n_rows=int(lg.size))
+    record("fwd", w, out, note=note)
     if w.dtype == "fp32":
         assert err_o <= TOL_F32_O, f"O max-abs {err_o:.3e} > {TOL_F32_O}"
     else:
-        assert excess <= TOL_O_MAX, f"O max-abs beyond output rounding {excess:.3e} > {TOL_O_MAX}"
+        assert err_reach <= TOL_O_MAX, f"O max-abs {err_reach:.3e} > {TOL_O_MAX}"
+        assert excess <= TOL_O_MAX, f"O max-abs beyond output rounding {excess:.3e} > {TOL_O_MAX} (|O| large)"
         assert rms <= TOL_O_RMS, f"O rel-RMS {rms:.3e} > {TOL_O_RMS}"
         assert err_l <= TOL_LSE, f"lse max-abs {err_l:.3e} > {TOL_LSE}"
-    return dict(o_maxabs=err_o, o_beyond_rounding=excess, o_relrms=rms, lse_maxabs=err_l)
+    return out
 
 
 def _head_view(inp, w, b, h):
@@ -118,7 +137,7 @@ def _head_view(inp, w, b, h):
     return q, k, v, n, sl
 
 
-def check_fwd_sampled(w: Workload, inp: dict, o, lse, samples):
+def check_fwd_sampled(w: Workload, inp: dict, o, lse, samples, note="sampled rows"):
     """Compare sampled rows of O and lse: ``samples`` is a list of (b, h, rows)."""
     ogs, orefs, lgs, lrefs = [], [], [], []
     og_all, lg_all = o.cpu(), lse.cpu()
@@ -133,19 +152,20 @@ def check_fwd_sampled(w: Workload, inp: dict, o, lse, samples):
         orefs.append(o_ref)
         lgs.append(f64(lg_all[b, h])[rows])
         lrefs.append(l_ref)
-    return _compare_fwd(w, np.concatenate(ogs), np.concatenate(orefs), np.concatenate(lgs), np.concatenate(lrefs))
+    return _compare_fwd(w, np.concatenate(ogs), np.concatenate(orefs), np.concatenate(lgs), np.concatenate(lrefs),
+                        note=note)
 
 
 def check_bwd_full(w: Workload, inp: dict, grads):
     ref = OA.attention_bwd(inp["q"], inp["k"], inp["v"], inp["do"], scale=inp["scale"], causal=w.causal,
                            alibi_slopes=inp["alibi_slopes"], cu_seqlens=inp["cu_seqlens"])
-    return _compare_bwd([f64(g) for g in grads], ref)
+    return _compare_bwd(w, [f64(g) for g in grads], ref, note="whole tensors")
 
 
 TOL_ZERO_GRAD_RMS = 1e-3
 
 
-def _compare_bwd(got, ref):
+def _compare_bwd(w, got, ref, note=""):
     """Relative RMS per gradient. A reference that is exactly zero (one key per
     row: P = 1 and dS = 0, so dQ = dK = 0) has no relative error; there the
     absolute RMS of the result must be below 1e-3 instead."""
@@ -153,17 +173,20 @@ def _compare_bwd(got, ref):
     for name, g, r in zip(("dq", "dk", "dv"), got, ref):
         assert np.isfinite(g).all(), f"non-finite {name}"
         if not np.any(r):
-            e = float(np.sqrt(np.mean(g ** 2))) if g.size else 0.0
-            out[name + "_abs_rms"] = e
+            out[name + "_abs_rms"] = float(np.sqrt(np.mean(g ** 2))) if g.size else 0.0
+        else:
+            out[name] = rel_rms(g, r)
+    record("bwd", w, out, note=note)
+    for name in ("dq", "dk", "dv"):
+        if name in out:
+            assert out[name] <= TOL_GRAD_RMS, f"{name} rel-RMS {out[name]:.3e} > {TOL_GRAD_RMS}"
+        else:
+            e = out[name + "_abs_rms"]
             assert e <= TOL_ZERO_GRAD_RMS, f"{name} abs-RMS {e:.3e} > {TOL_ZERO_GRAD_RMS} (zero reference)"
-            continue
-        e = rel_rms(g, r)
-        out[name] = e
-        assert e <= TOL_GRAD_RMS, f"{name} rel-RMS {e:.3e} > {TOL_GRAD_RMS}"
     return out
 
 
-def check_bwd_heads(w: Workload, inp: dict, grads, pairs):
+def check_bwd_heads(w: Workload, inp: dict, grads, pairs, note="whole (sequence, kv head) groups"):
     """Full-size backward check on whole (b, kv head) groups: every query head of
     the group is recomputed by the oracle, so dK and dV of that kv head and dQ of
     those query heads are exact references."""
@@ -185,7 +208,8 @@ def check_bwd_heads(w: Workload, inp: dict, grads, pairs):
         ref[1].append(dk_sum)
         got[2].append(f64(dv[sl][:, g]))
         ref[2].append(dv_sum)
-    return _compare_bwd([np.concatenate(x) for x in got], [np.concatenate(x) for x in ref])
+    return _compare_bwd(w, [np.concatenate(x) for x in got], [np.concatenate(x) for x in ref],
+                        note=f"{note} {pairs}")
 
 
 def small(w_name_or_w, **kw) -> Workload:
@@ -196,3 +220,50 @@ def small(w_name_or_w, **kw) -> Workload:
 
 
 __all__ = [name for name in dir() if not name.startswith("_")] + ["make_inputs"]
+
+
+_NAMED = ("fp32_small", "gpt2m", "long_causal", "varlen_alibi", "gqa")
+
+
+def _fmt(x):
+    return "—" if x is None else (f"{x:.2e}" if isinstance(x, float) else str(x))
+
+
+def write_report(path: str) -> None:
+    """RECORDS as JSON at ``path`` and as Markdown tables at ``path + '.md'``: the
+    named workloads at full size first (worst value of each metric over their
+    checks), then every comparison of the session."""
+    import json
+    import os
+
+    os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+    with open(path, "w") as f:
+        json.dump(RECORDS, f, indent=1)
+    fwd_keys = ("o_maxabs_gated", "o_beyond_rounding", "o_maxabs", "o_relrms", "lse_maxabs")
+    bwd_keys = ("dq", "dk", "dv")
+    lines = ["# GPU parity against the fp64 oracle", "",
+             "Bars: fp32 O max-abs <= 1e-5; 16-bit O max-abs <= 1e-2 (raw, on elements where half an ulp of the",
+             "output type is below 1e-2; beyond that rounding elsewhere), O relative RMS <= 5e-3, lse max-abs <= 1e-3;",
+             "dQ, dK, dV relative RMS <= 1e-2.", "",
+             "## Named workloads at full size (worst over their checks)", "",
+             "| workload | pass | checks | " + " | ".join(fwd_keys) + " | " + " | ".join(b + " rel-RMS" for b in bwd_keys)
+             + " |",
+             "|" + "---|" * (3 + len(fwd_keys) + len(bwd_keys))]
+    for name in _NAMED:
+        for kind in ("fwd", "bwd"):
+            rs = [r for r in RECORDS if r["workload"] == name and r["kind"] == kind]
+            if not rs:
+                continue
+            keys = fwd_keys if kind == "fwd" else bwd_keys
+            vals = {k: max((r[k] for r in rs if k in r), default=None) for k in keys}
+            cells = [_fmt(vals.get(k)) if k in keys else "" for k in fwd_keys + bwd_keys]
+            lines.append(f"| {name} | {kind} | {len(rs)} | " + " | ".join(cells) + " |")
+    lines += ["", "## Every comparison", "",
+              "| test | workload | pass | note | metrics |", "|---|---|---|---|---|"]
+    skip = {"test", "kind", "workload", "note", "dtype", "B", "H", "Hkv", "N", "d", "causal", "alibi"}
+    for r in RECORDS:
+        shape = f"{r['dtype']} B{r['B']} H{r['H']}/{r['Hkv']} N{r['N']} d{r['d']} c{int(r['causal'])} a{int(r['alibi'])}"
+        m = ", ".join(f"{k}={_fmt(v)}" for k, v in r.items() if k not in skip)
+        lines.append(f"| {r['test']} | {r['workload']} ({shape}) | {r['kind']} | {r.get('note', '')} | {m} |")
+    with open(path + ".md", "w") as f:
+        f.write("\n".join(lines) + "\n")

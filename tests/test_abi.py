@@ -129,3 +129,83 @@ def test_no_undefined_kernel_stubs():
     diagnostic that is deferred for device code can silently drop them)."""
     out = subprocess.run(["nm", "-D", "--undefined-only", fa.LIB_PATH], capture_output=True, text=True).stdout
     assert "__device_stub__" not in out, [l for l in out.splitlines() if "__device_stub__" in l][:3]
+
+
+def _val_case(**over):
+    """Keyword arguments of a valid dense (or packed) call on host tensors, with overrides."""
+    import torch
+
+    bf = torch.bfloat16
+    base = dict(q=torch.zeros(2, 8, 4, 64, dtype=bf), k=torch.zeros(2, 8, 2, 64, dtype=bf),
+                v=torch.zeros(2, 8, 2, 64, dtype=bf), cu_seqlens=None, max_seqlen=None, alibi_slopes=None,
+                q_like=(), lse=None)
+    base.update(over)
+    return base
+
+
+def _validate(**kw):
+    q, k, v = kw.pop("q"), kw.pop("k"), kw.pop("v")
+    return fa._binding.validate(q, k, v, require_device=False, **kw)
+
+
+def test_binding_validation_accepts_valid_calls():
+    import torch
+
+    assert _validate(**_val_case()) == (2, 4, 2, 8, 64)
+    c = _val_case(alibi_slopes=torch.zeros(4), lse=torch.zeros(2, 4, 8),
+                  q_like=(("o", torch.zeros(2, 8, 4, 64, dtype=torch.bfloat16)),))
+    assert _validate(**c) == (2, 4, 2, 8, 64)
+    bf = torch.bfloat16
+    packed = dict(q=torch.zeros(30, 4, 128, dtype=bf), k=torch.zeros(30, 1, 128, dtype=bf),
+                  v=torch.zeros(30, 1, 128, dtype=bf), cu_seqlens=torch.tensor([0, 10, 30], dtype=torch.int32),
+                  max_seqlen=20, lse=torch.zeros(2, 4, 20))
+    assert _validate(**_val_case(**packed)) == (2, 4, 1, 20, 128)
+
+
+def _bad_cases():
+    import torch
+
+    bf, f16 = torch.bfloat16, torch.float16
+    cu = torch.tensor([0, 10, 30], dtype=torch.int32)
+    packed = dict(q=torch.zeros(30, 4, 128, dtype=bf), k=torch.zeros(30, 2, 128, dtype=bf),
+                  v=torch.zeros(30, 2, 128, dtype=bf), cu_seqlens=cu, max_seqlen=20)
+    return {
+        "k_wrong_N": dict(k=torch.zeros(2, 7, 2, 64, dtype=bf)),
+        "k_wrong_B": dict(k=torch.zeros(1, 8, 2, 64, dtype=bf)),
+        "k_wrong_d": dict(k=torch.zeros(2, 8, 2, 32, dtype=bf)),
+        "v_differs_from_k": dict(v=torch.zeros(2, 8, 1, 64, dtype=bf)),
+        "k_dtype": dict(k=torch.zeros(2, 8, 2, 64, dtype=f16)),
+        "q_dtype_int": dict(q=torch.zeros(2, 8, 4, 64, dtype=torch.int16)),
+        "heads_not_multiple": dict(k=torch.zeros(2, 8, 3, 64, dtype=bf), v=torch.zeros(2, 8, 3, 64, dtype=bf)),
+        "noncontiguous_v": dict(v=torch.zeros(2, 8, 64, 2, dtype=bf).transpose(2, 3)),
+        "slopes_dtype": dict(alibi_slopes=torch.zeros(4, dtype=torch.float64)),
+        "slopes_shape": dict(alibi_slopes=torch.zeros(2)),
+        "lse_shape": dict(lse=torch.zeros(2, 4, 9)),
+        "lse_dtype": dict(lse=torch.zeros(2, 4, 8, dtype=bf)),
+        "out_shape": dict(q_like=(("out", torch.zeros(2, 8, 4, 32, dtype=bf)),)),
+        "dout_dtype": dict(q_like=(("dout", torch.zeros(2, 8, 4, 64, dtype=f16)),)),
+        "o_missing": dict(q_like=(("o", None),)),
+        "packed_cu_int64": dict(packed, cu_seqlens=cu.to(torch.int64)),
+        "packed_cu_2d": dict(packed, cu_seqlens=cu.reshape(1, 3)),
+        "packed_no_max": dict(packed, max_seqlen=None),
+        "packed_zero_max": dict(packed, max_seqlen=0),
+        "packed_k_rows": dict(packed, k=torch.zeros(29, 2, 128, dtype=bf)),
+        "packed_lse_shape": dict(packed, lse=torch.zeros(4, 2, 20)),
+        "dense_given_3d": dict(q=torch.zeros(8, 4, 64, dtype=bf)),
+    }
+
+
+@pytest.mark.parametrize("name", sorted(_bad_cases()))
+def test_binding_validation_rejects(name):
+    with pytest.raises(ValueError):
+        _validate(**_val_case(**_bad_cases()[name]))
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+
+    q = torch.zeros(1, 8, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device"):
+        fa.attention(q, q, q)
+    with pytest.raises(ValueError, match="device"):
+        fa.attention_bwd(q, q, q, q, q, torch.zeros(1, 2, 8))

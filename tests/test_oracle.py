@@ -307,9 +307,25 @@ def pin_online_equals_two_pass(orc):
                   [0, 8, 16, n],  # uneven last tile
                   sorted(set([0, n] + list(rng.integers(1, n, size=5))))]
         for b in splits:
-            o, l = OA.online_head_fwd(q, k, v, 0.45, b, causal, slope)
-            np.testing.assert_allclose(o, o_ref, atol=1e-12)
-            np.testing.assert_allclose(l, l_ref, atol=1e-12)
+            for order in ("stream", "tree"):
+                o, l = OA.online_head_fwd(q, k, v, 0.45, b, causal, slope, order=order)
+                np.testing.assert_allclose(o, o_ref, atol=1e-12)
+                np.testing.assert_allclose(l, l_ref, atol=1e-12)
+
+
+def pin_merge_state_by_hand(orc):
+    """Two one-key states merged by hand: keys with scores 0 and ln 3 give weights 1/4 and 3/4."""
+    a = (np.array([0.0]), np.array([1.0]), np.array([[2.0, -4.0]]))
+    b = (np.array([math.log(3.0)]), np.array([1.0]), np.array([[6.0, 8.0]]))
+    for x, y in ((a, b), (b, a)):
+        m, ell, u = OA.merge_states(x, y)
+        np.testing.assert_allclose(m, [math.log(3.0)], atol=1e-15)
+        np.testing.assert_allclose(u / ell[:, None], [[0.25 * 2 + 0.75 * 6, 0.25 * -4 + 0.75 * 8]], atol=1e-14)
+        np.testing.assert_allclose(m + np.log(ell), [math.log(4.0)], atol=1e-15)
+    empty = (np.array([-np.inf]), np.array([0.0]), np.zeros((1, 2)))
+    for x, y in ((a, empty), (empty, a)):
+        m, ell, u = OA.merge_states(x, y)
+        assert m[0] == 0.0 and ell[0] == 1.0 and np.array_equal(u, a[2])
 
 
 def pin_rows_fwd(orc):

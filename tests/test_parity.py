@@ -35,14 +35,13 @@ for dt in ("bf16", "fp16"):
     for d in (64, 128):
         for causal in (False, True):
             for alibi in (False, True):
-                if dt == "fp16" and alibi:
-                    continue
                 FWD_SMALL.append(Workload(f"{dt}_d{d}_c{int(causal)}_a{int(alibi)}", dt, 2, 4, 2, 300, d,
                                           causal=causal, alibi=alibi, backward=False))
 for d in (64, 128):
     for causal in (False, True):
-        FWD_SMALL.append(Workload(f"fp32_d{d}_c{int(causal)}", "fp32", 2, 2, 1, 150, d, causal=causal,
-                                  alibi=causal, backward=False))
+        for alibi in (False, True):
+            FWD_SMALL.append(Workload(f"fp32_d{d}_c{int(causal)}_a{int(alibi)}", "fp32", 2, 2, 1, 150, d,
+                                      causal=causal, alibi=alibi, backward=False))
 
 
 @pytest.mark.parametrize("w", FWD_SMALL, ids=[w.name for w in FWD_SMALL])
@@ -84,24 +83,31 @@ def test_fwd_gpt2m_full():
     _banner(str(r))
 
 
-def _sample_rows(n, rng, extra=24):
-    base = [0, 1, 63, 64, 127, 128, n // 2, n - 129, n - 128, n - 65, n - 64, n - 2, n - 1]
-    return sorted(set([r for r in base if 0 <= r < n] + list(rng.integers(0, max(n, 1), size=extra))))
+FWD_TILE = 256  # query rows per forward workgroup
+
+
+def _tile_rows(n, rng):
+    """One random row in every FWD_TILE-row query tile of a length-n sequence, plus
+    the first and last rows of the sequence and of the last tile."""
+    rows = {0, n - 1, max(0, (n - 1) // FWD_TILE * FWD_TILE)}
+    for t0 in range(0, n, FWD_TILE):
+        rows.add(int(rng.integers(t0, min(n, t0 + FWD_TILE))))
+    return sorted(r for r in rows if 0 <= r < n)
 
 
 @pytest.mark.parametrize("name", ["long_causal", "gqa", "varlen_alibi"])
-def test_fwd_full_size_sampled(name):
+def test_fwd_full_size_every_tile(name):
+    """Full size, the benchmark's launch: at least one checked row in every
+    (sequence, query head, query tile) workgroup of the forward grid, so every
+    grid column (and with it every XCD) and every causal tile length is seen."""
     w = WORKLOADS[name]
     _banner(f"fwd full {name}")
     inp = make_inputs(w, 0, with_grad=False)
     o, lse = gpu_fwd(w, to_dev(inp))
     rng = np.random.default_rng(1)
     lens = (inp["cu_seqlens"][1:] - inp["cu_seqlens"][:-1]).tolist() if inp["cu_seqlens"] is not None else [w.N] * w.B
-    samples = []
-    for b in range(w.B):
-        for h in sorted(set([0, w.H - 1] + list(rng.integers(0, w.H, size=2)))):
-            samples.append((b, h, _sample_rows(lens[b], rng, extra=8 if w.B > 4 else 24)))
-    r = check_fwd_sampled(w, inp, o, lse, samples)
+    samples = [(b, h, _tile_rows(lens[b], rng)) for b in range(w.B) for h in range(w.H)]
+    r = check_fwd_sampled(w, inp, o, lse, samples, note="every (sequence, head, 256-row tile)")
     _banner(str(r))
 
 
@@ -136,8 +142,6 @@ for dt in ("bf16", "fp16"):
     for d in (64, 128):
         for causal in (False, True):
             for alibi in (False, True):
-                if dt == "fp16" and alibi:
-                    continue
                 BWD_SMALL.append(Workload(f"{dt}_d{d}_c{int(causal)}_a{int(alibi)}", dt, 2, 4, 2, 300, d,
                                           causal=causal, alibi=alibi))
 
@@ -176,10 +180,20 @@ def test_bwd_gpt2m_full():
     _banner(str(_bwd_case(WORKLOADS["gpt2m"])))
 
 
-@pytest.mark.parametrize("name,pairs", [("long_causal", [(0, 0), (0, 31)]), ("gqa", [(1, 5)])])
-def test_bwd_full_size_groups(name, pairs):
+# (sequence, kv head) groups checked in full at full size. The dK/dV grid has one
+# column per kv head and the dQ grid one per query head; workgroups go to the
+# eight XCDs by column mod 8, so these groups reach every XCD of both grids.
+BWD_FULL = {
+    "long_causal": [(0, g) for g in (0, 9, 18, 27, 4, 13, 22, 31)],
+    "gqa": [(0, 0), (1, 1), (0, 2), (1, 3), (0, 4), (1, 5), (0, 6), (1, 7)],
+}
+
+
+@pytest.mark.parametrize("name", sorted(BWD_FULL))
+def test_bwd_full_size_groups(name):
     """Full-size backward: whole (sequence, kv head) groups against the oracle."""
     w = WORKLOADS[name]
+    pairs = BWD_FULL[name]
     _banner(f"bwd full {name} {pairs}")
     inp = make_inputs(w, 0, with_grad=True)
     dinp = to_dev(inp)
