@@ -81,6 +81,23 @@ __device__ __forceinline__ uint4 ld_s16(const uint16_t* p) { return *reinterpret
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// acc + x0 + x1 for a packed pair of 16-bit values (x0, x1), with one v_dot2
+// against (1, 1): the products are exact and the sum is taken in fp32.
+template <typename T>
+__device__ __forceinline__ float add_pair(uint32_t pair, float acc);
+template <>
+__device__ __forceinline__ float add_pair<__bf16>(uint32_t pair, float acc) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), one, acc, false);
+}
+template <>
+__device__ __forceinline__ float add_pair<_Float16>(uint32_t pair, float acc) {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair), one, acc, false);
+}
+
 // Maximum / sum of x over lanes l and l ^ 32 with v_permlane32_swap (a
 // register exchange between the two halves of the wave, no LDS round trip).
 // Both lanes get the same value, with the same rounding.

@@ -28,15 +28,22 @@
 // transposed V operand comes from the transposing LDS read.
 //
 // Softmax bookkeeping. Scores are kept in log2 units (scale * log2(e) folded
-// into one FMA before exp2). The reference maximum m is only raised when a
-// tile's maximum exceeds it by more than TAU = 8 (a factor 256): P = 2^(t - m)
-// then stays below 256, which fp32 accumulators and the 16-bit P operand hold
-// with their usual relative precision, and the rescale of O and l is skipped
-// for almost every tile. The result is unchanged in exact arithmetic because
-// the final division uses sums taken against the same reference.
+// into one FMA before exp2). A tile that takes its row maximum raises the
+// reference m only when that maximum exceeds it by more than TAU = 8 (a factor
+// 256), so the rescale of O and l is skipped for almost every tile. Plain
+// tiles after the first take no maximum at all: P = 2^(t - m) is formed against
+// the current reference and the tile's row sum, computed anyway, shows whether
+// any P exceeded the bound the accumulators allow (then the tile is redone with
+// its maximum). P keeps the relative precision of its type at any magnitude, so
+// where the reference sits does not change the result, which is exact in real
+// arithmetic because the final division uses sums taken against the same
+// reference.
 //
 // Numerics: scores, sums and the O accumulator are fp32; P is rounded to the
-// input type for the second product; lse is converted back to natural log.
+// input type for the second product. O is divided by the sum of exactly those
+// rounded P values (so its weights sum to one and a row dominated by one key
+// reproduces that key's V), while lse uses the fp32 sum of the unrounded P and
+// is converted back to natural log.
 #include "fa_device.hpp"
 
 namespace fa {
@@ -46,6 +53,15 @@ constexpr int BR = 256;    // query rows per workgroup
 constexpr int BC = 128;    // keys per K/V tile
 constexpr int NT = 512;    // threads per workgroup (8 waves, two per SIMD)
 constexpr float TAU = 8.f; // lazy-rescale threshold, log2 units
+// Largest fp32 sum of one lane's 64 P values of a tile that the path without
+// a row maximum accepts. Every P is then at most this bound, which must fit the
+// 16-bit type P is rounded to for the second product: 2^32 for bf16 (the O
+// accumulator and the sums stay far inside fp32 range for any length) and
+// 2^15 for fp16 (largest finite value 65504).
+template <typename T>
+constexpr float sum_bound() {
+    return sizeof(T) == 2 && __is_same(T, _Float16) ? 32768.f : 4294967296.f;
+}
 
 template <typename T, int D, bool CAUSAL, bool ALIBI>
 __global__ __launch_bounds__(NT, 1) void fwd_mfma_kernel(Args a) {
@@ -118,7 +134,8 @@ __global__ __launch_bounds__(NT, 1) void fwd_mfma_kernel(Args a) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
     float m_ref = -INFINITY;  // reference max, log2 units (same in lanes l and l ^ 32)
-    float l_run = 0.f;        // this lane's share of the running sum
+    float l_run = 0.f;        // this lane's share of the running sum of P (fp32, for lse)
+    float l_rnd = 0.f;        // the same sum over P rounded to T (the weights the product uses)
 
     const float c2 = a.scale_log2;
     const float slope2 = ALIBI ? ld_uniform(a.slopes + h) * kLog2e : 0.f;
@@ -132,21 +149,42 @@ __global__ __launch_bounds__(NT, 1) void fwd_mfma_kernel(Args a) {
         // S^T = K Q^T for BC keys x 32 queries (raw, unscaled scores). The K
         // operand loads run two (kb, kk) groups ahead of the MFMAs; scheduling
         // barriers keep that order.
-        constexpr int NG1 = BC / 32 * D / 16;
         f32x16 s[BC / 32];
+        // (also written out inline for the first product below: with both as
+        // calls the register allocator spills the non-causal ALiBi instance)
+        auto score_product = [&]() {
+            constexpr int NG1 = BC / 32 * D / 16;
 #pragma unroll
-        for (int kb = 0; kb < BC / 32; ++kb) s[kb] = f32x16{};
-        uint4 fk[3];
-        auto load1 = [&](int gi) { fk[gi % 3] = ld_s16(Ks + 32 * (gi / (D / 16)) * D + roff[gi % (D / 16)]); };
-        load1(0);
-        load1(1);
+            for (int kb = 0; kb < BC / 32; ++kb) s[kb] = f32x16{};
+            uint4 fk[3];
+            auto load1 = [&](int gi) { fk[gi % 3] = ld_s16(Ks + 32 * (gi / (D / 16)) * D + roff[gi % (D / 16)]); };
+            load1(0);
+            load1(1);
 #pragma unroll
-        for (int gi = 0; gi < NG1; ++gi) {
-            if (gi + 2 < NG1) load1(gi + 2);
-            __builtin_amdgcn_sched_barrier(0);
-            const int kb = gi / (D / 16), kk = gi % (D / 16);
-            s[kb] = Mfma<T>::mma(as_v8<T>(fk[gi % 3]), qf[kk], s[kb]);
-            __builtin_amdgcn_sched_barrier(0);
+            for (int gi = 0; gi < NG1; ++gi) {
+                if (gi + 2 < NG1) load1(gi + 2);
+                __builtin_amdgcn_sched_barrier(0);
+                const int kb = gi / (D / 16), kk = gi % (D / 16);
+                s[kb] = Mfma<T>::mma(as_v8<T>(fk[gi % 3]), qf[kk], s[kb]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        {
+            constexpr int NG1 = BC / 32 * D / 16;
+#pragma unroll
+            for (int kb = 0; kb < BC / 32; ++kb) s[kb] = f32x16{};
+            uint4 fk[3];
+            auto load1 = [&](int gi) { fk[gi % 3] = ld_s16(Ks + 32 * (gi / (D / 16)) * D + roff[gi % (D / 16)]); };
+            load1(0);
+            load1(1);
+#pragma unroll
+            for (int gi = 0; gi < NG1; ++gi) {
+                if (gi + 2 < NG1) load1(gi + 2);
+                __builtin_amdgcn_sched_barrier(0);
+                const int kb = gi / (D / 16), kk = gi % (D / 16);
+                s[kb] = Mfma<T>::mma(as_v8<T>(fk[gi % 3]), qf[kk], s[kb]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
 
         // Scores in log2 units. Plain tiles keep the raw score and fold the
@@ -156,55 +194,85 @@ __global__ __launch_bounds__(NT, 1) void fwd_mfma_kernel(Args a) {
         // a negative scale reverses the score order: the max of raw scores
         // would be the wrong end, so such tiles materialise too
         const bool materialise = ALIBI || edge || !(c2 >= 0.f);
-        float mt;
-        if (materialise) {
-            mt = -INFINITY;
+        float ls = 0.f;
+
+        // Plain tiles after a wave's first tile skip the row maximum: P is taken
+        // against the current reference directly, and the fp32 row sum, which lse
+        // needs anyway, bounds every element of the lane's share. Only if some
+        // lane's sum exceeds sum_bound<T>() (or overflowed) does the wave recompute the
+        // scores and take the maximum path below for this tile. Every live wave
+        // starts at tile 0, which sets a finite reference in each of its rows.
+        bool need_max = true;
+        if constexpr (!ALIBI) {  // ALiBi tiles always materialise
+            need_max = materialise || kt == 0;
+            if (!need_max) {
+#pragma unroll
+                for (int kb = 0; kb < BC / 32; ++kb) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float p = exp2_fast(fmaf(s[kb][r], c2, -m_ref));
+                        s[kb][r] = p;
+                        ls += p;
+                    }
+                }
+                if (__any(!(ls <= sum_bound<T>()))) {
+                    score_product();
+                    need_max = true;
+                    ls = 0.f;
+                }
+            }
+        }
+        if (need_max) {
+            float mt;
+            if (materialise) {
+                mt = -INFINITY;
+#pragma unroll
+                for (int kb = 0; kb < BC / 32; ++kb) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * kg + (r & 3);
+                        float t = s[kb][r] * c2;
+                        if (ALIBI) {
+                            const float dist = (float)(qi - key);
+                            t -= slope2 * (CAUSAL ? dist : fabsf(dist));
+                        }
+                        if (edge && (key >= len || (CAUSAL && key > qi))) t = -INFINITY;
+                        s[kb][r] = t;
+                        mt = fmaxf(mt, t);
+                    }
+                }
+            } else {
+                float mx = s[0][0];
+#pragma unroll
+                for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+                mt = mx * c2;
+            }
+            mt = max_xor32(mt);
+
+            // lazy rescale: raise the reference only when the tile max exceeds it by > TAU
+            const bool raise = mt > m_ref + TAU;
+            if (__any(raise)) {
+                const float m_new = raise ? mt : m_ref;
+                const float alpha = exp2_fast(m_ref - m_new);  // 0 on the first tile
+                l_run *= alpha;
+                l_rnd *= alpha;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+                m_ref = m_new;
+            }
+            const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;  // rows with no key yet
+
+            const float sc = materialise ? 1.f : c2;
 #pragma unroll
             for (int kb = 0; kb < BC / 32; ++kb) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * kg + (r & 3);
-                    float t = s[kb][r] * c2;
-                    if (ALIBI) {
-                        const float dist = (float)(qi - key);
-                        t -= slope2 * (CAUSAL ? dist : fabsf(dist));
-                    }
-                    if (edge && (key >= len || (CAUSAL && key > qi))) t = -INFINITY;
-                    s[kb][r] = t;
-                    mt = fmaxf(mt, t);
+                    const float p = exp2_fast(fmaf(s[kb][r], sc, -m_use));
+                    s[kb][r] = p;
+                    ls += p;
                 }
-            }
-        } else {
-            float mx = s[0][0];
-#pragma unroll
-            for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-            mt = mx * c2;
-        }
-        mt = max_xor32(mt);
-
-        // lazy rescale: raise the reference only when the tile max exceeds it by > TAU
-        const bool raise = mt > m_ref + TAU;
-        if (__any(raise)) {
-            const float m_new = raise ? mt : m_ref;
-            const float alpha = exp2_fast(m_ref - m_new);  // 0 on the first tile
-            l_run *= alpha;
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
-            m_ref = m_new;
-        }
-        const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;  // rows with no key yet
-
-        const float sc = materialise ? 1.f : c2;
-        float ls = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < BC / 32; ++kb) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = exp2_fast(fmaf(s[kb][r], sc, -m_use));
-                s[kb][r] = p;
-                ls += p;
             }
         }
         l_run += ls;
@@ -217,6 +285,18 @@ __global__ __launch_bounds__(NT, 1) void fwd_mfma_kernel(Args a) {
             const int kb = c >> 1, r0 = 8 * (c & 1);
             pf[c] = pack8<T>(s[kb][r0 + 0], s[kb][r0 + 1], s[kb][r0 + 2], s[kb][r0 + 3], s[kb][r0 + 4],
                              s[kb][r0 + 5], s[kb][r0 + 6], s[kb][r0 + 7]);
+        }
+        {
+            float r0 = 0.f, r1 = 0.f;
+#pragma unroll
+            for (int c = 0; c < BC / 16; ++c) {
+                const uint4 u = __builtin_bit_cast(uint4, pf[c]);
+                r0 = add_pair<T>(u.x, r0);
+                r1 = add_pair<T>(u.y, r1);
+                r0 = add_pair<T>(u.z, r0);
+                r1 = add_pair<T>(u.w, r1);
+            }
+            l_rnd += r0 + r1;
         }
         uint4 fv[3];
         auto load2 = [&](int gi) {
@@ -239,10 +319,11 @@ __global__ __launch_bounds__(NT, 1) void fwd_mfma_kernel(Args a) {
 
     two_stage_loop(stA, stB, nkt, issue, compute);
 
-    // ---- epilogue: O = O_acc / l, lse = (m + log2 l) * ln 2
+    // ---- epilogue: O = O_acc / (sum of rounded P), lse = (m + log2 l) * ln 2
     const float l_tot = sum_xor32(l_run);
+    const float lr_tot = sum_xor32(l_rnd);
     if (qi < len) {
-        const float inv = 1.f / l_tot;
+        const float inv = 1.f / lr_tot;
         T* O = reinterpret_cast<T*>(a.out) + (size_t)row0 * ldq + (size_t)h * D + (size_t)qi * ldq;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
