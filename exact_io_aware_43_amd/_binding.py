@@ -42,6 +42,10 @@ def lib() -> ctypes.CDLL:
         L.fa_bwd.restype = ci
         L.fa_bwd_stages.argtypes = L.fa_bwd.argtypes[:-1] + [ctypes.c_uint, vp]
         L.fa_bwd_stages.restype = ci
+        L.fa_bwd_noalloc.argtypes = L.fa_bwd.argtypes[:-3] + [vp]
+        L.fa_bwd_noalloc.restype = ci
+        L.fa_bwd_noalloc_max_bytes.argtypes = []
+        L.fa_bwd_noalloc_max_bytes.restype = sz
         L.fa_strerror.argtypes = [ci]
         L.fa_strerror.restype = ctypes.c_char_p
         L.fa_version.argtypes = []
@@ -76,6 +80,17 @@ def fa_bwd_stages(q, k, v, o, dout, lse, dq, dk, dv, B, H, Hkv, N, d, scale, cau
     """``fa_bwd_stages``: a subset (bitmask of FA_BWD_*) of fa_bwd's launches."""
     return lib().fa_bwd_stages(q, k, v, o, dout, lse, dq, dk, dv, B, H, Hkv, N, d, scale, causal, alibi_slopes,
                                cu_seqlens, dtype, workspace, workspace_bytes, stages, stream)
+
+
+def fa_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, B, H, Hkv, N, d, scale, causal, alibi_slopes, cu_seqlens,
+                   dtype, stream) -> int:
+    """``fa_bwd_noalloc``: fa_bwd with the library's static per-GPU scratch instead of a workspace."""
+    return lib().fa_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, B, H, Hkv, N, d, scale, causal, alibi_slopes,
+                                cu_seqlens, dtype, stream)
+
+
+def fa_bwd_noalloc_max_bytes() -> int:
+    return lib().fa_bwd_noalloc_max_bytes()
 
 
 def fa_strerror(status: int) -> str:

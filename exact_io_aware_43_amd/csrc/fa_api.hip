@@ -3,6 +3,7 @@
 // before the first launch, so a rejected call enqueues and writes nothing.
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/fa.h"
 #include "fa_internal.hpp"
@@ -92,11 +93,14 @@ size_t fa_bwd_workspace_size(int B, int H, int Hkv, int N, int d, int causal, in
     return workspace_bytes_for(B, H, N);
 }
 
-int fa_bwd_stages(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
-                  void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d, float scale, int causal,
-                  const float* alibi_slopes, const int* cu_seqlens, fa_dtype dtype, void* workspace,
-                  size_t workspace_bytes, unsigned stages, void* stream) {
-    if (stages == 0 || (stages & ~(unsigned)FA_BWD_ALL) != 0) return FA_ERR_INVALID_ARG;
+}  // extern "C"
+
+namespace {
+
+// Argument checks of the backward entry points other than the workspace.
+int check_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+              void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d, float scale, int causal,
+              const float* alibi_slopes, const int* cu_seqlens, fa_dtype dtype) {
     if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
     int st = check_common(B, H, Hkv, N, d, scale, causal, (int)dtype);
     if (st != FA_OK) return st;
@@ -106,9 +110,36 @@ int fa_bwd_stages(const void* q, const void* k, const void* v, const void* o, co
         if (!aligned16(p)) return FA_ERR_INVALID_ARG;
     if ((alibi_slopes && !aligned16(alibi_slopes)) || (cu_seqlens && !aligned16(cu_seqlens)))
         return FA_ERR_INVALID_ARG;
-    if (!workspace || !aligned16(workspace) || workspace_bytes < workspace_bytes_for(B, H, N))
-        return FA_ERR_WORKSPACE;
+    return FA_OK;
+}
 
+// Backward workspace kept in the library for callers that cannot allocate
+// (fa_bwd_noalloc): one copy per GPU, held until the process ends. Host code
+// never uses the array's name as an address; each device's address comes from
+// hipGetSymbolAddress, taken once with that device current.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+int scratch_for_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_LAUNCH;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return FA_ERR_LAUNCH;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return FA_OK;
+}
+
+int bwd_launch(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+               void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d, float scale, int causal,
+               const float* alibi_slopes, const int* cu_seqlens, fa_dtype dtype, void* workspace, unsigned stages,
+               void* stream) {
     fa::Args a = make_args(q, k, v, B, H, Hkv, N, scale, alibi_slopes, cu_seqlens);
     a.o = o;
     a.dout = dout;
@@ -122,6 +153,41 @@ int fa_bwd_stages(const void* q, const void* k, const void* v, const void* o, co
                                   reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
+
+}  // namespace
+
+extern "C" {
+
+int fa_bwd_stages(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                  void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d, float scale, int causal,
+                  const float* alibi_slopes, const int* cu_seqlens, fa_dtype dtype, void* workspace,
+                  size_t workspace_bytes, unsigned stages, void* stream) {
+    if (stages == 0 || (stages & ~(unsigned)FA_BWD_ALL) != 0) return FA_ERR_INVALID_ARG;
+    int st = check_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, Hkv, N, d, scale, causal, alibi_slopes, cu_seqlens,
+                       dtype);
+    if (st != FA_OK) return st;
+    if (!workspace || !aligned16(workspace) || workspace_bytes < workspace_bytes_for(B, H, N))
+        return FA_ERR_WORKSPACE;
+
+    return bwd_launch(q, k, v, o, dout, lse, dq, dk, dv, B, H, Hkv, N, d, scale, causal, alibi_slopes, cu_seqlens,
+                      dtype, workspace, stages, stream);
+}
+
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                   void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d, float scale, int causal,
+                   const float* alibi_slopes, const int* cu_seqlens, fa_dtype dtype, void* stream) {
+    int st = check_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, Hkv, N, d, scale, causal, alibi_slopes, cu_seqlens,
+                       dtype);
+    if (st != FA_OK) return st;
+    if (workspace_bytes_for(B, H, N) > kScratchBytes) return FA_ERR_SCRATCH;
+    void* ws = nullptr;
+    st = scratch_for_current_device(&ws);
+    if (st != FA_OK) return st;
+    return bwd_launch(q, k, v, o, dout, lse, dq, dk, dv, B, H, Hkv, N, d, scale, causal, alibi_slopes, cu_seqlens,
+                      dtype, ws, FA_BWD_ALL, stream);
+}
+
+size_t fa_bwd_noalloc_max_bytes(void) { return kScratchBytes; }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse, void* dq,
            void* dk, void* dv, int B, int H, int Hkv, int N, int d, float scale, int causal,
@@ -138,6 +204,7 @@ const char* fa_strerror(int status) {
         case FA_ERR_UNSUPPORTED: return "unsupported configuration (head dim must be 64 or 128; fp32 is forward only)";
         case FA_ERR_WORKSPACE: return "workspace missing, misaligned or smaller than fa_bwd_workspace_size()";
         case FA_ERR_LAUNCH: return "kernel launch failed";
+        case FA_ERR_SCRATCH: return "problem needs more backward scratch than fa_bwd_noalloc holds (fa_bwd_noalloc_max_bytes())";
         default: return "unknown status";
     }
 }

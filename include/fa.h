@@ -39,8 +39,9 @@
  * library never allocates, frees or synchronises; all work is enqueued on
  * `stream` (a hipStream_t, NULL for the default stream) and the call returns
  * at once. Inputs are read-only; outputs must not alias inputs or each other.
- * Base pointers must be 16-byte aligned. The library keeps no mutable global
- * state, so concurrent calls from several host threads are safe.
+ * Base pointers must be 16-byte aligned. Apart from fa_bwd_noalloc's scratch
+ * (see there) the library keeps no mutable global state, so concurrent calls
+ * from several host threads are safe.
  *
  * Errors: every entry returns FA_OK (0) or a negative fa_status. All argument
  * checks run before any launch; a call that fails them enqueues nothing and
@@ -66,7 +67,8 @@ typedef enum fa_status {
     FA_ERR_INVALID_ARG = -1, /* null pointer, bad size, H % Hkv != 0, non-finite scale, misalignment */
     FA_ERR_UNSUPPORTED = -2, /* head dim not in {64, 128}; fp32 backward */
     FA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than fa_bwd_workspace_size() */
-    FA_ERR_LAUNCH = -4       /* the kernel launch itself failed */
+    FA_ERR_LAUNCH = -4,      /* the kernel launch itself failed */
+    FA_ERR_SCRATCH = -5      /* fa_bwd_noalloc: problem larger than its built-in scratch */
 } fa_status;
 
 /*
@@ -137,6 +139,31 @@ int fa_bwd_stages(const void* q, const void* k, const void* v, const void* o,
                   const float* alibi_slopes, const int* cu_seqlens, fa_dtype dtype,
                   void* workspace, size_t workspace_bytes, unsigned stages,
                   void* stream);
+
+/*
+ * fa_bwd without the workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc. Same arguments, checks, results and errors as fa_bwd
+ * otherwise. The scratch (D and the rescaled row statistic, the same bytes
+ * fa_bwd_workspace_size reports) lives in a static device array inside the
+ * library: one copy per GPU of fa_bwd_noalloc_max_bytes() = 16 MiB, held until
+ * the process ends, i.e. problems with 8 * B * H * N64 <= 16 MiB (N64 = N
+ * rounded up to 64); larger ones return FA_ERR_SCRATCH before any launch.
+ * The call allocates and frees nothing; the first call on each device looks up
+ * that device's copy of the array once (hipGetSymbolAddress, under a lock).
+ * Every call on one GPU uses the same array: calls that overlap in time on one
+ * GPU (different streams, or several host threads without ordering) race and
+ * must be serialised by the caller. Nothing in the array needs to start at
+ * zero: each call writes every entry it reads before reading it.
+ */
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                   int B, int H, int Hkv, int N, int d, float scale, int causal,
+                   const float* alibi_slopes, const int* cu_seqlens, fa_dtype dtype,
+                   void* stream);
+
+/* Size in bytes of fa_bwd_noalloc's per-GPU scratch array. */
+size_t fa_bwd_noalloc_max_bytes(void);
 
 /* Static, human-readable text for a status code (never NULL, never freed). */
 const char* fa_strerror(int status);

@@ -30,7 +30,8 @@ def declared_functions():
 
 def test_header_declares_expected_api():
     assert declared_functions() == sorted(
-        ["fa_fwd", "fa_bwd", "fa_bwd_stages", "fa_bwd_workspace_size", "fa_strerror", "fa_version"])
+        ["fa_fwd", "fa_bwd", "fa_bwd_stages", "fa_bwd_workspace_size", "fa_bwd_noalloc", "fa_bwd_noalloc_max_bytes",
+         "fa_strerror", "fa_version"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -44,7 +45,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_strerror():
     assert fa.fa_version() == 10000
-    for code in (OK, INVALID, UNSUPPORTED, WORKSPACE, -4):
+    for code in (OK, INVALID, UNSUPPORTED, WORKSPACE, -4, -5):
         s = fa.fa_strerror(code)
         assert s and s != "unknown status"
     assert fa.fa_strerror(123) == "unknown status"
@@ -209,3 +210,26 @@ def test_binding_refuses_host_tensors():
         fa.attention(q, q, q)
     with pytest.raises(ValueError, match="device"):
         fa.attention_bwd(q, q, q, q, q, torch.zeros(1, 2, 8))
+
+
+def _noalloc(**kw):
+    a = dict(q=PTR[0], k=PTR[1], v=PTR[2], o=PTR[3], do=PTR[4], lse=PTR[5], dq=PTR[6], dk=PTR[7], dv=PTR[8],
+             B=2, H=4, Hkv=2, N=64, d=64, scale=0.125, causal=1, alibi=None, cu=None, dtype=fa.FA_BF16, stream=None)
+    a.update(kw)
+    return fa.fa_bwd_noalloc(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"], a["B"],
+                             a["H"], a["Hkv"], a["N"], a["d"], a["scale"], a["causal"], a["alibi"], a["cu"],
+                             a["dtype"], a["stream"])
+
+
+def test_noalloc_scratch_size():
+    assert fa.fa_bwd_noalloc_max_bytes() == 16 << 20
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), INVALID), (dict(dv=None), INVALID), (dict(H=3), INVALID), (dict(causal=2), INVALID),
+    (dict(dtype=fa.FA_FP32), UNSUPPORTED), (dict(d=32), UNSUPPORTED), (dict(dk=PTR[7] + 8), INVALID),
+    # 8 bytes per (sequence, head, position) above the 16 MiB scratch: rejected before any device call
+    (dict(B=1, H=64, Hkv=64, N=32768 + 1), -5), (dict(B=4, H=32, Hkv=8, N=16384 + 64), -5),
+])
+def test_noalloc_rejects(kw, expect):
+    assert _noalloc(**kw) == expect
