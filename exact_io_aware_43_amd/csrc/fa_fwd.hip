@@ -125,7 +125,15 @@ __global__ __launch_bounds__(NT, 1) void fwd_mfma_kernel(Args a) {
 
     DmaTile<D, BC, NT / 64> dma;
     dma.init(wave, lane, ldk);
-    auto issue = [&](uint16_t* st, int kt) {
+    // With ALiBi, key tiles are visited from the last (the diagonal one under
+    // the causal mask) down to the first: the bias falls with distance, so the
+    // tile of a row's nearest keys holds its largest scores, and the maximum
+    // taken on that first tile bounds every later one (ascending, each tile
+    // would exceed the last and force the maximum path every time). Without a
+    // bias the plain ascending order is kept.
+    auto tile_of = [&](int it) { return ALIBI ? nkt - 1 - it : it; };
+    auto issue = [&](uint16_t* st, int it) {
+        const int kt = tile_of(it);
         dma.issue(st, reinterpret_cast<const uint16_t*>(Kg), kt * BC, len, wave);
         dma.issue(st + TILE, reinterpret_cast<const uint16_t*>(Vg), kt * BC, len, wave);
     };
@@ -140,7 +148,9 @@ __global__ __launch_bounds__(NT, 1) void fwd_mfma_kernel(Args a) {
     const float c2 = a.scale_log2;
     const float slope2 = ALIBI ? ld_uniform(a.slopes + h) * kLog2e : 0.f;
 
-    auto compute = [&](const uint16_t* Ks, int kt) {
+    bool fresh = true;  // wave-uniform: no tile of this wave processed yet
+    auto compute = [&](const uint16_t* Ks, int it) {
+        const int kt = tile_of(it);
         const uint16_t* Vs = Ks + TILE;
         const int k0 = kt * BC;
         // wave-uniform: skip tiles that are entirely above this wave's diagonal
@@ -187,42 +197,60 @@ __global__ __launch_bounds__(NT, 1) void fwd_mfma_kernel(Args a) {
             }
         }
 
-        // Scores in log2 units. Plain tiles keep the raw score and fold the
-        // scale into the exponent's FMA; ALiBi, edge and negative-scale tiles materialise
-        // t = s * c2 + bias (or -inf when masked) and use scale 1 below.
+        // Scores in log2 units: t = s * scale * log2(e) + bias. The ALiBi bias
+        // -slope |i - j| is slope2 * (key - qi) on keys at or before the query and
+        // slope2 * (qi - key) after it. Element (kb, r) of this lane has
+        // key - qi = lin + off(kb, r) with lin = k0 + 4 kg - qi per tile and the
+        // compile-time off = 32 kb + 8 (r / 4) + r % 4.
         const bool edge = (k0 + BC > len) || (CAUSAL && k0 + BC - 1 > qw);
-        // a negative scale reverses the score order: the max of raw scores
-        // would be the wrong end, so such tiles materialise too
-        const bool materialise = ALIBI || edge || !(c2 >= 0.f);
+        const bool below = k0 + BC - 1 <= qw;  // every key <= every query of the wave
+        const bool above = k0 >= qw + 31;      // every key >= every query of the wave
+        const float lin = (float)(k0 + 4 * kg - qi);
+        auto off = [](int kb, int r) { return (float)(32 * kb + 8 * (r >> 2) + (r & 3)); };
         float ls = 0.f;
 
-        // Plain tiles after a wave's first tile skip the row maximum: P is taken
+        // Plain tiles after a wave's first tile take no row maximum: P is formed
         // against the current reference directly, and the fp32 row sum, which lse
         // needs anyway, bounds every element of the lane's share. Only if some
-        // lane's sum exceeds sum_bound<T>() (or overflowed) does the wave recompute the
-        // scores and take the maximum path below for this tile. Every live wave
-        // starts at tile 0, which sets a finite reference in each of its rows.
+        // lane's sum exceeds sum_bound<T>() (or overflowed) does the wave recompute
+        // the scores and take the maximum path for this tile. A wave's first tile
+        // always takes the maximum path; every row of a live wave sees at least
+        // one key of every tile it visits (causal: key k0 <= its query), so that
+        // sets a finite reference in each row.
+        // ALiBi tiles qualify when the bias is linear in the key over the whole
+        // tile (no key on both sides of any of the wave's queries).
         bool need_max = true;
-        if constexpr (!ALIBI) {  // ALiBi tiles always materialise
-            need_max = materialise || kt == 0;
-            if (!need_max) {
+        // (in ascending order, without ALiBi, a wave's first tile is tile 0)
+        const bool first = ALIBI ? fresh : kt == 0;
+        if (!first && !edge && (!ALIBI || below || above)) {
+            need_max = false;
+            const float sl = ALIBI ? (below ? slope2 : -slope2) : 0.f;
+            const float base = ALIBI ? fmaf(sl, lin, -m_ref) : -m_ref;
 #pragma unroll
-                for (int kb = 0; kb < BC / 32; ++kb) {
+            for (int kb = 0; kb < BC / 32; ++kb) {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const float p = exp2_fast(fmaf(s[kb][r], c2, -m_ref));
-                        s[kb][r] = p;
-                        ls += p;
-                    }
-                }
-                if (__any(!(ls <= sum_bound<T>()))) {
-                    score_product();
-                    need_max = true;
-                    ls = 0.f;
+                for (int r = 0; r < 16; ++r) {
+                    float t = fmaf(s[kb][r], c2, base);
+                    if (ALIBI) t = fmaf(sl, off(kb, r), t);
+                    const float p = exp2_fast(t);
+                    s[kb][r] = p;
+                    ls += p;
                 }
             }
+            if (__any(!(ls <= sum_bound<T>()))) {
+                score_product();
+                need_max = true;
+                ls = 0.f;
+            }
         }
+        // Maximum path: t materialised (masked keys -inf), tile maximum, lazy
+        // raise of the reference. (One body with a run-time mask test: separate
+        // masked and unmasked copies make the register allocator spill.)
         if (need_max) {
+            // Unmasked tiles without a bias keep raw scores (the scale goes into
+            // the exponent's FMA); a negative scale reverses the order of raw
+            // scores, so it materialises like the others.
+            const bool materialise = ALIBI || edge || !(c2 >= 0.f);
             float mt;
             if (materialise) {
                 mt = -INFINITY;
@@ -230,12 +258,12 @@ __global__ __launch_bounds__(NT, 1) void fwd_mfma_kernel(Args a) {
                 for (int kb = 0; kb < BC / 32; ++kb) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * kg + (r & 3);
                         float t = s[kb][r] * c2;
                         if (ALIBI) {
-                            const float dist = (float)(qi - key);
-                            t -= slope2 * (CAUSAL ? dist : fabsf(dist));
+                            const float d = lin + off(kb, r);  // key - qi, exact in fp32
+                            t = fmaf(slope2, CAUSAL ? d : -fabsf(d), t);
                         }
+                        const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * kg + (r & 3);
                         if (edge && (key >= len || (CAUSAL && key > qi))) t = -INFINITY;
                         s[kb][r] = t;
                         mt = fmaxf(mt, t);
@@ -263,7 +291,6 @@ __global__ __launch_bounds__(NT, 1) void fwd_mfma_kernel(Args a) {
                 m_ref = m_new;
             }
             const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;  // rows with no key yet
-
             const float sc = materialise ? 1.f : c2;
 #pragma unroll
             for (int kb = 0; kb < BC / 32; ++kb) {
@@ -276,6 +303,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_mfma_kernel(Args a) {
             }
         }
         l_run += ls;
+        if (ALIBI) fresh = false;
 
         // O^T += V^T P^T, 16 keys per MFMA; transposed V loads two groups ahead
         constexpr int NG2 = BC / 16 * D / 32;
