@@ -48,6 +48,12 @@ the design notes of the repository):
    inputs; entries past a sequence's length are NaN here.
 7. A masked score contributes exactly zero; exp(-inf - (-inf)) never occurs in
    the two-pass form because every causal row keeps its diagonal.
+8. Dropout ([PN] Key design 1 stage table: the fused operator drops attention
+   probabilities and the backward regenerates them from the saved generator
+   state, Key design 3): the softmax and lse use every score; the
+   probabilities that multiply V are dropped with a counter-based mask and the
+   kept ones scaled so their expectation is unchanged. The mask is defined in
+   oracle/philox.py.
 """
 
 from __future__ import annotations
@@ -55,6 +61,8 @@ from __future__ import annotations
 import math
 
 import numpy as np
+
+from . import philox as PX
 
 __all__ = [
     "attention_fwd",
@@ -105,9 +113,15 @@ def _softmax_rows(s):
     return e / ell[:, None], m + np.log(ell)
 
 
-def head_fwd(qh, kh, vh, scale, causal=False, slope=None):
-    """One (sequence, head): O = softmax(S) V and lse. Arrays are [n, d] fp64."""
+def head_fwd(qh, kh, vh, scale, causal=False, slope=None, keep=None, keep_scale=1.0):
+    """One (sequence, head): O = softmax(S) V and lse. Arrays are [n, d] fp64.
+
+    With a dropout mask ``keep`` [n, n] (boolean), O = (P o keep * keep_scale) V:
+    the softmax and lse use every score; dropout acts on the probabilities
+    that multiply V ([PN] Key design 1 stage table)."""
     p, lse = _softmax_rows(_scores(qh, kh, scale, causal, slope))
+    if keep is not None:
+        p = np.where(keep, p * keep_scale, 0.0)
     return p @ vh, lse
 
 
@@ -122,15 +136,20 @@ def head_rows_fwd(qh, kh, vh, rows, scale, causal=False, slope=None):
     return p @ vh, lse
 
 
-def head_bwd(qh, kh, vh, doh, scale, causal=False, slope=None):
+def head_bwd(qh, kh, vh, doh, scale, causal=False, slope=None, keep=None, keep_scale=1.0):
     """Gradients of sum(O * dO) for one (sequence, head), by recomputing P ([PN] Key design 3).
 
     D_i is taken from its definition sum_j P_ij dP_ij; the identity D_i = dO_i . O_i
-    stated on the page is checked by the tests, not assumed here.
+    stated on the page is checked by the tests, not assumed here. With a dropout
+    mask, O = (P o keep * keep_scale) V, so dV uses the dropped probabilities and
+    the gradient reaching P is (dO V^T) o keep * keep_scale.
     """
     p, _ = _softmax_rows(_scores(qh, kh, scale, causal, slope))
-    dv = p.T @ doh
+    pd = p if keep is None else np.where(keep, p * keep_scale, 0.0)
+    dv = pd.T @ doh
     dp = doh @ vh.T
+    if keep is not None:
+        dp = np.where(keep, dp * keep_scale, 0.0)
     dcorr = (p * dp).sum(axis=1)
     ds = p * (dp - dcorr[:, None])
     dq = scale * (ds @ kh)
@@ -157,12 +176,22 @@ def _heads(q, k):
     return H, Hkv, H // Hkv
 
 
-def attention_fwd(q, k, v, scale=None, causal=False, alibi_slopes=None, cu_seqlens=None):
+def _dropout(dropout, n, b, h, H):
+    """(keep mask, keep scale) of (sequence b, head h) for dropout=(p_drop, seed, offset), or (None, 1)."""
+    if dropout is None:
+        return None, 1.0
+    p_drop, seed, offset = dropout
+    K = PX.keep_threshold(p_drop)
+    return PX.dropout_keep(n, n, b, h, H, seed, offset, K), 256.0 / K
+
+
+def attention_fwd(q, k, v, scale=None, causal=False, alibi_slopes=None, cu_seqlens=None, dropout=None):
     """Exact attention forward in fp64.
 
     Dense: q [B, N, H, d], k and v [B, N, Hkv, d]. Packed (``cu_seqlens`` given):
     q [T, H, d], k and v [T, Hkv, d]. Returns (o, lse): o in q's layout, lse
-    [B, H, Nmax] (NaN past each sequence's end).
+    [B, H, Nmax] (NaN past each sequence's end). ``dropout`` = (p_drop, seed,
+    offset) applies the mask defined in oracle/philox.py.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     H, Hkv, G = _heads(q, k)
@@ -178,14 +207,15 @@ def attention_fwd(q, k, v, scale=None, causal=False, alibi_slopes=None, cu_seqle
             continue
         for h in range(H):
             g = h // G
+            keep, ks = _dropout(dropout, n, b, h, H)
             oh, lh = head_fwd(q[idx][:, h], k[idx][:, g], v[idx][:, g], scale, causal,
-                              None if slopes is None else slopes[h])
+                              None if slopes is None else slopes[h], keep, ks)
             o[idx + (h,)] = oh
             lse[b, h, :n] = lh
     return o, lse
 
 
-def attention_bwd(q, k, v, do, scale=None, causal=False, alibi_slopes=None, cu_seqlens=None):
+def attention_bwd(q, k, v, do, scale=None, causal=False, alibi_slopes=None, cu_seqlens=None, dropout=None):
     """Exact attention backward in fp64: (dq, dk, dv) of the loss sum(O * dO).
 
     Layouts as in :func:`attention_fwd`. dk and dv of a kv head sum over its
@@ -202,8 +232,9 @@ def attention_bwd(q, k, v, do, scale=None, causal=False, alibi_slopes=None, cu_s
             continue
         for h in range(H):
             g = h // G
+            keep, ks = _dropout(dropout, n, b, h, H)
             gq, gk, gv = head_bwd(q[idx][:, h], k[idx][:, g], v[idx][:, g], do[idx][:, h], scale,
-                                  causal, None if slopes is None else slopes[h])
+                                  causal, None if slopes is None else slopes[h], keep, ks)
             dq[idx + (h,)] = gq
             dk[idx + (g,)] += gk
             dv[idx + (g,)] += gv
@@ -272,7 +303,7 @@ def online_head_fwd(qh, kh, vh, scale, bounds, causal=False, slope=None, order="
     return u / ell[:, None], m + np.log(ell)
 
 
-def brute_fwd(q, k, v, scale=None, causal=False, alibi_slopes=None, cu_seqlens=None):
+def brute_fwd(q, k, v, scale=None, causal=False, alibi_slopes=None, cu_seqlens=None, dropout=None):
     """Scalar-loop attention with textbook softmax, for tiny inputs (N <= 8).
 
     Pure Python: nested lists, ``math.exp`` and running sums, no BLAS and no
@@ -294,6 +325,7 @@ def brute_fwd(q, k, v, scale=None, causal=False, alibi_slopes=None, cu_seqlens=N
         o_seq = o[idx]  # basic slicing: a view into o
         for h in range(H):
             g = h // G
+            keep, kscale = _dropout(dropout, n, b, h, H)
             for i in range(n):
                 keys = range(i + 1) if causal else range(n)
                 w = []
@@ -308,8 +340,9 @@ def brute_fwd(q, k, v, scale=None, causal=False, alibi_slopes=None, cu_seqlens=N
                 z = sum(w)
                 out = [0.0] * len(vs[0][g]) if n else []
                 for wj, j in zip(w, keys):
+                    f = 1.0 if keep is None else (kscale if keep[i, j] else 0.0)
                     for c in range(len(out)):
-                        out[c] += wj / z * vs[j][g][c]
+                        out[c] += f * wj / z * vs[j][g][c]
                 o_seq[i, h] = out
                 lse[b, h, i] = math.log(z)
     return o, lse

@@ -401,20 +401,20 @@ def _m_softmax_no_max_in_lse(s):
     return p, lse - s.max(axis=1)
 
 
-def _m_head_bwd_no_scale(qh, kh, vh, doh, scale, causal=False, slope=None):
-    dq, dk, dv = OA.head_bwd(qh, kh, vh, doh, scale, causal, slope)
+def _m_head_bwd_no_scale(qh, kh, vh, doh, scale, causal=False, slope=None, keep=None, keep_scale=1.0):
+    dq, dk, dv = OA.head_bwd(qh, kh, vh, doh, scale, causal, slope, keep, keep_scale)
     return dq / scale, dk, dv
 
 
-def _m_head_bwd_ds_sign(qh, kh, vh, doh, scale, causal=False, slope=None):
+def _m_head_bwd_ds_sign(qh, kh, vh, doh, scale, causal=False, slope=None, keep=None, keep_scale=1.0):
     p, _ = OA._softmax_rows(OA._scores(qh, kh, scale, causal, slope))
     dp = doh @ vh.T
     ds = p * (dp + (p * dp).sum(axis=1)[:, None])
     return scale * ds @ kh, scale * ds.T @ qh, p.T @ doh
 
 
-def _m_head_bwd_dv_untransposed(qh, kh, vh, doh, scale, causal=False, slope=None):
-    dq, dk, _ = OA.head_bwd(qh, kh, vh, doh, scale, causal, slope)
+def _m_head_bwd_dv_untransposed(qh, kh, vh, doh, scale, causal=False, slope=None, keep=None, keep_scale=1.0):
+    dq, dk, _ = OA.head_bwd(qh, kh, vh, doh, scale, causal, slope, keep, keep_scale)
     p, _ = OA._softmax_rows(OA._scores(qh, kh, scale, causal, slope))
     return dq, dk, p @ doh
 
