@@ -82,6 +82,8 @@ def parse():
     ap.add_argument("--no-telemetry", action="store_true",
                     help="skip the amd-smi reading under load (profiling runs: keeps the trace to the timed work)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--dropout", type=float, default=0.0,
+                    help="drop probability of the fused dropout (fa_fwd_dropout / fa_bwd_dropout); 0 = none")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the measurement run a plain 1 GiB fp32 copy (negation) for counter calibration")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -140,16 +142,25 @@ def main():
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     P = lambda t: None if t is None else t.data_ptr()  # noqa: E731
 
+    drop = args.dropout
+    fargs = lambda: (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, Hkv, N, d,  # noqa
+                     scale, causal, P(slopes), P(cu), dt)
+
     def fwd():
-        st = fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, Hkv, N, d,
-                       scale, causal, P(slopes), P(cu), dt, sh)
+        if drop:
+            st = fa.fa_fwd_dropout(*fargs(), drop, args.seed + 1, 0, sh)
+        else:
+            st = fa.fa_fwd(*fargs(), sh)
         if st:
             raise fa.FaError(st)
 
     def bwd(stages=fa.FA_BWD_ALL):
-        st = fa.fa_bwd_stages(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
-                              lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, N, d, scale,
-                              causal, P(slopes), P(cu), dt, ws.data_ptr(), ws_bytes, stages, sh)
+        a_ = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(), dq.data_ptr(),
+              dk.data_ptr(), dv.data_ptr(), B, H, Hkv, N, d, scale, causal, P(slopes), P(cu), dt)
+        if drop:  # the dropout backward runs its three launches as one call
+            st = fa.fa_bwd_dropout(*a_, drop, args.seed + 1, 0, ws.data_ptr(), ws_bytes, sh)
+        else:
+            st = fa.fa_bwd_stages(*a_, ws.data_ptr(), ws_bytes, stages, sh)
         if st:
             raise fa.FaError(st)
 
@@ -220,8 +231,11 @@ def main():
         "bwd_dkdv": 2 * qb + 4 * kvb + 2 * vec,       # Q, dO, K, V, D, L in; dK, dV out
         "bwd_dq": 3 * qb + 2 * kvb + 2 * vec,         # Q, dO, K, V, D, L in; dQ out
     }
+    alg_bytes["bwd"] = alg_bytes["bwd_dsum"] + alg_bytes["bwd_dkdv"] + alg_bytes["bwd_dq"]  # the three launches
     kernels = {"fwd": dict(ms=time_launches(fwd, "fwd"), work=f_fwd, bound="mfma")}
-    if has_bwd:
+    if has_bwd and drop:
+        kernels["bwd"] = dict(ms=time_launches(bwd, "bwd"), work=2.5 * f_fwd, bound="mfma")
+    elif has_bwd:
         kernels.update({
             "bwd_dsum": dict(ms=time_launches(lambda: bwd(fa.FA_BWD_PREP), "bwd_dsum"), work=dsum_bytes,
                              bound="hbm"),
@@ -304,10 +318,11 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "H": H, "Hkv": Hkv, "N": N, "d": d, "causal": bool(w.causal),
                    "alibi": bool(w.alibi), "pass": "forward+backward" if has_bwd else "forward",
-                   **({"sequences": len(lens), "tokens": int(T)} if cu is not None else {})},
+                   **({"sequences": len(lens), "tokens": int(T)} if cu is not None else {}),
+                   **({"dropout": drop} if drop else {})},
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "fwd_tflops": round(f_fwd / (kernels["fwd"]["ms"] * 1e-3) / 1e12, 2),
-        "bwd_tflops": (round(f_bwd / (sum(kernels[n]["ms"] for n in ("bwd_dsum", "bwd_dkdv", "bwd_dq")) * 1e-3)
+        "bwd_tflops": (round(f_bwd / (sum(kr["ms"] for n, kr in kernels.items() if n.startswith("bwd")) * 1e-3)
                              / 1e12, 2) if has_bwd else None),
         "kernels": {n: {"ms": round(kr["ms"], 4), "achieved": round(kr["achieved"], 2), "unit": kr["unit"],
                         "frac": round(kr["frac"], 4),

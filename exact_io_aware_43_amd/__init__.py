@@ -20,6 +20,8 @@ from ._binding import (  # noqa: F401
     attention,
     attention_bwd,
     fa_bwd,
+    fa_bwd_dropout,
+    fa_fwd_dropout,
     fa_bwd_noalloc,
     fa_bwd_noalloc_max_bytes,
     fa_bwd_stages,

@@ -42,6 +42,11 @@ def lib() -> ctypes.CDLL:
         L.fa_bwd.restype = ci
         L.fa_bwd_stages.argtypes = L.fa_bwd.argtypes[:-1] + [ctypes.c_uint, vp]
         L.fa_bwd_stages.restype = ci
+        u64, u32 = ctypes.c_ulonglong, ctypes.c_uint
+        L.fa_fwd_dropout.argtypes = L.fa_fwd.argtypes[:-1] + [cf, u64, u32, vp]
+        L.fa_fwd_dropout.restype = ci
+        L.fa_bwd_dropout.argtypes = L.fa_bwd.argtypes[:-3] + [cf, u64, u32, vp, sz, vp]
+        L.fa_bwd_dropout.restype = ci
         L.fa_bwd_noalloc.argtypes = L.fa_bwd.argtypes[:-3] + [vp]
         L.fa_bwd_noalloc.restype = ci
         L.fa_bwd_noalloc_max_bytes.argtypes = []
@@ -59,6 +64,20 @@ def lib() -> ctypes.CDLL:
 def fa_fwd(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, alibi_slopes, cu_seqlens, dtype, stream) -> int:
     """``fa_fwd`` with integer device pointers (or None for NULL); returns the status."""
     return lib().fa_fwd(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, alibi_slopes, cu_seqlens, dtype, stream)
+
+
+def fa_fwd_dropout(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, alibi_slopes, cu_seqlens, dtype, p_drop, seed,
+                   offset, stream) -> int:
+    """``fa_fwd_dropout`` with integer device pointers (or None for NULL); returns the status."""
+    return lib().fa_fwd_dropout(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, alibi_slopes, cu_seqlens, dtype,
+                                p_drop, seed, offset, stream)
+
+
+def fa_bwd_dropout(q, k, v, o, dout, lse, dq, dk, dv, B, H, Hkv, N, d, scale, causal, alibi_slopes, cu_seqlens,
+                   dtype, p_drop, seed, offset, workspace, workspace_bytes, stream) -> int:
+    """``fa_bwd_dropout`` with integer device pointers (or None for NULL); returns the status."""
+    return lib().fa_bwd_dropout(q, k, v, o, dout, lse, dq, dk, dv, B, H, Hkv, N, d, scale, causal, alibi_slopes,
+                                cu_seqlens, dtype, p_drop, seed, offset, workspace, workspace_bytes, stream)
 
 
 def fa_bwd_workspace_size(B, H, Hkv, N, d, causal, varlen, dtype) -> int:
@@ -198,20 +217,26 @@ def validate(q, k, v, *, cu_seqlens=None, max_seqlen=None, alibi_slopes=None, q_
 def attention(q, k, v, causal: bool = False, softmax_scale: Optional[float] = None,
               alibi_slopes: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None,
               max_seqlen: Optional[int] = None, out: Optional[torch.Tensor] = None,
-              lse: Optional[torch.Tensor] = None):
-    """Exact attention forward through ``fa_fwd``: returns (o, lse).
+              lse: Optional[torch.Tensor] = None, dropout_p: float = 0.0, seed: int = 0, offset: int = 0):
+    """Exact attention forward through ``fa_fwd`` (``fa_fwd_dropout`` when
+    ``dropout_p`` > 0): returns (o, lse).
 
-    Mirrors ``flash_attn_func(q, k, v, softmax_scale=None, causal=...)`` (no
-    dropout). ``lse`` is fp32 [B, H, N] (N = max_seqlen for packed inputs).
-    Every tensor is validated against the layouts of the C ABI before the call.
+    Mirrors ``flash_attn_func(q, k, v, dropout_p, softmax_scale, causal)``; the
+    dropout mask is the generator's (``seed``, ``offset``), which the backward
+    call must repeat. ``lse`` is fp32 [B, H, N] (N = max_seqlen for packed
+    inputs). Every tensor is validated against the layouts of the C ABI.
     """
     B, H, Hkv, N, d = validate(q, k, v, cu_seqlens=cu_seqlens, max_seqlen=max_seqlen, alibi_slopes=alibi_slopes,
                                q_like=(() if out is None else (("out", out),)), lse=lse)
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     o = torch.empty_like(q) if out is None else out
     l = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
-    st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(), B, H, Hkv, N, d, scale,
-                int(bool(causal)), _ptr(alibi_slopes), _ptr(cu_seqlens), _DTYPE[q.dtype], _stream_handle())
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(), B, H, Hkv, N, d, scale,
+            int(bool(causal)), _ptr(alibi_slopes), _ptr(cu_seqlens), _DTYPE[q.dtype])
+    if dropout_p:
+        st = fa_fwd_dropout(*args, float(dropout_p), int(seed), int(offset), _stream_handle())
+    else:
+        st = fa_fwd(*args, _stream_handle())
     if st != FA_OK:
         raise FaError(st)
     return o, l
@@ -219,8 +244,10 @@ def attention(q, k, v, causal: bool = False, softmax_scale: Optional[float] = No
 
 def attention_bwd(dout, q, k, v, o, lse, causal: bool = False, softmax_scale: Optional[float] = None,
                   alibi_slopes: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None,
-                  max_seqlen: Optional[int] = None, workspace: Optional[torch.Tensor] = None):
-    """Exact attention backward through ``fa_bwd``: returns (dq, dk, dv)."""
+                  max_seqlen: Optional[int] = None, workspace: Optional[torch.Tensor] = None,
+                  dropout_p: float = 0.0, seed: int = 0, offset: int = 0):
+    """Exact attention backward through ``fa_bwd`` (``fa_bwd_dropout`` when
+    ``dropout_p`` > 0, with the forward's seed and offset): returns (dq, dk, dv)."""
     B, H, Hkv, N, d = validate(q, k, v, cu_seqlens=cu_seqlens, max_seqlen=max_seqlen, alibi_slopes=alibi_slopes,
                                q_like=(("o", o), ("dout", dout)), lse=lse)
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
@@ -231,10 +258,14 @@ def attention_bwd(dout, q, k, v, o, lse, causal: bool = False, softmax_scale: Op
     elif not (workspace.is_contiguous() and workspace.device == q.device):
         raise ValueError("workspace must be a contiguous tensor on q's device")
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
-                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, N, d, scale, int(bool(causal)),
-                _ptr(alibi_slopes), _ptr(cu_seqlens), dt, workspace.data_ptr(),
-                workspace.numel() * workspace.element_size(), _stream_handle())
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, N, d, scale, int(bool(causal)),
+            _ptr(alibi_slopes), _ptr(cu_seqlens), dt)
+    ws = (workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream_handle())
+    if dropout_p:
+        st = fa_bwd_dropout(*args, float(dropout_p), int(seed), int(offset), *ws)
+    else:
+        st = fa_bwd(*args, *ws)
     if st != FA_OK:
         raise FaError(st)
     return dq, dk, dv
@@ -245,14 +276,16 @@ class FlashAttnFn(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, q, k, v, causal=False, softmax_scale=None, alibi_slopes=None, cu_seqlens=None,
-                max_seqlen=None):
-        o, lse = attention(q, k, v, causal, softmax_scale, alibi_slopes, cu_seqlens, max_seqlen)
+                max_seqlen=None, dropout_p=0.0, seed=0, offset=0):
+        o, lse = attention(q, k, v, causal, softmax_scale, alibi_slopes, cu_seqlens, max_seqlen,
+                           dropout_p=dropout_p, seed=seed, offset=offset)
         ctx.save_for_backward(q, k, v, o, lse)
         ctx.args = (causal, softmax_scale, alibi_slopes, cu_seqlens, max_seqlen)
+        ctx.drop = dict(dropout_p=dropout_p, seed=seed, offset=offset)  # the saved generator state
         return o
 
     @staticmethod
     def backward(ctx, do):
         q, k, v, o, lse = ctx.saved_tensors
-        dq, dk, dv = attention_bwd(do.contiguous(), q, k, v, o, lse, *ctx.args)
-        return dq, dk, dv, None, None, None, None, None
+        dq, dk, dv = attention_bwd(do.contiguous(), q, k, v, o, lse, *ctx.args, **ctx.drop)
+        return dq, dk, dv, None, None, None, None, None, None, None, None

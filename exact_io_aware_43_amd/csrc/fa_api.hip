@@ -54,19 +54,46 @@ fa::Args make_args(const void* q, const void* k, const void* v, int B, int H, in
     return a;
 }
 
+// Dropout arguments as the kernels take them. `on` is false when nothing is
+// dropped (K = 256), which runs the instances without dropout.
+struct Dropout {
+    bool on = false;
+    uint32_t seed_lo = 0, seed_hi = 0, offset = 0, keep_k = 256;
+    float scale = 1.f;
+};
+
+// K = round(256 (1 - p_drop)), kept when the random byte is below K; false for
+// p_drop outside [0, 1) or rounding to K = 0.
+bool make_dropout(float p_drop, unsigned long long seed, unsigned int offset, Dropout& dr) {
+    if (!(p_drop >= 0.f && p_drop < 1.f)) return false;
+    const int K = (int)std::nearbyint(256.0 * (1.0 - (double)p_drop));
+    if (K < 1 || K > 256) return false;
+    dr.on = K < 256;
+    dr.seed_lo = (uint32_t)(seed & 0xFFFFFFFFull);
+    dr.seed_hi = (uint32_t)(seed >> 32);
+    dr.offset = offset;
+    dr.keep_k = (uint32_t)K;
+    dr.scale = (float)(256.0 / (double)K);
+    return true;
+}
+
+void set_dropout(fa::Args& a, const Dropout& dr) {
+    a.seed_lo = dr.seed_lo;
+    a.seed_hi = dr.seed_hi;
+    a.drop_offset = dr.offset;
+    a.keep_k = dr.keep_k;
+    a.drop_scale = dr.scale;
+}
+
 // D and lse * log2(e), fp32 each, [B, H, N64] (see round64).
 size_t workspace_rows(int B, int H, int N) { return (size_t)B * (size_t)H * (size_t)round64(N); }
 size_t workspace_bytes_for(int B, int H, int N) {
     return (2 * workspace_rows(B, H, N) * sizeof(float) + 255) & ~(size_t)255;
 }
 
-}  // namespace
-
-extern "C" {
-
-int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N, int d,
-           float scale, int causal, const float* alibi_slopes, const int* cu_seqlens, fa_dtype dtype,
-           void* stream) {
+int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N, int d,
+             float scale, int causal, const float* alibi_slopes, const int* cu_seqlens, fa_dtype dtype,
+             const Dropout& dr, void* stream) {
     if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
     int st = check_common(B, H, Hkv, N, d, scale, causal, (int)dtype);
     if (st != FA_OK) return st;
@@ -78,13 +105,34 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
     fa::Args a = make_args(q, k, v, B, H, Hkv, N, scale, alibi_slopes, cu_seqlens);
     a.out = o;
     a.lse = lse;
+    set_dropout(a, dr);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     hipError_t e;
     if (dtype == FA_FP32)
         e = fa::launch_fwd_f32(a, d, causal != 0, alibi_slopes != nullptr, s);
     else
-        e = fa::launch_fwd_mfma(a, (int)dtype, d, causal != 0, alibi_slopes != nullptr, s);
+        e = fa::launch_fwd_mfma(a, (int)dtype, d, causal != 0, alibi_slopes != nullptr, dr.on, s);
     return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N, int d,
+           float scale, int causal, const float* alibi_slopes, const int* cu_seqlens, fa_dtype dtype,
+           void* stream) {
+    return fwd_impl(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, alibi_slopes, cu_seqlens, dtype, Dropout{},
+                    stream);
+}
+
+int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N,
+                   int d, float scale, int causal, const float* alibi_slopes, const int* cu_seqlens, fa_dtype dtype,
+                   float p_drop, unsigned long long seed, unsigned int offset, void* stream) {
+    Dropout dr;
+    if (!make_dropout(p_drop, seed, offset, dr)) return FA_ERR_INVALID_ARG;
+    if (dr.on && dtype == FA_FP32) return FA_ERR_UNSUPPORTED;
+    return fwd_impl(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, alibi_slopes, cu_seqlens, dtype, dr, stream);
 }
 
 size_t fa_bwd_workspace_size(int B, int H, int Hkv, int N, int d, int causal, int varlen, fa_dtype dtype) {
@@ -139,7 +187,7 @@ int scratch_for_current_device(void** out) {
 int bwd_launch(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d, float scale, int causal,
                const float* alibi_slopes, const int* cu_seqlens, fa_dtype dtype, void* workspace, unsigned stages,
-               void* stream) {
+               void* stream, const Dropout& dr = Dropout{}) {
     fa::Args a = make_args(q, k, v, B, H, Hkv, N, scale, alibi_slopes, cu_seqlens);
     a.o = o;
     a.dout = dout;
@@ -149,7 +197,8 @@ int bwd_launch(const void* q, const void* k, const void* v, const void* o, const
     a.dv = dv;
     a.dsum = reinterpret_cast<float*>(workspace);
     a.lse2 = a.dsum + workspace_rows(B, H, N);
-    hipError_t e = fa::launch_bwd(a, (int)dtype, d, causal != 0, alibi_slopes != nullptr, stages,
+    set_dropout(a, dr);
+    hipError_t e = fa::launch_bwd(a, (int)dtype, d, causal != 0, alibi_slopes != nullptr, dr.on, stages,
                                   reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
@@ -188,6 +237,22 @@ int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, c
 }
 
 size_t fa_bwd_noalloc_max_bytes(void) { return kScratchBytes; }
+
+int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                   void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d, float scale, int causal,
+                   const float* alibi_slopes, const int* cu_seqlens, fa_dtype dtype, float p_drop,
+                   unsigned long long seed, unsigned int offset, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+    Dropout dr;
+    if (!make_dropout(p_drop, seed, offset, dr)) return FA_ERR_INVALID_ARG;
+    int st = check_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, Hkv, N, d, scale, causal, alibi_slopes, cu_seqlens,
+                       dtype);
+    if (st != FA_OK) return st;
+    if (!workspace || !aligned16(workspace) || workspace_bytes < workspace_bytes_for(B, H, N))
+        return FA_ERR_WORKSPACE;
+    return bwd_launch(q, k, v, o, dout, lse, dq, dk, dv, B, H, Hkv, N, d, scale, causal, alibi_slopes, cu_seqlens,
+                      dtype, workspace, FA_BWD_ALL, stream, dr);
+}
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse, void* dq,
            void* dk, void* dv, int B, int H, int Hkv, int N, int d, float scale, int causal,

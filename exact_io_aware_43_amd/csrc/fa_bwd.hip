@@ -78,17 +78,18 @@ __global__ __launch_bounds__(NT) void bwd_dsum_kernel(Args a) {
 constexpr int DQ_BK = 64;  // keys per K/V tile
 
 // NW waves per workgroup, 32 queries each: 8 (two per SIMD) where the kernel
-// fits in 256 registers per lane. The d = 128 non-causal instance does not
-// (the compiler spills it there) and runs 4 waves, one per SIMD.
-template <int D, bool CAUSAL>
+// fits in 256 registers per lane. The d = 128 non-causal instances and the
+// d = 128 causal instance with both ALiBi and dropout do not (the compiler
+// spills them there) and run 4 waves, one per SIMD.
+template <int D, bool CAUSAL, bool ALIBI, bool DROP>
 constexpr int dq_waves() {
-    return (D == 128 && !CAUSAL) ? 4 : 8;
+    return (D == 128 && (!CAUSAL || (ALIBI && DROP))) ? 4 : 8;
 }
 
-template <typename T, int D, bool CAUSAL, bool ALIBI>
-__global__ __launch_bounds__((64 * dq_waves<D, CAUSAL>()), 1) void bwd_dq_kernel(Args a) {
-    constexpr int DQ_NT = 64 * dq_waves<D, CAUSAL>();
-    constexpr int DQ_BQ = 32 * dq_waves<D, CAUSAL>();
+template <typename T, int D, bool CAUSAL, bool ALIBI, bool DROP>
+__global__ __launch_bounds__((64 * dq_waves<D, CAUSAL, ALIBI, DROP>()), 1) void bwd_dq_kernel(Args a) {
+    constexpr int DQ_NT = 64 * dq_waves<D, CAUSAL, ALIBI, DROP>();
+    constexpr int DQ_BQ = 32 * dq_waves<D, CAUSAL, ALIBI, DROP>();
     constexpr int TILE = DQ_BK * D;  // stage: K tile then V tile, swizzled
     __shared__ __attribute__((aligned(16))) uint16_t stA[2 * TILE];
     __shared__ __attribute__((aligned(16))) uint16_t stB[2 * TILE];
@@ -128,6 +129,8 @@ __global__ __launch_bounds__((64 * dq_waves<D, CAUSAL>()), 1) void bwd_dq_kernel
     const float dsum = (qi < len) ? a.dsum[vidx] : 0.f;
     const float c2 = a.scale_log2;
     const float slope2 = ALIBI ? ld_uniform(a.slopes + h) * kLog2e : 0.f;
+    const uint32_t drop_row = (uint32_t)(b * a.H + h);  // dropout generator counter word 2
+    const uint32_t keep2 = a.keep_k | (a.keep_k << 16);
 
     int roff[D / 16], toff[D / 32][2];
 #pragma unroll
@@ -189,6 +192,16 @@ __global__ __launch_bounds__((64 * dq_waves<D, CAUSAL>()), 1) void bwd_dq_kernel
                     dp = Mfma<T>::mma(as_v8<T>(fv[kk % 3]), df[kk], dp);
                     __builtin_amdgcn_sched_barrier(0);
                 }
+                // With dropout the gradient reaching P is dP o keep * 256 / K:
+                // this lane's 16 bytes come from one generator call per 32-key
+                // block (byte r for element r, as in the forward).
+                uint32_t wd[4] = {0u, 0u, 0u, 0u};
+                if constexpr (DROP) {
+                    const uint4 w = philox4x32_10(2u * (uint32_t)(k0 / 32 + kb) + (uint32_t)kg, (uint32_t)qi,
+                                                  drop_row, a.drop_offset, a.seed_lo, a.seed_hi);
+                    wd[0] = w.x, wd[1] = w.y, wd[2] = w.z, wd[3] = w.w;
+                }
+                uint32_t keepm = 0u;  // 16-bit keep masks of the element pair (r & ~1, r | 1)
                 // dS^T = P^T (dP^T - D), P^T = exp2(S^T * scale * log2(e) - L * log2(e)) [+ ALiBi]
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
@@ -200,7 +213,14 @@ __global__ __launch_bounds__((64 * dq_waves<D, CAUSAL>()), 1) void bwd_dq_kernel
                     }
                     float p = exp2_fast(fmaf(s[r], c2, bias));
                     if (masked && (kj >= len || (CAUSAL && kj > qi))) p = 0.f;
-                    dp[r] = p * (dp[r] - dsum);
+                    float g = dp[r];
+                    if constexpr (DROP) {
+                        if ((r & 1) == 0) keepm = keep_mask2(wd[r >> 2], (r >> 1) & 1, keep2);
+                        const uint32_t m = (r & 1) ? (uint32_t)((int)keepm >> 16)
+                                                   : (uint32_t)((int)(keepm << 16) >> 16);
+                        g = __uint_as_float(__float_as_uint(g) & m) * a.drop_scale;
+                    }
+                    dp[r] = p * (g - dsum);
                 }
                 V8<T> dsb[2];
 #pragma unroll
@@ -251,7 +271,7 @@ __global__ __launch_bounds__((64 * dq_waves<D, CAUSAL>()), 1) void bwd_dq_kernel
     }
 }
 
-template <typename T, int D, bool CAUSAL, bool ALIBI>
+template <typename T, int D, bool CAUSAL, bool ALIBI, bool DROP>
 hipError_t launch(const Args& a, unsigned stages, hipStream_t s) {
     if (stages & 1u) {
         constexpr int RPB = NT / (D / 8);
@@ -261,30 +281,38 @@ hipError_t launch(const Args& a, unsigned stages, hipStream_t s) {
         if (e != hipSuccess) return e;
     }
     if (stages & 2u) {
-        hipError_t e = launch_bwd_dkdv(a, std::is_same<T, __bf16>::value ? 2 : 1, D, CAUSAL, ALIBI, s);
+        hipError_t e = launch_bwd_dkdv(a, std::is_same<T, __bf16>::value ? 2 : 1, D, CAUSAL, ALIBI, DROP, s);
         if (e != hipSuccess) return e;
     }
     if (stages & 4u) {
-        constexpr int nw = dq_waves<D, CAUSAL>();
+        constexpr int nw = dq_waves<D, CAUSAL, ALIBI, DROP>();
         dim3 grid(a.H, a.B, (a.N + 32 * nw - 1) / (32 * nw));
-        hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL, ALIBI>), grid, dim3(64 * nw), 0, s, a);
+        hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL, ALIBI, DROP>), grid, dim3(64 * nw), 0, s, a);
         return hipGetLastError();
     }
     return hipSuccess;
 }
 
+template <typename T, int D, bool DROP>
+hipError_t launch_m(const Args& a, bool causal, bool alibi, unsigned st, hipStream_t s) {
+    if (causal) return alibi ? launch<T, D, true, true, DROP>(a, st, s) : launch<T, D, true, false, DROP>(a, st, s);
+    return alibi ? launch<T, D, false, true, DROP>(a, st, s) : launch<T, D, false, false, DROP>(a, st, s);
+}
+
 template <typename T, int D>
-hipError_t launch_d(const Args& a, bool causal, bool alibi, unsigned st, hipStream_t s) {
-    if (causal) return alibi ? launch<T, D, true, true>(a, st, s) : launch<T, D, true, false>(a, st, s);
-    return alibi ? launch<T, D, false, true>(a, st, s) : launch<T, D, false, false>(a, st, s);
+hipError_t launch_d(const Args& a, bool causal, bool alibi, bool drop, unsigned st, hipStream_t s) {
+    return drop ? launch_m<T, D, true>(a, causal, alibi, st, s) : launch_m<T, D, false>(a, causal, alibi, st, s);
 }
 
 }  // namespace
 
-hipError_t launch_bwd(const Args& a, int dtype, int d, bool causal, bool alibi, unsigned st, hipStream_t s) {
+hipError_t launch_bwd(const Args& a, int dtype, int d, bool causal, bool alibi, bool drop, unsigned st,
+                      hipStream_t s) {
     if (dtype == 2)
-        return d == 64 ? launch_d<__bf16, 64>(a, causal, alibi, st, s) : launch_d<__bf16, 128>(a, causal, alibi, st, s);
-    return d == 64 ? launch_d<_Float16, 64>(a, causal, alibi, st, s) : launch_d<_Float16, 128>(a, causal, alibi, st, s);
+        return d == 64 ? launch_d<__bf16, 64>(a, causal, alibi, drop, st, s)
+                       : launch_d<__bf16, 128>(a, causal, alibi, drop, st, s);
+    return d == 64 ? launch_d<_Float16, 64>(a, causal, alibi, drop, st, s)
+                   : launch_d<_Float16, 128>(a, causal, alibi, drop, st, s);
 }
 
 }  // namespace fa

@@ -33,7 +33,7 @@ constexpr int KV_BQ = 64;       // queries per step (two blocks of 32)
 
 #define FA_SB() __builtin_amdgcn_sched_barrier(0)
 
-template <typename T, int D, bool CAUSAL, bool ALIBI>
+template <typename T, int D, bool CAUSAL, bool ALIBI, bool DROP>
 __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
     // stage: Q tile, dO tile (swizzled [KV_BQ x D] each), with L*log2(e) and D
     // (fp32, KV_BQ each) in a small array of their own: the two tile stages
@@ -46,6 +46,9 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
     __shared__ __attribute__((aligned(16))) float vecA[2 * KV_BQ];
     __shared__ __attribute__((aligned(16))) float vecB[2 * KV_BQ];
     __shared__ __attribute__((aligned(16))) uint16_t vt[KV_BK * D];  // V rows k0 .. k0 + KV_BK, swizzled
+    // dropout: each wave's 32 x 32 block of random bytes, stored key-major
+    // with the queries of one lane half (kg) contiguous (see the step below)
+    __shared__ __attribute__((aligned(16))) uint8_t dmask[DROP ? NW * 32 * 32 : 16];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int kg = lane >> 5;
@@ -124,6 +127,9 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
         if (wave == 1) dma_vec64(vec + KV_BQ, a.dsum + vbase, lane);
     };
 
+    const uint32_t keep2 = a.keep_k | (a.keep_k << 16);
+    uint8_t* dm = dmask + (DROP ? wave * 32 * 32 : 0);
+
     auto step = [&](const uint16_t* S, int h, int q0, auto masked) {
         constexpr bool MASKED = decltype(masked)::value;
         const uint16_t* Qs = S;
@@ -162,6 +168,27 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
                 FA_SB();
             }
 
+            // ---- dropout bytes of this block. The generator gives 16 bytes per
+            // (query, half of the wave's 32 keys), the layout the forward uses;
+            // this lane owns one key, so the wave writes its block to LDS and
+            // reads it back transposed. Lane (query ql, half) writes the byte of
+            // key 8 i + 4 half + j to row key, column 16 ((ql / 4) % 2) + 4 (ql / 8)
+            // + ql % 4; lane (key, kg) then reads its 16 queries
+            // 8 i + 4 kg + j as one 16-byte row segment, byte r for element r.
+            uint32_t wd[4] = {0u, 0u, 0u, 0u};
+            if constexpr (DROP) {
+                const int ql = lane & 31, half = lane >> 5;
+                const uint4 w = philox4x32_10(2u * (uint32_t)(kw / 32) + (uint32_t)half, (uint32_t)(q0 + 32 * qb + ql),
+                                              (uint32_t)(b * a.H + h), a.drop_offset, a.seed_lo, a.seed_hi);
+                const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+                const int colq = 16 * ((ql >> 2) & 1) + 4 * (ql >> 3) + (ql & 3);
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    dm[(8 * (e >> 2) + 4 * half + (e & 3)) * 32 + colq] = (uint8_t)(ww[e >> 2] >> (8 * (e & 3)));
+                const uint4 rd = *reinterpret_cast<const uint4*>(dm + (lane & 31) * 32 + 16 * kg);
+                wd[0] = rd.x, wd[1] = rd.y, wd[2] = rd.z, wd[3] = rd.w;
+            }
+
             // ---- softmax backward, row group i = accumulator rows 4i .. 4i + 3
             float pv[16], dsr[16];
 #pragma unroll
@@ -182,7 +209,13 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
                     float p = exp2_fast(fmaf(sc[r], c2, bias));
                     if (MASKED && key > qi) p = 0.f;
                     pv[r] = p;
-                    dsr[r] = p * (dpc[r] - dv[j]);
+                    float g = dpc[r];
+                    if constexpr (DROP) {  // the gradient reaching P: dP o keep * 256 / K
+                        const uint32_t m2 = keep_mask2(wd[r >> 2], (r >> 1) & 1, keep2);
+                        const uint32_t m = (r & 1) ? (uint32_t)((int)m2 >> 16) : (uint32_t)((int)(m2 << 16) >> 16);
+                        g = __uint_as_float(__float_as_uint(g) & m) * a.drop_scale;
+                    }
+                    dsr[r] = p * (g - dv[j]);
                 }
             }
             V8<T> pb[2], db8[2];  // P and dS per 16-query chunk, as B operands
@@ -193,6 +226,14 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
                                   pv[r0 + 7]);
                 db8[h2] = pack8<T>(dsr[r0], dsr[r0 + 1], dsr[r0 + 2], dsr[r0 + 3], dsr[r0 + 4], dsr[r0 + 5],
                                    dsr[r0 + 6], dsr[r0 + 7]);
+                if constexpr (DROP) {  // dV takes the dropped probabilities (scaled at the end)
+                    uint4 u = __builtin_bit_cast(uint4, pb[h2]);
+                    u.x &= keep_mask2(wd[2 * h2], 0, keep2);
+                    u.y &= keep_mask2(wd[2 * h2], 1, keep2);
+                    u.z &= keep_mask2(wd[2 * h2 + 1], 0, keep2);
+                    u.w &= keep_mask2(wd[2 * h2 + 1], 1, keep2);
+                    pb[h2] = as_v8<T>(u);
+                }
             }
 
             // ---- dV^T += dO^T P, dK^T += Q^T dS: groups (chunk c of the block, db)
@@ -239,6 +280,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
         T* dK = reinterpret_cast<T*>(a.dk) + (size_t)(row0 + key) * ldk + (size_t)g * D;
         T* dV = reinterpret_cast<T*>(a.dv) + (size_t)(row0 + key) * ldk + (size_t)g * D;
         const float sc = a.scale;
+        const float vs = DROP ? a.drop_scale : 1.f;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
@@ -247,8 +289,8 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
                 const int r = 4 * i;
                 *reinterpret_cast<uint2*>(dK + d0) = pack4<T>(dkacc[db][r] * sc, dkacc[db][r + 1] * sc,
                                                               dkacc[db][r + 2] * sc, dkacc[db][r + 3] * sc);
-                *reinterpret_cast<uint2*>(dV + d0) =
-                    pack4<T>(dvacc[db][r], dvacc[db][r + 1], dvacc[db][r + 2], dvacc[db][r + 3]);
+                *reinterpret_cast<uint2*>(dV + d0) = pack4<T>(dvacc[db][r] * vs, dvacc[db][r + 1] * vs,
+                                                              dvacc[db][r + 2] * vs, dvacc[db][r + 3] * vs);
             }
         }
     }
@@ -256,24 +298,30 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
 
 #undef FA_SB
 
-template <typename T, int D, bool CAUSAL, bool ALIBI>
+template <typename T, int D, bool CAUSAL, bool ALIBI, bool DROP>
 hipError_t launch(const Args& a, hipStream_t s) {
     dim3 grid(a.Hkv, a.B, (a.N + KV_BK - 1) / KV_BK);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL, ALIBI>), grid, dim3(NT), 0, s, a);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL, ALIBI, DROP>), grid, dim3(NT), 0, s, a);
     return hipGetLastError();
 }
 
+template <typename T, int D, bool DROP>
+hipError_t launch_m(const Args& a, bool causal, bool alibi, hipStream_t s) {
+    if (causal) return alibi ? launch<T, D, true, true, DROP>(a, s) : launch<T, D, true, false, DROP>(a, s);
+    return alibi ? launch<T, D, false, true, DROP>(a, s) : launch<T, D, false, false, DROP>(a, s);
+}
+
 template <typename T, int D>
-hipError_t launch_d(const Args& a, bool causal, bool alibi, hipStream_t s) {
-    if (causal) return alibi ? launch<T, D, true, true>(a, s) : launch<T, D, true, false>(a, s);
-    return alibi ? launch<T, D, false, true>(a, s) : launch<T, D, false, false>(a, s);
+hipError_t launch_d(const Args& a, bool causal, bool alibi, bool drop, hipStream_t s) {
+    return drop ? launch_m<T, D, true>(a, causal, alibi, s) : launch_m<T, D, false>(a, causal, alibi, s);
 }
 
 }  // namespace
 
-hipError_t launch_bwd_dkdv(const Args& a, int dtype, int d, bool causal, bool alibi, hipStream_t s) {
-    if (dtype == 2) return d == 64 ? launch_d<__bf16, 64>(a, causal, alibi, s) : launch_d<__bf16, 128>(a, causal, alibi, s);
-    return d == 64 ? launch_d<_Float16, 64>(a, causal, alibi, s) : launch_d<_Float16, 128>(a, causal, alibi, s);
+hipError_t launch_bwd_dkdv(const Args& a, int dtype, int d, bool causal, bool alibi, bool drop, hipStream_t s) {
+    if (dtype == 2)
+        return d == 64 ? launch_d<__bf16, 64>(a, causal, alibi, drop, s) : launch_d<__bf16, 128>(a, causal, alibi, drop, s);
+    return d == 64 ? launch_d<_Float16, 64>(a, causal, alibi, drop, s) : launch_d<_Float16, 128>(a, causal, alibi, drop, s);
 }
 
 }  // namespace fa

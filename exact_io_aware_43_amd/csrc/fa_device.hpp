@@ -98,6 +98,43 @@ __device__ __forceinline__ float add_pair<_Float16>(uint32_t pair, float acc) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair), one, acc, false);
 }
 
+// Philox-4x32 with 10 rounds (Salmon, Moraes, Dror, Shaw, "Parallel Random
+// Numbers: As Easy as 1, 2, 3", SC'11): a bijection of the 128-bit counter
+// (c0, c1, c2, c3) under the 64-bit key (k0, k1). Each round takes the 64-bit
+// products of c0 and c2 with the multipliers 0xD2511F53 and 0xCD9E8D57, mixes
+// their high halves with the other words and the key, and bumps the key by
+// the Weyl constants 0x9E3779B9 and 0xBB67AE85. The key is wave-uniform, so
+// its schedule runs on the scalar unit.
+__device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                               uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+        const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+        c0 = hi1 ^ c1 ^ k0;
+        c1 = lo1;
+        c2 = hi0 ^ c3 ^ k1;
+        c3 = lo0;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    return make_uint4(c0, c1, c2, c3);
+}
+
+// Keep mask of two 16-bit values from two random bytes of `word` (bytes
+// 2 * hi and 2 * hi + 1): each 16-bit half is 0xFFFF when its byte is below
+// K (`k2` = K | K << 16, K <= 256) and 0 otherwise. The bytes are spread to
+// the halves, K subtracted in 16-bit lanes and the sign bit replicated.
+__device__ __forceinline__ uint32_t keep_mask2(uint32_t word, int hi, uint32_t k2) {
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    typedef short i16x2 __attribute__((ext_vector_type(2)));
+    const uint32_t x = __builtin_amdgcn_perm(0u, word, hi ? 0x0c030c02u : 0x0c010c00u);
+    const u16x2 d = __builtin_bit_cast(u16x2, x) - __builtin_bit_cast(u16x2, k2);
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(i16x2, d) >> (short)15);
+}
+
 // Maximum / sum of x over lanes l and l ^ 32 with v_permlane32_swap (a
 // register exchange between the two halves of the wave, no LDS round trip).
 // Both lanes get the same value, with the same rounding.

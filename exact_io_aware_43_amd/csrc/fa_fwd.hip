@@ -63,7 +63,7 @@ constexpr float sum_bound() {
     return sizeof(T) == 2 && __is_same(T, _Float16) ? 32768.f : 4294967296.f;
 }
 
-template <typename T, int D, bool CAUSAL, bool ALIBI>
+template <typename T, int D, bool CAUSAL, bool ALIBI, bool DROP>
 __global__ __launch_bounds__(NT, 1) void fwd_mfma_kernel(Args a) {
     // Two named K/V stages (swizzled [BC x D] tiles, K then V): the prefetch
     // into one overlaps the reads of the other, which the compiler can only
@@ -147,6 +147,8 @@ __global__ __launch_bounds__(NT, 1) void fwd_mfma_kernel(Args a) {
 
     const float c2 = a.scale_log2;
     const float slope2 = ALIBI ? ld_uniform(a.slopes + h) * kLog2e : 0.f;
+    const uint32_t drop_row = (uint32_t)(b * a.H + h);  // generator counter word 2
+    const uint32_t keep2 = a.keep_k | (a.keep_k << 16);
 
     bool fresh = true;  // wave-uniform: no tile of this wave processed yet
     auto compute = [&](const uint16_t* Ks, int it) {
@@ -326,6 +328,28 @@ __global__ __launch_bounds__(NT, 1) void fwd_mfma_kernel(Args a) {
             }
             l_rnd += r0 + r1;
         }
+        if constexpr (DROP) {
+            // Dropout on the probabilities that multiply V (the sums above keep
+            // every one): one generator call per 32-key block gives this lane's
+            // 16 bytes, byte r deciding accumulator element r (key
+            // k0 + 32 kb + 8 (r / 4) + 4 kg + r % 4 of query qi); the 256 / K
+            // factor is applied to O at the end.
+#pragma unroll
+            for (int kb = 0; kb < BC / 32; ++kb) {
+                const uint4 w = philox4x32_10(2u * (uint32_t)(k0 / 32 + kb) + (uint32_t)kg, (uint32_t)qi, drop_row,
+                                              a.drop_offset, a.seed_lo, a.seed_hi);
+                const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    uint4 u = __builtin_bit_cast(uint4, pf[2 * kb + half]);
+                    u.x &= keep_mask2(wd[2 * half], 0, keep2);
+                    u.y &= keep_mask2(wd[2 * half], 1, keep2);
+                    u.z &= keep_mask2(wd[2 * half + 1], 0, keep2);
+                    u.w &= keep_mask2(wd[2 * half + 1], 1, keep2);
+                    pf[2 * kb + half] = as_v8<T>(u);
+                }
+            }
+        }
         uint4 fv[3];
         auto load2 = [&](int gi) {
             const int c = gi / (D / 32), db = gi % (D / 32);
@@ -351,7 +375,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_mfma_kernel(Args a) {
     const float l_tot = sum_xor32(l_run);
     const float lr_tot = sum_xor32(l_rnd);
     if (qi < len) {
-        const float inv = 1.f / lr_tot;
+        const float inv = (DROP ? a.drop_scale : 1.f) / lr_tot;
         T* O = reinterpret_cast<T*>(a.out) + (size_t)row0 * ldq + (size_t)h * D + (size_t)qi * ldq;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
@@ -367,25 +391,31 @@ __global__ __launch_bounds__(NT, 1) void fwd_mfma_kernel(Args a) {
     }
 }
 
-template <typename T, int D, bool CAUSAL, bool ALIBI>
+template <typename T, int D, bool CAUSAL, bool ALIBI, bool DROP>
 hipError_t launch(const Args& a, hipStream_t s) {
     const int nqt = (a.N + BR - 1) / BR;
     dim3 grid(a.H, a.B, nqt);
-    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, CAUSAL, ALIBI>), grid, dim3(NT), 0, s, a);
+    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, CAUSAL, ALIBI, DROP>), grid, dim3(NT), 0, s, a);
     return hipGetLastError();
 }
 
+template <typename T, int D, bool DROP>
+hipError_t launch_m(const Args& a, bool causal, bool alibi, hipStream_t s) {
+    if (causal) return alibi ? launch<T, D, true, true, DROP>(a, s) : launch<T, D, true, false, DROP>(a, s);
+    return alibi ? launch<T, D, false, true, DROP>(a, s) : launch<T, D, false, false, DROP>(a, s);
+}
+
 template <typename T, int D>
-hipError_t launch_d(const Args& a, bool causal, bool alibi, hipStream_t s) {
-    if (causal) return alibi ? launch<T, D, true, true>(a, s) : launch<T, D, true, false>(a, s);
-    return alibi ? launch<T, D, false, true>(a, s) : launch<T, D, false, false>(a, s);
+hipError_t launch_d(const Args& a, bool causal, bool alibi, bool drop, hipStream_t s) {
+    return drop ? launch_m<T, D, true>(a, causal, alibi, s) : launch_m<T, D, false>(a, causal, alibi, s);
 }
 
 }  // namespace
 
-hipError_t launch_fwd_mfma(const Args& a, int dtype, int d, bool causal, bool alibi, hipStream_t s) {
-    if (dtype == 2) return d == 64 ? launch_d<__bf16, 64>(a, causal, alibi, s) : launch_d<__bf16, 128>(a, causal, alibi, s);
-    return d == 64 ? launch_d<_Float16, 64>(a, causal, alibi, s) : launch_d<_Float16, 128>(a, causal, alibi, s);
+hipError_t launch_fwd_mfma(const Args& a, int dtype, int d, bool causal, bool alibi, bool drop, hipStream_t s) {
+    if (dtype == 2)
+        return d == 64 ? launch_d<__bf16, 64>(a, causal, alibi, drop, s) : launch_d<__bf16, 128>(a, causal, alibi, drop, s);
+    return d == 64 ? launch_d<_Float16, 64>(a, causal, alibi, drop, s) : launch_d<_Float16, 128>(a, causal, alibi, drop, s);
 }
 
 }  // namespace fa

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
+#include <cstdint>
 
 namespace fa {
 
@@ -30,14 +31,21 @@ struct Args {
     int N64;           // N rounded up to a multiple of 64: row pitch of the workspace vectors
     float scale;       // softmax scale
     float scale_log2;  // scale * log2(e)
+    // dropout (instances with dropout only): Philox key, counter word 3, keep
+    // threshold K (a probability is kept when its random byte is below K) and
+    // the factor 256 / K applied to kept probabilities
+    uint32_t seed_lo, seed_hi, drop_offset, keep_k;
+    float drop_scale;
 };
 
-// Each returns hipSuccess or the launch error. `dtype` follows fa_dtype.
-hipError_t launch_fwd_mfma(const Args& a, int dtype, int d, bool causal, bool alibi, hipStream_t s);
+// Each returns hipSuccess or the launch error. `dtype` follows fa_dtype;
+// `drop` selects the instances with dropout (16-bit only).
+hipError_t launch_fwd_mfma(const Args& a, int dtype, int d, bool causal, bool alibi, bool drop, hipStream_t s);
 hipError_t launch_fwd_f32(const Args& a, int d, bool causal, bool alibi, hipStream_t s);
 // The dK/dV launch alone (built in its own translation unit with its own flags).
-hipError_t launch_bwd_dkdv(const Args& a, int dtype, int d, bool causal, bool alibi, hipStream_t s);
+hipError_t launch_bwd_dkdv(const Args& a, int dtype, int d, bool causal, bool alibi, bool drop, hipStream_t s);
 // `stages`: bit 0 = D pre-pass, bit 1 = dK/dV, bit 2 = dQ (enqueued in that order).
-hipError_t launch_bwd(const Args& a, int dtype, int d, bool causal, bool alibi, unsigned stages, hipStream_t s);
+hipError_t launch_bwd(const Args& a, int dtype, int d, bool causal, bool alibi, bool drop, unsigned stages,
+                      hipStream_t s);
 
 }  // namespace fa

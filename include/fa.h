@@ -89,6 +89,36 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            void* stream);
 
 /*
+ * Forward pass with dropout on the attention probabilities: the fused dropout
+ * of the page's Key design 1 stage table, whose mask the backward regenerates
+ * from the saved generator state (Key design 3). The softmax and lse use
+ * every score; the probabilities that multiply V are dropped and the kept
+ * ones scaled, O = (P o M * 256 / K) V.
+ *
+ *   p_drop : drop probability in [0, 1). K = round(256 (1 - p_drop)) must be
+ *            at least 1; a probability is kept when its random byte is below
+ *            K (the effective keep rate is K / 256, and the factor 256 / K
+ *            keeps every expectation unchanged). K = 256 (p_drop < 1/512)
+ *            drops nothing and equals fa_fwd.
+ *   seed   : 64-bit key of the generator; offset: its 32-bit counter word 3
+ *            (advance it between calls that share a seed).
+ *
+ * Mask M for sequence b, query head h, query position i and key position j
+ * (positions within the sequence): the byte (j % 4) (little-endian) of output
+ * word (j % 32) / 8 of Philox-4x32 with 10 rounds (Salmon, Moraes, Dror, Shaw,
+ * "Parallel Random Numbers: As Easy as 1, 2, 3", SC'11) under key
+ * (seed mod 2^32, seed / 2^32) at counter
+ * (2 (j / 32) + (j / 4) % 2, i, b H + h, offset). Other arguments, layouts
+ * and errors as fa_fwd; FA_FP32 with dropout is FA_ERR_UNSUPPORTED, and an
+ * out-of-range p_drop is FA_ERR_INVALID_ARG.
+ */
+int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int Hkv, int N, int d, float scale, int causal,
+                   const float* alibi_slopes, const int* cu_seqlens, fa_dtype dtype,
+                   float p_drop, unsigned long long seed, unsigned int offset,
+                   void* stream);
+
+/*
  * Bytes of device scratch fa_bwd needs for these sizes: the per-row
  * D_i = dO_i . O_i of Key design 3 and the row statistic rescaled to log2
  * units, both fp32 [B, H, N64] with N64 = N rounded up to a multiple of 64
@@ -115,6 +145,20 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            int B, int H, int Hkv, int N, int d, float scale, int causal,
            const float* alibi_slopes, const int* cu_seqlens, fa_dtype dtype,
            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward pass of fa_fwd_dropout: the same mask is regenerated from
+ * (p_drop, seed, offset), which must equal the forward call's. dV takes the
+ * dropped probabilities, dV = (P o M * 256 / K)^T dout, and the gradient
+ * reaching P is (dout V^T) o M * 256 / K; D_i = dout_i . O_i still holds with
+ * the dropped O. Other arguments, workspace, results and errors as fa_bwd.
+ */
+int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
+                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                   int B, int H, int Hkv, int N, int d, float scale, int causal,
+                   const float* alibi_slopes, const int* cu_seqlens, fa_dtype dtype,
+                   float p_drop, unsigned long long seed, unsigned int offset,
+                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * The three launches of fa_bwd, selectable one by one, for callers that split

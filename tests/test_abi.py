@@ -30,8 +30,8 @@ def declared_functions():
 
 def test_header_declares_expected_api():
     assert declared_functions() == sorted(
-        ["fa_fwd", "fa_bwd", "fa_bwd_stages", "fa_bwd_workspace_size", "fa_bwd_noalloc", "fa_bwd_noalloc_max_bytes",
-         "fa_strerror", "fa_version"])
+        ["fa_fwd", "fa_fwd_dropout", "fa_bwd", "fa_bwd_dropout", "fa_bwd_stages", "fa_bwd_workspace_size",
+         "fa_bwd_noalloc", "fa_bwd_noalloc_max_bytes", "fa_strerror", "fa_version"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -233,3 +233,25 @@ def test_noalloc_scratch_size():
 ])
 def test_noalloc_rejects(kw, expect):
     assert _noalloc(**kw) == expect
+
+
+@pytest.mark.parametrize("p_drop,expect", [
+    (-0.1, INVALID), (1.0, INVALID), (1.5, INVALID), (float("nan"), INVALID), (0.999, INVALID),
+])
+def test_dropout_rejects_probability(p_drop, expect):
+    a = [PTR[0], PTR[1], PTR[2], PTR[3], PTR[4], 1, 4, 2, 64, 128, 0.125, 0, None, None, fa.FA_BF16]
+    assert fa.fa_fwd_dropout(*a, p_drop, 1, 0, None) == expect
+    b = [PTR[0], PTR[1], PTR[2], PTR[3], PTR[4], PTR[5], PTR[6], PTR[7], PTR[8], 2, 4, 2, 64, 64, 0.125, 1, None,
+         None, fa.FA_BF16]
+    assert fa.fa_bwd_dropout(*b, p_drop, 1, 0, PTR[9], 1 << 20, None) == expect
+
+
+def test_dropout_rejects_like_plain_calls():
+    assert fa.fa_fwd_dropout(None, PTR[1], PTR[2], PTR[3], PTR[4], 1, 4, 2, 64, 128, 0.125, 0, None, None,
+                             fa.FA_BF16, 0.1, 1, 0, None) == INVALID
+    assert fa.fa_fwd_dropout(PTR[0], PTR[1], PTR[2], PTR[3], PTR[4], 1, 4, 2, 64, 128, 0.125, 0, None, None,
+                             fa.FA_FP32, 0.1, 1, 0, None) == UNSUPPORTED
+    b = [PTR[0], PTR[1], PTR[2], PTR[3], PTR[4], PTR[5], PTR[6], PTR[7], PTR[8], 2, 4, 2, 64, 64, 0.125, 1, None,
+         None, fa.FA_BF16, 0.1, 1, 0]
+    assert fa.fa_bwd_dropout(*b, None, 1 << 20, None) == WORKSPACE
+    assert fa.fa_bwd_dropout(*b, PTR[9], 16, None) == WORKSPACE
