@@ -73,6 +73,7 @@ __all__ = [
     "online_head_fwd",
     "tile_state",
     "merge_states",
+    "decode_fwd",
     "brute_fwd",
 ]
 
@@ -301,6 +302,48 @@ def online_head_fwd(qh, kh, vh, scale, bounds, causal=False, slope=None, order="
         raise ValueError(order)
     m, ell, u = acc
     return u / ell[:, None], m + np.log(ell)
+
+
+def decode_fwd(q, k_cache, v_cache, cache_seqlens, scale=None, causal=True, alibi_slopes=None):
+    """Attention of a few new queries over a key/value cache, in fp64 (the decode
+    workload; "FlashAttention: Faster Attention Without Dropping a Single
+    Interaction", Limitations: long context and inference, and "If the parent
+    paper were rewritten in 2026": a separate single-token decode protocol).
+
+    q [B, Nq, H, d]; k_cache, v_cache [B, Nk, Hkv, d]; cache_seqlens [B]: batch
+    entry b holds L_b valid keys (positions 0 .. L_b - 1), and its Nq queries are
+    the last Nq tokens of that sequence, at positions L_b - Nq + t. Causal keeps
+    key j <= L_b - Nq + t (the mask aligned to the end of the cache); ALiBi adds
+    -slope_h |position(t) - j|. Returns o [B, Nq, H, d] and lse [B, H, Nq]; a
+    query that sees no key (L_b = 0, or causal with L_b - Nq + t < 0) has
+    O = 0 and lse = -inf.
+    """
+    q, k, v = _f64(q), _f64(k_cache), _f64(v_cache)
+    B, Nq, H, d = q.shape
+    Hkv = k.shape[2]
+    G = H // Hkv
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    slopes = None if alibi_slopes is None else _f64(alibi_slopes).reshape(-1)
+    lens = [int(x) for x in np.asarray(cache_seqlens).reshape(-1)]
+    o = np.zeros((B, Nq, H, d))
+    lse = np.full((B, H, Nq), -np.inf)
+    for b in range(B):
+        L = lens[b]
+        pos = L - Nq + np.arange(Nq)
+        for h in range(H):
+            g = h // G
+            s = scale * (q[b, :, h] @ k[b, :L, g].T)
+            if slopes is not None:
+                s = s - slopes[h] * np.abs(pos[:, None] - np.arange(L)[None, :]).astype(np.float64)
+            if causal:
+                s = np.where(np.arange(L)[None, :] > pos[:, None], -np.inf, s)
+            seen = np.isfinite(s).any(axis=1) if L else np.zeros(Nq, dtype=bool)
+            if not seen.any():
+                continue
+            p, l = _softmax_rows(s[seen])
+            o[b, seen, h] = p @ v[b, :L, g]
+            lse[b, h, seen] = l
+    return o, lse
 
 
 def brute_fwd(q, k, v, scale=None, causal=False, alibi_slopes=None, cu_seqlens=None, dropout=None):

@@ -448,3 +448,65 @@ def test_planted_mistakes(name):
         except AssertionError:
             caught.append(pin.__name__)
     assert caught, f"no pin catches the planted mistake {name}"
+
+
+# ------------------------------------------------------------------ decode (KV cache)
+
+def test_decode_is_the_last_rows_of_causal_attention():
+    """Causal decode of the last Nq tokens equals those rows of full causal attention
+    over the same sequence (with ALiBi and GQA); the cache rows past L_b are ignored."""
+    rng = RNG(60)
+    B, H, Hkv, d, Nk, Nq = 3, 4, 2, 5, 20, 3
+    lens = [20, 7, 3]
+    qf = _rand(rng, B, Nk, H, d)
+    k, v = _rand(rng, B, Nk, Hkv, d), _rand(rng, B, Nk, Hkv, d)
+    sl = np.array([0.5, 0.25, 0.125, 0.0625])
+    q = np.stack([qf[b, lens[b] - Nq:lens[b]] for b in range(B)])
+    o, lse = OA.decode_fwd(q, k, v, lens, scale=0.6, causal=True, alibi_slopes=sl)
+    for b in range(B):
+        L = lens[b]
+        of, lf = OA.attention_fwd(qf[None, b, :L], k[None, b, :L], v[None, b, :L], scale=0.6, causal=True,
+                                  alibi_slopes=sl)
+        np.testing.assert_allclose(o[b], of[0, L - Nq:], atol=1e-14)
+        np.testing.assert_allclose(lse[b], lf[0, :, L - Nq:], atol=1e-14)
+    # garbage in the cache past each length changes nothing
+    k2, v2 = k.copy(), v.copy()
+    for b in range(B):
+        k2[b, lens[b]:] = 1e3
+        v2[b, lens[b]:] = -1e3
+    o2, l2 = OA.decode_fwd(q, k2, v2, lens, scale=0.6, causal=True, alibi_slopes=sl)
+    assert np.array_equal(o, o2) and np.array_equal(lse, l2)
+
+
+def test_decode_non_causal_and_empty():
+    """Non-causal decode is attention of the queries over the valid cache; a query
+    that sees no key gives O = 0, lse = -inf."""
+    rng = RNG(61)
+    q, k, v = _rand(rng, 2, 2, 2, 4), _rand(rng, 2, 9, 1, 4), _rand(rng, 2, 9, 1, 4)
+    o, lse = OA.decode_fwd(q, k, v, [9, 0], causal=False)
+    ob, lb = OA.brute_fwd(np.concatenate([q[:1], np.zeros((1, 7, 2, 4))], axis=1)[:, :9],
+                          k[:1], v[:1], scale=0.5, causal=False)
+    np.testing.assert_allclose(o[0], ob[0, :2], atol=1e-13)
+    np.testing.assert_allclose(lse[0], lb[0, :, :2], atol=1e-13)
+    assert np.all(o[1] == 0) and np.all(lse[1] == -np.inf)
+    # causal with fewer keys than queries: the first query of a 1-key cache sees nothing
+    o, lse = OA.decode_fwd(q, k, v, [1, 2], causal=True)
+    assert lse[0, 0, 0] == -np.inf and np.all(o[0, 0] == 0)
+    np.testing.assert_allclose(o[0, 1, :], np.broadcast_to(v[0, 0, 0], (2, 4)), atol=1e-15)
+
+
+def test_decode_split_merge():
+    """States of key splits merged with merge_states give the decode output (the
+    split-KV combine of Key design 2)."""
+    rng = RNG(62)
+    L, d = 37, 6
+    q, k, v = _rand(rng, 2, d), _rand(rng, L, d), _rand(rng, L, d)
+    ref_o, ref_l = OA.head_fwd(q, k, v, 0.4)
+    for splits in ([0, 10, 37], [0, 1, 2, 3, 37], [0, 20, 36, 37]):
+        states = [OA.tile_state(q, k, v, lo, hi, 0.4, False) for lo, hi in zip(splits[:-1], splits[1:])]
+        acc = states[0]
+        for st in states[1:]:
+            acc = OA.merge_states(acc, st)
+        m, ell, u = acc
+        np.testing.assert_allclose(u / ell[:, None], ref_o, atol=1e-13)
+        np.testing.assert_allclose(m + np.log(ell), ref_l, atol=1e-13)
