@@ -108,6 +108,9 @@ def main():
     import exact_io_aware_43_amd as fa
     from exact_io_aware_43_amd.workloads import WORKLOADS, flops, make_inputs, seq_lengths
 
+    if args.workload == "decode":
+        bench_decode(args)
+        return
     w = WORKLOADS[args.workload]
     if w.dtype == "fp32":
         raise SystemExit(f"workload {w.name} is the fp32 latency case (one or two workgroups); it is a parity "
@@ -346,6 +349,68 @@ def main():
         torch.neg(x, out=y)
         torch.cuda.synchronize()
         print(f"[bench] copy calibration: neg of {COPY_BYTES} bytes", file=sys.stderr, flush=True)
+
+
+def bench_decode(args):
+    """Decode over a key/value cache (fa_fwd_kvcache): one new query per sequence
+    against long caches. Bound by HBM: every cached key and value is read once
+    per kv head, so the roofline is the algorithmic bytes (valid K and V rows,
+    Q, O, lse) over the launch time against 8 TB/s; TFLOP/s (4 H Nq L d per
+    sequence) is reported beside it."""
+    import torch
+
+    import exact_io_aware_43_amd as fa
+    from exact_io_aware_43_amd.workloads import DECODE, make_decode_inputs
+
+    w, Nq, lengths = DECODE
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = make_decode_inputs(w, Nq, lengths, seed=args.seed)
+    q, kc, vc, cl = (inp[x].to(dev) for x in ("q", "k_cache", "v_cache", "cache_seqlens"))
+    lens = inp["cache_seqlens"].tolist()
+    B, H, Hkv, Nk, d = w.B, w.H, w.Hkv, w.N, w.d
+    print(f"[bench] decode {w} Nq={Nq} lengths={lens}", file=sys.stderr, flush=True)
+    ws_bytes = fa.fa_kvcache_workspace_size(B, H, Hkv, Nq, Nk, d, 0)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def step():
+        st = fa.fa_fwd_kvcache(q.data_ptr(), kc.data_ptr(), vc.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                               cl.data_ptr(), B, H, Hkv, Nq, Nk, d, inp["scale"], 1, None, fa.FA_BF16, 0,
+                               ws.data_ptr(), ws_bytes, sh)
+        if st:
+            raise fa.FaError(st)
+
+    for _ in range(args.warmup + 1):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    keys = sum(lens)
+    flop = 4.0 * H * Nq * keys * d
+    alg_bytes = 2 * keys * Hkv * d * 2 + 2 * B * Nq * H * d * 2 + 4 * B * H * Nq
+    gbs = alg_bytes / (ms * 1e-3) / 1e9
+    splits = ws_bytes // (B * H * Nq * (d + 1) * 4) if ws_bytes else 1
+    out = {
+        "metric": METRIC, "value": round(flop / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": "decode", "B": B, "H": H, "Hkv": Hkv, "Nq": Nq, "cache_capacity": Nk,
+                   "cache_lengths": lens, "d": d, "causal": True, "pass": "forward (decode)"},
+        "roofline": {"kernel": "decode_split+merge", "bound": "hbm", "achieved": round(gbs, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "avg_launch_ms": round(ms, 4), "work_per_launch": int(alg_bytes)},
+        "splits": int(splits),
+    }
+    print(json.dumps(out), flush=True)
 
 
 def _cpu_model():

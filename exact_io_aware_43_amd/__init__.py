@@ -19,6 +19,7 @@ from ._binding import (  # noqa: F401
     LIB_PATH,
     attention,
     attention_bwd,
+    attention_kvcache,
     fa_bwd,
     fa_bwd_dropout,
     fa_fwd_dropout,
@@ -27,6 +28,8 @@ from ._binding import (  # noqa: F401
     fa_bwd_stages,
     fa_bwd_workspace_size,
     fa_fwd,
+    fa_fwd_kvcache,
+    fa_kvcache_workspace_size,
     fa_strerror,
     fa_version,
     lib,

@@ -47,6 +47,10 @@ def lib() -> ctypes.CDLL:
         L.fa_fwd_dropout.restype = ci
         L.fa_bwd_dropout.argtypes = L.fa_bwd.argtypes[:-3] + [cf, u64, u32, vp, sz, vp]
         L.fa_bwd_dropout.restype = ci
+        L.fa_kvcache_workspace_size.argtypes = [ci] * 7
+        L.fa_kvcache_workspace_size.restype = sz
+        L.fa_fwd_kvcache.argtypes = [vp] * 6 + [ci] * 6 + [cf, ci, vp, ci, ci, vp, sz, vp]
+        L.fa_fwd_kvcache.restype = ci
         L.fa_bwd_noalloc.argtypes = L.fa_bwd.argtypes[:-3] + [vp]
         L.fa_bwd_noalloc.restype = ci
         L.fa_bwd_noalloc_max_bytes.argtypes = []
@@ -78,6 +82,17 @@ def fa_bwd_dropout(q, k, v, o, dout, lse, dq, dk, dv, B, H, Hkv, N, d, scale, ca
     """``fa_bwd_dropout`` with integer device pointers (or None for NULL); returns the status."""
     return lib().fa_bwd_dropout(q, k, v, o, dout, lse, dq, dk, dv, B, H, Hkv, N, d, scale, causal, alibi_slopes,
                                 cu_seqlens, dtype, p_drop, seed, offset, workspace, workspace_bytes, stream)
+
+
+def fa_kvcache_workspace_size(B, H, Hkv, Nq, Nk, d, num_splits) -> int:
+    return lib().fa_kvcache_workspace_size(B, H, Hkv, Nq, Nk, d, num_splits)
+
+
+def fa_fwd_kvcache(q, k_cache, v_cache, o, lse, cache_seqlens, B, H, Hkv, Nq, Nk, d, scale, causal, alibi_slopes,
+                   dtype, num_splits, workspace, workspace_bytes, stream) -> int:
+    """``fa_fwd_kvcache`` with integer device pointers (or None for NULL); returns the status."""
+    return lib().fa_fwd_kvcache(q, k_cache, v_cache, o, lse, cache_seqlens, B, H, Hkv, Nq, Nk, d, scale, causal,
+                                alibi_slopes, dtype, num_splits, workspace, workspace_bytes, stream)
 
 
 def fa_bwd_workspace_size(B, H, Hkv, N, d, causal, varlen, dtype) -> int:
@@ -269,6 +284,44 @@ def attention_bwd(dout, q, k, v, o, lse, causal: bool = False, softmax_scale: Op
     if st != FA_OK:
         raise FaError(st)
     return dq, dk, dv
+
+
+def attention_kvcache(q, k_cache, v_cache, cache_seqlens, causal: bool = True,
+                      softmax_scale: Optional[float] = None, alibi_slopes: Optional[torch.Tensor] = None,
+                      num_splits: int = 0, workspace: Optional[torch.Tensor] = None):
+    """Decode through ``fa_fwd_kvcache``: q [B, Nq, H, d] against k_cache, v_cache
+    [B, Nk, Hkv, d] with int32 cache_seqlens [B]; returns (o [B, Nq, H, d], lse [B, H, Nq])."""
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        if not isinstance(t, torch.Tensor) or t.dim() != 4:
+            raise ValueError(f"{name} must be a 4-d tensor")
+    if not q.is_cuda:
+        raise ValueError("libfa takes device tensors (q is on the host)")
+    B, Nq, H, d = q.shape
+    Nk, Hkv = k_cache.shape[1], k_cache.shape[2]
+    dev, dt = q.device, q.dtype
+    if dt not in (torch.float16, torch.bfloat16):
+        raise ValueError("decode takes float16 or bfloat16")
+    _expect(q, "q", q.shape, dt, dev)
+    _expect(k_cache, "k_cache", (B, Nk, Hkv, d), dt, dev)
+    _expect(v_cache, "v_cache", (B, Nk, Hkv, d), dt, dev)
+    _expect(cache_seqlens, "cache_seqlens", (B,), torch.int32, dev)
+    if alibi_slopes is not None:
+        _expect(alibi_slopes, "alibi_slopes", (H,), torch.float32, dev)
+    if H % Hkv:
+        raise ValueError(f"query heads ({H}) must be a multiple of kv heads ({Hkv})")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    ws_bytes = fa_kvcache_workspace_size(B, H, Hkv, Nq, Nk, d, num_splits)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+    st = fa_fwd_kvcache(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                        cache_seqlens.data_ptr(), B, H, Hkv, Nq, Nk, d, scale, int(bool(causal)), _ptr(alibi_slopes),
+                        _DTYPE[dt], int(num_splits), _ptr(workspace),
+                        0 if workspace is None else workspace.numel() * workspace.element_size(), _stream_handle())
+    if st != FA_OK:
+        raise FaError(st)
+    return o, lse
 
 
 class FlashAttnFn(torch.autograd.Function):

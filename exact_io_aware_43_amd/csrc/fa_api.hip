@@ -1,6 +1,7 @@
 // C-ABI entry points of libfa (declared in include/fa.h): argument checks,
 // selection of the compiled kernel instance, and the launches. Every check runs
 // before the first launch, so a rejected call enqueues and writes nothing.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <mutex>
@@ -203,9 +204,86 @@ int bwd_launch(const void* q, const void* k, const void* v, const void* o, const
     return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+// Key ranges per (sequence, kv head) of a decode problem. num_splits = 0
+// aims at one workgroup per compute unit (measured on the decode workload:
+// 4 ranges per sequence and kv head streamed the caches at 5.1 TB/s, 16 at
+// 4.4 and 32 at 3.6, each range adding fixed set-up, merge and partial-write
+// cost) with at least 512 keys per range of an Nk-key cache; any count is
+// capped at one range per 128 keys. The device cuts each sequence's own
+// length into that many ranges.
+constexpr int kComputeUnits = 256;
+
+int decode_splits(int B, int H, int Hkv, int Nq, int Nk, int num_splits) {
+    const int tiles = (Nk + 127) / 128;
+    int S = num_splits;
+    if (S <= 0) {
+        const long long rgroups = ((long long)(H / Hkv) * Nq + 31) / 32;
+        const long long base = (long long)Hkv * rgroups * B;
+        S = (int)((kComputeUnits + base - 1) / base);
+        S = std::min(S, std::max(1, Nk / 512));
+    }
+    return std::max(1, std::min(S, tiles));
+}
+
+size_t decode_workspace_bytes(int B, int H, int Nq, int d, int splits) {
+    if (splits <= 1) return 0;
+    const size_t rows = (size_t)B * H * Nq * splits;
+    return (rows * (size_t)(d + 1) * sizeof(float) + 255) & ~(size_t)255;
+}
+
+int check_decode(int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal, int dtype) {
+    if (B <= 0 || H <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || d <= 0) return FA_ERR_INVALID_ARG;
+    if (H % Hkv != 0 || (causal != 0 && causal != 1) || !std::isfinite(scale)) return FA_ERR_INVALID_ARG;
+    if (!valid_dtype(dtype)) return FA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (dtype == FA_FP32) return FA_ERR_UNSUPPORTED;
+    if ((long long)B * Nk * Hkv >= (1ll << 31) || (long long)B * Nq * H >= (1ll << 31)) return FA_ERR_INVALID_ARG;
+    return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t fa_kvcache_workspace_size(int B, int H, int Hkv, int Nq, int Nk, int d, int num_splits) {
+    if (check_decode(B, H, Hkv, Nq, Nk, d, 1.0f, 0, FA_BF16) != FA_OK || num_splits < 0) return 0;
+    return decode_workspace_bytes(B, H, Nq, d, decode_splits(B, H, Hkv, Nq, Nk, num_splits));
+}
+
+int fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                   const int* cache_seqlens, int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                   const float* alibi_slopes, fa_dtype dtype, int num_splits, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+    if (!q || !k_cache || !v_cache || !o || !lse || !cache_seqlens || num_splits < 0) return FA_ERR_INVALID_ARG;
+    int st = check_decode(B, H, Hkv, Nq, Nk, d, scale, causal, (int)dtype);
+    if (st != FA_OK) return st;
+    const void* ptrs[] = {q, k_cache, v_cache, o, lse};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return FA_ERR_INVALID_ARG;
+    if (!aligned16(cache_seqlens) || (alibi_slopes && !aligned16(alibi_slopes))) return FA_ERR_INVALID_ARG;
+    fa::DecodeArgs a{};
+    a.splits = decode_splits(B, H, Hkv, Nq, Nk, num_splits);
+    const size_t need = decode_workspace_bytes(B, H, Nq, d, a.splits);
+    if (need > 0 && (!workspace || !aligned16(workspace) || workspace_bytes < need)) return FA_ERR_WORKSPACE;
+    a.q = q;
+    a.k = k_cache;
+    a.v = v_cache;
+    a.o = o;
+    a.lse = lse;
+    a.seqlens = cache_seqlens;
+    a.slopes = alibi_slopes;
+    a.part_o = reinterpret_cast<float*>(workspace);
+    a.part_lse = need > 0 ? a.part_o + (size_t)B * H * Nq * a.splits * d : nullptr;
+    a.B = B;
+    a.H = H;
+    a.Hkv = Hkv;
+    a.Nq = Nq;
+    a.Nk = Nk;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    hipError_t e = fa::launch_decode(a, (int)dtype, d, causal != 0, alibi_slopes != nullptr,
+                                     reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
 
 int fa_bwd_stages(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                   void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d, float scale, int causal,

@@ -38,6 +38,22 @@ struct Args {
     float drop_scale;
 };
 
+// A decode problem: Nq new queries per sequence against a cache of up to Nk
+// keys (seqlens[b] valid); each sequence's keys are cut into `splits` ranges.
+struct DecodeArgs {
+    const void* q;        // [B, Nq, H, d]
+    const void* k;        // [B, Nk, Hkv, d]
+    const void* v;
+    void* o;              // [B, Nq, H, d]
+    float* lse;           // [B, H, Nq]
+    const int* seqlens;   // [B], device
+    const float* slopes;  // [H] or NULL
+    float* part_o;        // splits > 1: [B, H, Nq, splits, d] fp32
+    float* part_lse;      //             [B, H, Nq, splits]
+    int B, H, Hkv, Nq, Nk, splits;
+    float scale_log2;
+};
+
 // Each returns hipSuccess or the launch error. `dtype` follows fa_dtype;
 // `drop` selects the instances with dropout (16-bit only).
 hipError_t launch_fwd_mfma(const Args& a, int dtype, int d, bool causal, bool alibi, bool drop, hipStream_t s);
@@ -47,5 +63,6 @@ hipError_t launch_bwd_dkdv(const Args& a, int dtype, int d, bool causal, bool al
 // `stages`: bit 0 = D pre-pass, bit 1 = dK/dV, bit 2 = dQ (enqueued in that order).
 hipError_t launch_bwd(const Args& a, int dtype, int d, bool causal, bool alibi, bool drop, unsigned stages,
                       hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, int dtype, int d, bool causal, bool alibi, hipStream_t s);
 
 }  // namespace fa

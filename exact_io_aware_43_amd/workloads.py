@@ -15,6 +15,8 @@ Named workloads (shapes of the pages' attention benchmarks, synthetic values):
 * ``varlen_alibi`` 32 packed sequences, lengths uniform in [64, 8192], H=16,
   d=128, bf16, causal, ALiBi slopes 2^(-8(h+1)/H), forward only.
 * ``gqa``          B=2, H=32, Hkv=8, N=8192, d=128, bf16, causal.
+* ``DECODE``       one new query per sequence, B=8, H=32, Hkv=8, against key/
+  value caches of 8192 .. 16384 keys (capacity 16384), d=128, bf16, causal.
 """
 
 from __future__ import annotations
@@ -26,7 +28,7 @@ from typing import Optional
 import numpy as np
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "alibi_slopes", "flops"]
+__all__ = ["Workload", "WORKLOADS", "DECODE", "make_inputs", "make_decode_inputs", "alibi_slopes", "flops"]
 
 
 @dataclass(frozen=True)
@@ -109,6 +111,32 @@ def make_inputs(w: Workload, seed: int = 0, lengths=None, with_grad: Optional[bo
     out["scale"] = 1.0 / math.sqrt(w.d)
     out["max_seqlen"] = max_seqlen
     return out
+
+
+# Decode over a key/value cache: one new query per sequence against caches of
+# 8192 .. 16384 keys (lengths drawn from the seed), GQA with 4 query heads per
+# kv head (the shape of the long-context workloads above).
+DECODE = (Workload("decode", "bf16", 8, 32, 8, 16384, 128, causal=True, backward=False), 1, None)
+
+
+def make_decode_inputs(w: Workload, Nq: int, lengths=None, seed: int = 0) -> dict:
+    """Inputs of a decode call: q [B, Nq, H, d], k_cache / v_cache [B, N, Hkv, d]
+    (N = w.N, the cache capacity) and int32 cache_seqlens [B]. Draw order:
+    lengths (uniform in [N/2, N] unless given), Q, K cache, V cache; values are
+    fp32 standard normals times ``std`` rounded to the storage type."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if lengths is None:
+        lengths = rng.integers(w.N // 2, w.N + 1, size=w.B)
+    lengths = np.asarray(lengths, dtype=np.int64)
+    return {
+        "q": _normal(rng, (w.B, Nq, w.H, w.d), w.std, w.dtype),
+        "k_cache": _normal(rng, (w.B, w.N, w.Hkv, w.d), w.std, w.dtype),
+        "v_cache": _normal(rng, (w.B, w.N, w.Hkv, w.d), w.std, w.dtype),
+        "cache_seqlens": torch.from_numpy(lengths.astype(np.int32)),
+        "alibi_slopes": alibi_slopes(w.H) if w.alibi else None,
+        "scale": 1.0 / math.sqrt(w.d),
+        "Nq": Nq,
+    }
 
 
 def seq_lengths(inputs: dict, w: Workload) -> list:

@@ -119,6 +119,45 @@ int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* 
                    void* stream);
 
 /*
+ * Decode over a key/value cache: attention of Nq new queries per sequence
+ * against a cache of keys and values (the inference workload the page's
+ * Limitations section sets apart from training, "long context and inference
+ * remain unsolved"). The keys are split into ranges processed in parallel,
+ * and the partial states merge exactly (Key design 2: the (m, l, O) state of
+ * disjoint key sets combines with m = max m_s, l = sum l_s e^(m_s - m)).
+ *
+ *   q             : [B, Nq, H, d]; o : [B, Nq, H, d] (written); lse : float
+ *                   [B, H, Nq] (written; -inf for a query that sees no key).
+ *   k_cache, v_cache : [B, Nk, Hkv, d]; sequence b uses its first
+ *                   cache_seqlens[b] rows.
+ *   cache_seqlens : int32 [B], device memory: L_b, the valid keys of sequence
+ *                   b, the new tokens included; lengths above Nk are treated
+ *                   as Nk and negative ones as 0 (not checked on the host).
+ *   causal        : 1 aligns the mask to the end of the cache: query t sits at
+ *                   position L_b - Nq + t and keeps keys j <= L_b - Nq + t.
+ *   alibi_slopes  : float [H] or NULL; the bias is -slope_h |position - j|.
+ *   num_splits    : key ranges per sequence and kv head (each sequence's
+ *                   L_b keys are cut into that many ranges of ceil(L_b / S)
+ *                   keys rounded up to 32); 0 lets the library pick from the
+ *                   sizes (about one workgroup per compute unit, at least
+ *                   512 keys per range of an Nk-key cache). At most one range
+ *                   per 128 keys of Nk is used.
+ *   workspace     : fp32 partial results when more than one range is used,
+ *                   fa_kvcache_workspace_size(...) bytes (0: NULL allowed).
+ *
+ * FA_BF16 and FA_FP16 only (FA_FP32 is FA_ERR_UNSUPPORTED); d in {64, 128}.
+ * Other conventions (alignment, asynchrony, errors) as fa_fwd.
+ */
+size_t fa_kvcache_workspace_size(int B, int H, int Hkv, int Nq, int Nk, int d,
+                                 int num_splits);
+
+int fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, void* o,
+                   float* lse, const int* cache_seqlens, int B, int H, int Hkv,
+                   int Nq, int Nk, int d, float scale, int causal,
+                   const float* alibi_slopes, fa_dtype dtype, int num_splits,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Bytes of device scratch fa_bwd needs for these sizes: the per-row
  * D_i = dO_i . O_i of Key design 3 and the row statistic rescaled to log2
  * units, both fp32 [B, H, N64] with N64 = N rounded up to a multiple of 64

@@ -31,7 +31,8 @@ def declared_functions():
 def test_header_declares_expected_api():
     assert declared_functions() == sorted(
         ["fa_fwd", "fa_fwd_dropout", "fa_bwd", "fa_bwd_dropout", "fa_bwd_stages", "fa_bwd_workspace_size",
-         "fa_bwd_noalloc", "fa_bwd_noalloc_max_bytes", "fa_strerror", "fa_version"])
+         "fa_bwd_noalloc", "fa_bwd_noalloc_max_bytes", "fa_fwd_kvcache", "fa_kvcache_workspace_size",
+         "fa_strerror", "fa_version"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -255,3 +256,41 @@ def test_dropout_rejects_like_plain_calls():
          None, fa.FA_BF16, 0.1, 1, 0]
     assert fa.fa_bwd_dropout(*b, None, 1 << 20, None) == WORKSPACE
     assert fa.fa_bwd_dropout(*b, PTR[9], 16, None) == WORKSPACE
+
+
+def test_kvcache_workspace_size():
+    # one split: nothing needed
+    assert fa.fa_kvcache_workspace_size(1, 8, 8, 1, 100, 128, 1) == 0
+    # explicit splits: fp32 O and lse per (sequence, head, query, split)
+    assert fa.fa_kvcache_workspace_size(2, 8, 2, 3, 4096, 128, 4) == ((2 * 8 * 3 * 4 * 129 * 4 + 255) & ~255)
+    # at most one split per 128 keys of the capacity
+    assert fa.fa_kvcache_workspace_size(1, 4, 4, 1, 300, 64, 64) == ((1 * 4 * 1 * 3 * 65 * 4 + 255) & ~255)
+    # auto: one workgroup per compute unit, at least 512 keys per range
+    assert fa.fa_kvcache_workspace_size(8, 32, 8, 1, 16384, 128, 0) == ((8 * 32 * 1 * 4 * 129 * 4 + 255) & ~255)
+    assert fa.fa_kvcache_workspace_size(1, 8, 1, 1, 2048, 128, 0) == ((1 * 8 * 1 * 4 * 129 * 4 + 255) & ~255)
+    # auto: a deterministic choice; a large batch of heads needs no split
+    assert fa.fa_kvcache_workspace_size(64, 64, 64, 1, 4096, 128, 0) == 0
+    assert fa.fa_kvcache_workspace_size(1, 8, 1, 1, 65536, 128, 0) > 0
+    for bad in [(0, 8, 8, 1, 100, 128, 0), (1, 8, 3, 1, 100, 128, 0), (1, 8, 8, 0, 100, 128, 0),
+                (1, 8, 8, 1, 0, 128, 0), (1, 8, 8, 1, 100, 96, 0), (1, 8, 8, 1, 100, 128, -1)]:
+        assert fa.fa_kvcache_workspace_size(*bad) == 0
+
+
+def _kv(**kw):
+    a = dict(q=PTR[0], k=PTR[1], v=PTR[2], o=PTR[3], lse=PTR[4], cl=PTR[5], B=2, H=8, Hkv=2, Nq=1, Nk=4096, d=128,
+             scale=0.125, causal=1, alibi=None, dtype=fa.FA_BF16, splits=4, ws=PTR[6], ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return fa.fa_fwd_kvcache(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cl"], a["B"], a["H"], a["Hkv"], a["Nq"],
+                             a["Nk"], a["d"], a["scale"], a["causal"], a["alibi"], a["dtype"], a["splits"], a["ws"],
+                             a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), INVALID), (dict(cl=None), INVALID), (dict(lse=None), INVALID), (dict(H=6, Hkv=4), INVALID),
+    (dict(Nq=0), INVALID), (dict(Nk=0), INVALID), (dict(causal=3), INVALID), (dict(splits=-2), INVALID),
+    (dict(scale=math.nan), INVALID), (dict(d=256), UNSUPPORTED), (dict(dtype=fa.FA_FP32), UNSUPPORTED),
+    (dict(k=PTR[1] + 4), INVALID), (dict(cl=PTR[5] + 4), INVALID),
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=100), WORKSPACE), (dict(ws=PTR[6] + 8), WORKSPACE),
+])
+def test_kvcache_rejects(kw, expect):
+    assert _kv(**kw) == expect
