@@ -86,6 +86,9 @@ def parse():
                     help="drop probability of the fused dropout (fa_fwd_dropout / fa_bwd_dropout); 0 = none")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the measurement run a plain 1 GiB fp32 copy (negation) for counter calibration")
+    ap.add_argument("--counters-from", nargs="+", metavar="DIR",
+                    help="summarise rocprofv3 --pmc runs of this script (any counters, one or more directories) as "
+                         "a per-kernel Markdown table (mean per dispatch) and exit; needs no GPU")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, both "
                          "with --copy-calibration) into profiles/traffic.json and exit; needs no GPU")
@@ -94,6 +97,9 @@ def parse():
 
 def main():
     args = parse()
+    if args.counters_from:
+        print(summarise_counters(args.counters_from))
+        return
     if args.traffic_from:
         summarise_traffic(args.workload, *args.traffic_from)
         return
@@ -488,6 +494,32 @@ def _counter_rows(d):
         with open(fn) as f:
             for r in csv.DictReader(f):
                 yield r["Kernel_Name"], (fn, r["Dispatch_Id"]), r["Counter_Name"], float(r["Counter_Value"])
+
+
+def summarise_counters(dirs):
+    """Per-kernel mean of every counter over its dispatches, from rocprofv3 --pmc
+    CSV directories, as a Markdown table (kernels by the symbols bench.py
+    launches; rows without a known symbol are skipped)."""
+    acc = {}
+    for d in dirs:
+        for name, disp, cname, val in _counter_rows(d):
+            key = next((k for k, sym in KERNEL_SYMBOLS.items() if sym in name), None)
+            if key is None:
+                continue
+            acc.setdefault(key, {}).setdefault(cname, {}).setdefault(disp, 0.0)
+            acc[key][cname][disp] += val
+    counters = sorted({c for k in acc.values() for c in k})
+    lines = ["| kernel | dispatches | " + " | ".join(counters) + " |", "|" + "---|" * (len(counters) + 2)]
+    for k in KERNEL_SYMBOLS:
+        if k not in acc:
+            continue
+        n = max(len(v) for v in acc[k].values())
+        cells = []
+        for c in counters:
+            vals = acc[k].get(c)
+            cells.append("—" if not vals else f"{sum(vals.values()) / len(vals):.4g}")
+        lines.append(f"| {k} | {n} | " + " | ".join(cells) + " |")
+    return "\n".join(lines)
 
 
 def _per_dispatch(d, counter):

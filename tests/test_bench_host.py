@@ -91,3 +91,18 @@ def test_source_hash_follows_the_kernel_sources():
     # the pre-pass and dQ kernels share one source file and its dependencies
     assert h["bwd_dsum"] == h["bwd_dq"]
     assert len({h["fwd"], h["bwd_dkdv"], h["bwd_dq"]}) == 3
+
+
+def test_counter_summary_means_per_dispatch(tmp_path):
+    b = _bench()
+    d = str(tmp_path / "pmc")
+    _write_counters(d, [
+        (1, "void fa::(anonymous namespace)::fwd_mfma_kernel<__bf16, 128, true, false, false>(fa::Args)", "MfmaUtil", 40.0),
+        (2, "void fa::(anonymous namespace)::fwd_mfma_kernel<__bf16, 128, true, false, false>(fa::Args)", "MfmaUtil", 60.0),
+        (3, "void fa::(anonymous namespace)::bwd_dq_kernel<__bf16, 128, true, false, false>(fa::Args)", "LdsUtil", 70.0),
+        (4, "neg_kernel", "MfmaUtil", 1.0),
+    ])
+    out = b.summarise_counters([d])
+    assert "| fwd | 2 | — | 50 |" in out.replace("50.0", "50")
+    assert "| bwd_dq | 1 | 70 | — |" in out
+    assert "neg" not in out
