@@ -54,6 +54,14 @@ the design notes of the repository):
    probabilities that multiply V are dropped with a counter-based mask and the
    kept ones scaled so their expectation is unchanged. The mask is defined in
    oracle/philox.py.
+9. Sliding window (named only: the usage contract's mask row lists sliding
+   window next to ALiBi and softcapping): ``window`` = (left, right) keeps key
+   j for query i when i - left <= j <= i + right; a negative bound is
+   unbounded. Positions are within a sequence, and causal masking applies as
+   well (so right is effectively 0 under it).
+10. Softcapping (named only, same row): the scaled score u = scale * <q_i, k_j>
+   becomes cap * tanh(u / cap) for cap > 0, before the ALiBi bias and the masks;
+   by the chain rule the gradient reaching u is dS * (1 - tanh(u / cap)^2).
 """
 
 from __future__ import annotations
@@ -93,16 +101,35 @@ def _bias(rows: np.ndarray, n_keys: int, slope: float) -> np.ndarray:
     return -slope * np.abs(rows.astype(np.float64)[:, None] - j[None, :])
 
 
-def _scores(qh, kh, scale, causal, slope, rows=None):
-    """S = scale * Q K^T + beta with the causal entries set to -inf ([PN] Key design 1)."""
+def _allowed(rows: np.ndarray, n_keys: int, causal: bool, window) -> np.ndarray:
+    """Boolean [len(rows), n_keys]: key j visible from query position i (readings 3 and 9)."""
+    i = rows.astype(np.int64)[:, None]
+    j = np.arange(n_keys, dtype=np.int64)[None, :]
+    ok = np.ones((len(rows), n_keys), dtype=bool)
+    if causal:
+        ok &= j <= i
+    if window is not None:
+        left, right = window
+        if left >= 0:
+            ok &= j >= i - left
+        if right >= 0:
+            ok &= j <= i + right
+    return ok
+
+
+def _scores(qh, kh, scale, causal, slope, rows=None, window=None, softcap=0.0):
+    """S = cap(scale * Q K^T) + beta with the masked entries set to -inf ([PN] Key design 1;
+    softcapping and the window are readings 10 and 9)."""
     n = kh.shape[0]
     if rows is None:
         rows = np.arange(qh.shape[0])
     s = scale * (qh @ kh.T)
+    if softcap > 0.0:
+        s = softcap * np.tanh(s / softcap)
     if slope is not None:
         s = s + _bias(rows, n, slope)
-    if causal:
-        s = np.where(np.arange(n)[None, :] > rows[:, None], -np.inf, s)
+    if causal or window is not None:
+        s = np.where(_allowed(rows, n, causal, window), s, -np.inf)
     return s
 
 
@@ -114,38 +141,40 @@ def _softmax_rows(s):
     return e / ell[:, None], m + np.log(ell)
 
 
-def head_fwd(qh, kh, vh, scale, causal=False, slope=None, keep=None, keep_scale=1.0):
+def head_fwd(qh, kh, vh, scale, causal=False, slope=None, keep=None, keep_scale=1.0, window=None, softcap=0.0):
     """One (sequence, head): O = softmax(S) V and lse. Arrays are [n, d] fp64.
 
     With a dropout mask ``keep`` [n, n] (boolean), O = (P o keep * keep_scale) V:
     the softmax and lse use every score; dropout acts on the probabilities
     that multiply V ([PN] Key design 1 stage table)."""
-    p, lse = _softmax_rows(_scores(qh, kh, scale, causal, slope))
+    p, lse = _softmax_rows(_scores(qh, kh, scale, causal, slope, window=window, softcap=softcap))
     if keep is not None:
         p = np.where(keep, p * keep_scale, 0.0)
     return p @ vh, lse
 
 
-def head_rows_fwd(qh, kh, vh, rows, scale, causal=False, slope=None):
+def head_rows_fwd(qh, kh, vh, rows, scale, causal=False, slope=None, window=None, softcap=0.0):
     """O and lse for the query positions ``rows`` only (the full K and V are used).
 
     Row i of the output depends only on q_i, K and V, so a sample of rows can be
     checked at sizes where a whole N x N matrix per head would be wasteful.
     """
     rows = np.asarray(rows, dtype=np.int64)
-    p, lse = _softmax_rows(_scores(qh[rows], kh, scale, causal, slope, rows=rows))
+    p, lse = _softmax_rows(_scores(qh[rows], kh, scale, causal, slope, rows=rows, window=window, softcap=softcap))
     return p @ vh, lse
 
 
-def head_bwd(qh, kh, vh, doh, scale, causal=False, slope=None, keep=None, keep_scale=1.0):
+def head_bwd(qh, kh, vh, doh, scale, causal=False, slope=None, keep=None, keep_scale=1.0, window=None,
+             softcap=0.0):
     """Gradients of sum(O * dO) for one (sequence, head), by recomputing P ([PN] Key design 3).
 
     D_i is taken from its definition sum_j P_ij dP_ij; the identity D_i = dO_i . O_i
     stated on the page is checked by the tests, not assumed here. With a dropout
     mask, O = (P o keep * keep_scale) V, so dV uses the dropped probabilities and
-    the gradient reaching P is (dO V^T) o keep * keep_scale.
+    the gradient reaching P is (dO V^T) o keep * keep_scale. With softcapping the
+    gradient reaching the scaled score u is dS * (1 - tanh(u / cap)^2) (reading 10).
     """
-    p, _ = _softmax_rows(_scores(qh, kh, scale, causal, slope))
+    p, _ = _softmax_rows(_scores(qh, kh, scale, causal, slope, window=window, softcap=softcap))
     pd = p if keep is None else np.where(keep, p * keep_scale, 0.0)
     dv = pd.T @ doh
     dp = doh @ vh.T
@@ -153,6 +182,8 @@ def head_bwd(qh, kh, vh, doh, scale, causal=False, slope=None, keep=None, keep_s
         dp = np.where(keep, dp * keep_scale, 0.0)
     dcorr = (p * dp).sum(axis=1)
     ds = p * (dp - dcorr[:, None])
+    if softcap > 0.0:
+        ds = ds * (1.0 - np.tanh(scale * (qh @ kh.T) / softcap) ** 2)
     dq = scale * (ds @ kh)
     dk = scale * (ds.T @ qh)
     return dq, dk, dv
@@ -186,13 +217,15 @@ def _dropout(dropout, n, b, h, H):
     return PX.dropout_keep(n, n, b, h, H, seed, offset, K), 256.0 / K
 
 
-def attention_fwd(q, k, v, scale=None, causal=False, alibi_slopes=None, cu_seqlens=None, dropout=None):
+def attention_fwd(q, k, v, scale=None, causal=False, alibi_slopes=None, cu_seqlens=None, dropout=None,
+                  window=None, softcap=0.0):
     """Exact attention forward in fp64.
 
     Dense: q [B, N, H, d], k and v [B, N, Hkv, d]. Packed (``cu_seqlens`` given):
     q [T, H, d], k and v [T, Hkv, d]. Returns (o, lse): o in q's layout, lse
     [B, H, Nmax] (NaN past each sequence's end). ``dropout`` = (p_drop, seed,
-    offset) applies the mask defined in oracle/philox.py.
+    offset) applies the mask defined in oracle/philox.py; ``window`` = (left,
+    right) and ``softcap`` are readings 9 and 10.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     H, Hkv, G = _heads(q, k)
@@ -210,13 +243,14 @@ def attention_fwd(q, k, v, scale=None, causal=False, alibi_slopes=None, cu_seqle
             g = h // G
             keep, ks = _dropout(dropout, n, b, h, H)
             oh, lh = head_fwd(q[idx][:, h], k[idx][:, g], v[idx][:, g], scale, causal,
-                              None if slopes is None else slopes[h], keep, ks)
+                              None if slopes is None else slopes[h], keep, ks, window, softcap)
             o[idx + (h,)] = oh
             lse[b, h, :n] = lh
     return o, lse
 
 
-def attention_bwd(q, k, v, do, scale=None, causal=False, alibi_slopes=None, cu_seqlens=None, dropout=None):
+def attention_bwd(q, k, v, do, scale=None, causal=False, alibi_slopes=None, cu_seqlens=None, dropout=None,
+                  window=None, softcap=0.0):
     """Exact attention backward in fp64: (dq, dk, dv) of the loss sum(O * dO).
 
     Layouts as in :func:`attention_fwd`. dk and dv of a kv head sum over its
@@ -235,7 +269,7 @@ def attention_bwd(q, k, v, do, scale=None, causal=False, alibi_slopes=None, cu_s
             g = h // G
             keep, ks = _dropout(dropout, n, b, h, H)
             gq, gk, gv = head_bwd(q[idx][:, h], k[idx][:, g], v[idx][:, g], do[idx][:, h], scale,
-                                  causal, None if slopes is None else slopes[h], keep, ks)
+                                  causal, None if slopes is None else slopes[h], keep, ks, window, softcap)
             dq[idx + (h,)] = gq
             dk[idx + (g,)] += gk
             dv[idx + (g,)] += gv
@@ -346,7 +380,8 @@ def decode_fwd(q, k_cache, v_cache, cache_seqlens, scale=None, causal=True, alib
     return o, lse
 
 
-def brute_fwd(q, k, v, scale=None, causal=False, alibi_slopes=None, cu_seqlens=None, dropout=None):
+def brute_fwd(q, k, v, scale=None, causal=False, alibi_slopes=None, cu_seqlens=None, dropout=None,
+              window=None, softcap=0.0):
     """Scalar-loop attention with textbook softmax, for tiny inputs (N <= 8).
 
     Pure Python: nested lists, ``math.exp`` and running sums, no BLAS and no
@@ -370,13 +405,21 @@ def brute_fwd(q, k, v, scale=None, causal=False, alibi_slopes=None, cu_seqlens=N
             g = h // G
             keep, kscale = _dropout(dropout, n, b, h, H)
             for i in range(n):
-                keys = range(i + 1) if causal else range(n)
+                lo, hi = 0, (i + 1 if causal else n)
+                if window is not None:
+                    if window[0] >= 0:
+                        lo = max(lo, i - window[0])
+                    if window[1] >= 0:
+                        hi = min(hi, i + window[1] + 1)
+                keys = range(lo, hi)
                 w = []
                 for j in keys:
                     s = 0.0
                     for c in range(d):
                         s += qs[i][h][c] * ks[j][g][c]
                     s *= scale
+                    if softcap > 0.0:
+                        s = softcap * math.tanh(s / softcap)
                     if slopes is not None:
                         s -= slopes[h] * abs(i - j)
                     w.append(math.exp(s))

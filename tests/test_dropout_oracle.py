@@ -189,10 +189,12 @@ def test_planted_dropout_mistakes(monkeypatch):
     q, k, v = _rand(rng, 1, 6, 2, 3), _rand(rng, 1, 6, 2, 3), _rand(rng, 1, 6, 2, 3)
     orig_fwd, orig_bwd = OA.head_fwd, OA.head_bwd
 
-    def fwd_no_scale(qh, kh, vh, scale, causal=False, slope=None, keep=None, keep_scale=1.0):
-        return orig_fwd(qh, kh, vh, scale, causal, slope, keep, 1.0)
+    def fwd_no_scale(qh, kh, vh, scale, causal=False, slope=None, keep=None, keep_scale=1.0, window=None,
+                     softcap=0.0):
+        return orig_fwd(qh, kh, vh, scale, causal, slope, keep, 1.0, window, softcap)
 
-    def bwd_dp_unmasked(qh, kh, vh, doh, scale, causal=False, slope=None, keep=None, keep_scale=1.0):
+    def bwd_dp_unmasked(qh, kh, vh, doh, scale, causal=False, slope=None, keep=None, keep_scale=1.0, window=None,
+                        softcap=0.0):
         dq, dk, _ = orig_bwd(qh, kh, vh, doh, scale, causal, slope)
         _, _, dv = orig_bwd(qh, kh, vh, doh, scale, causal, slope, keep, keep_scale)
         return dq, dk, dv

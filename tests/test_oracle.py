@@ -368,11 +368,11 @@ def _mutant(**overrides):
     return mod
 
 
-def _m_scores_no_scale(qh, kh, scale, causal, slope, rows=None):
-    return OA._scores(qh, kh, 1.0, causal, slope, rows)
+def _m_scores_no_scale(qh, kh, scale, causal, slope, rows=None, window=None, softcap=0.0):
+    return OA._scores(qh, kh, 1.0, causal, slope, rows, window, softcap)
 
 
-def _m_scores_transposed(qh, kh, scale, causal, slope, rows=None):
+def _m_scores_transposed(qh, kh, scale, causal, slope, rows=None, window=None, softcap=0.0):
     n = kh.shape[0]
     rows = np.arange(qh.shape[0]) if rows is None else rows
     s = scale * (kh @ qh.T)[: len(rows)] if kh.shape[0] == qh.shape[0] else scale * (qh @ kh.T)
@@ -383,12 +383,12 @@ def _m_scores_transposed(qh, kh, scale, causal, slope, rows=None):
     return s
 
 
-def _m_scores_alibi_sign(qh, kh, scale, causal, slope, rows=None):
-    return OA._scores(qh, kh, scale, causal, None if slope is None else -slope, rows)
+def _m_scores_alibi_sign(qh, kh, scale, causal, slope, rows=None, window=None, softcap=0.0):
+    return OA._scores(qh, kh, scale, causal, None if slope is None else -slope, rows, window, softcap)
 
 
-def _m_scores_mask_off_by_one(qh, kh, scale, causal, slope, rows=None):
-    s = OA._scores(qh, kh, scale, False, slope, rows)
+def _m_scores_mask_off_by_one(qh, kh, scale, causal, slope, rows=None, window=None, softcap=0.0):
+    s = OA._scores(qh, kh, scale, False, slope, rows, window, softcap)
     if causal:
         n = kh.shape[0]
         rows = np.arange(qh.shape[0]) if rows is None else rows
@@ -401,20 +401,23 @@ def _m_softmax_no_max_in_lse(s):
     return p, lse - s.max(axis=1)
 
 
-def _m_head_bwd_no_scale(qh, kh, vh, doh, scale, causal=False, slope=None, keep=None, keep_scale=1.0):
-    dq, dk, dv = OA.head_bwd(qh, kh, vh, doh, scale, causal, slope, keep, keep_scale)
+def _m_head_bwd_no_scale(qh, kh, vh, doh, scale, causal=False, slope=None, keep=None, keep_scale=1.0, window=None,
+                         softcap=0.0):
+    dq, dk, dv = OA.head_bwd(qh, kh, vh, doh, scale, causal, slope, keep, keep_scale, window, softcap)
     return dq / scale, dk, dv
 
 
-def _m_head_bwd_ds_sign(qh, kh, vh, doh, scale, causal=False, slope=None, keep=None, keep_scale=1.0):
+def _m_head_bwd_ds_sign(qh, kh, vh, doh, scale, causal=False, slope=None, keep=None, keep_scale=1.0, window=None,
+                        softcap=0.0):
     p, _ = OA._softmax_rows(OA._scores(qh, kh, scale, causal, slope))
     dp = doh @ vh.T
     ds = p * (dp + (p * dp).sum(axis=1)[:, None])
     return scale * ds @ kh, scale * ds.T @ qh, p.T @ doh
 
 
-def _m_head_bwd_dv_untransposed(qh, kh, vh, doh, scale, causal=False, slope=None, keep=None, keep_scale=1.0):
-    dq, dk, _ = OA.head_bwd(qh, kh, vh, doh, scale, causal, slope, keep, keep_scale)
+def _m_head_bwd_dv_untransposed(qh, kh, vh, doh, scale, causal=False, slope=None, keep=None, keep_scale=1.0,
+                                window=None, softcap=0.0):
+    dq, dk, _ = OA.head_bwd(qh, kh, vh, doh, scale, causal, slope, keep, keep_scale, window, softcap)
     p, _ = OA._softmax_rows(OA._scores(qh, kh, scale, causal, slope))
     return dq, dk, p @ doh
 
