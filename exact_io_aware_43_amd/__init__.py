@@ -22,7 +22,9 @@ from ._binding import (  # noqa: F401
     attention_kvcache,
     fa_bwd,
     fa_bwd_dropout,
+    fa_bwd_ext,
     fa_fwd_dropout,
+    fa_fwd_ext,
     fa_bwd_noalloc,
     fa_bwd_noalloc_max_bytes,
     fa_bwd_stages,

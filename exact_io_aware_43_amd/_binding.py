@@ -47,6 +47,10 @@ def lib() -> ctypes.CDLL:
         L.fa_fwd_dropout.restype = ci
         L.fa_bwd_dropout.argtypes = L.fa_bwd.argtypes[:-3] + [cf, u64, u32, vp, sz, vp]
         L.fa_bwd_dropout.restype = ci
+        L.fa_fwd_ext.argtypes = L.fa_fwd.argtypes[:-1] + [ci, ci, cf, cf, u64, u32, vp]
+        L.fa_fwd_ext.restype = ci
+        L.fa_bwd_ext.argtypes = L.fa_bwd.argtypes[:-3] + [ci, ci, cf, cf, u64, u32, vp, sz, vp]
+        L.fa_bwd_ext.restype = ci
         L.fa_kvcache_workspace_size.argtypes = [ci] * 7
         L.fa_kvcache_workspace_size.restype = sz
         L.fa_fwd_kvcache.argtypes = [vp] * 6 + [ci] * 6 + [cf, ci, vp, ci, ci, vp, sz, vp]
@@ -82,6 +86,21 @@ def fa_bwd_dropout(q, k, v, o, dout, lse, dq, dk, dv, B, H, Hkv, N, d, scale, ca
     """``fa_bwd_dropout`` with integer device pointers (or None for NULL); returns the status."""
     return lib().fa_bwd_dropout(q, k, v, o, dout, lse, dq, dk, dv, B, H, Hkv, N, d, scale, causal, alibi_slopes,
                                 cu_seqlens, dtype, p_drop, seed, offset, workspace, workspace_bytes, stream)
+
+
+def fa_fwd_ext(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, alibi_slopes, cu_seqlens, dtype, window_left,
+               window_right, softcap, p_drop, seed, offset, stream) -> int:
+    """``fa_fwd_ext`` with integer device pointers (or None for NULL); returns the status."""
+    return lib().fa_fwd_ext(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, alibi_slopes, cu_seqlens, dtype,
+                            window_left, window_right, softcap, p_drop, seed, offset, stream)
+
+
+def fa_bwd_ext(q, k, v, o, dout, lse, dq, dk, dv, B, H, Hkv, N, d, scale, causal, alibi_slopes, cu_seqlens, dtype,
+               window_left, window_right, softcap, p_drop, seed, offset, workspace, workspace_bytes, stream) -> int:
+    """``fa_bwd_ext`` with integer device pointers (or None for NULL); returns the status."""
+    return lib().fa_bwd_ext(q, k, v, o, dout, lse, dq, dk, dv, B, H, Hkv, N, d, scale, causal, alibi_slopes,
+                            cu_seqlens, dtype, window_left, window_right, softcap, p_drop, seed, offset, workspace,
+                            workspace_bytes, stream)
 
 
 def fa_kvcache_workspace_size(B, H, Hkv, Nq, Nk, d, num_splits) -> int:
@@ -232,14 +251,17 @@ def validate(q, k, v, *, cu_seqlens=None, max_seqlen=None, alibi_slopes=None, q_
 def attention(q, k, v, causal: bool = False, softmax_scale: Optional[float] = None,
               alibi_slopes: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None,
               max_seqlen: Optional[int] = None, out: Optional[torch.Tensor] = None,
-              lse: Optional[torch.Tensor] = None, dropout_p: float = 0.0, seed: int = 0, offset: int = 0):
+              lse: Optional[torch.Tensor] = None, dropout_p: float = 0.0, seed: int = 0, offset: int = 0,
+              window_size=(-1, -1), softcap: float = 0.0):
     """Exact attention forward through ``fa_fwd`` (``fa_fwd_dropout`` when
-    ``dropout_p`` > 0): returns (o, lse).
+    ``dropout_p`` > 0, ``fa_fwd_ext`` with a window or softcapping): returns
+    (o, lse).
 
-    Mirrors ``flash_attn_func(q, k, v, dropout_p, softmax_scale, causal)``; the
-    dropout mask is the generator's (``seed``, ``offset``), which the backward
-    call must repeat. ``lse`` is fp32 [B, H, N] (N = max_seqlen for packed
-    inputs). Every tensor is validated against the layouts of the C ABI.
+    Mirrors ``flash_attn_func(q, k, v, dropout_p, softmax_scale, causal,
+    window_size, softcap)``; the dropout mask is the generator's (``seed``,
+    ``offset``), which the backward call must repeat. ``lse`` is fp32
+    [B, H, N] (N = max_seqlen for packed inputs). Every tensor is validated
+    against the layouts of the C ABI.
     """
     B, H, Hkv, N, d = validate(q, k, v, cu_seqlens=cu_seqlens, max_seqlen=max_seqlen, alibi_slopes=alibi_slopes,
                                q_like=(() if out is None else (("out", out),)), lse=lse)
@@ -248,7 +270,10 @@ def attention(q, k, v, causal: bool = False, softmax_scale: Optional[float] = No
     l = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(), B, H, Hkv, N, d, scale,
             int(bool(causal)), _ptr(alibi_slopes), _ptr(cu_seqlens), _DTYPE[q.dtype])
-    if dropout_p:
+    wl, wr = (int(x) for x in window_size)
+    if (wl, wr) != (-1, -1) or softcap:
+        st = fa_fwd_ext(*args, wl, wr, float(softcap), float(dropout_p), int(seed), int(offset), _stream_handle())
+    elif dropout_p:
         st = fa_fwd_dropout(*args, float(dropout_p), int(seed), int(offset), _stream_handle())
     else:
         st = fa_fwd(*args, _stream_handle())
@@ -260,9 +285,11 @@ def attention(q, k, v, causal: bool = False, softmax_scale: Optional[float] = No
 def attention_bwd(dout, q, k, v, o, lse, causal: bool = False, softmax_scale: Optional[float] = None,
                   alibi_slopes: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None,
                   max_seqlen: Optional[int] = None, workspace: Optional[torch.Tensor] = None,
-                  dropout_p: float = 0.0, seed: int = 0, offset: int = 0):
+                  dropout_p: float = 0.0, seed: int = 0, offset: int = 0, window_size=(-1, -1),
+                  softcap: float = 0.0):
     """Exact attention backward through ``fa_bwd`` (``fa_bwd_dropout`` when
-    ``dropout_p`` > 0, with the forward's seed and offset): returns (dq, dk, dv)."""
+    ``dropout_p`` > 0, with the forward's seed and offset; ``fa_bwd_ext`` with a
+    window or softcapping): returns (dq, dk, dv)."""
     B, H, Hkv, N, d = validate(q, k, v, cu_seqlens=cu_seqlens, max_seqlen=max_seqlen, alibi_slopes=alibi_slopes,
                                q_like=(("o", o), ("dout", dout)), lse=lse)
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
@@ -277,7 +304,10 @@ def attention_bwd(dout, q, k, v, o, lse, causal: bool = False, softmax_scale: Op
             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, N, d, scale, int(bool(causal)),
             _ptr(alibi_slopes), _ptr(cu_seqlens), dt)
     ws = (workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream_handle())
-    if dropout_p:
+    wl, wr = (int(x) for x in window_size)
+    if (wl, wr) != (-1, -1) or softcap:
+        st = fa_bwd_ext(*args, wl, wr, float(softcap), float(dropout_p), int(seed), int(offset), *ws)
+    elif dropout_p:
         st = fa_bwd_dropout(*args, float(dropout_p), int(seed), int(offset), *ws)
     else:
         st = fa_bwd(*args, *ws)
@@ -329,16 +359,17 @@ class FlashAttnFn(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, q, k, v, causal=False, softmax_scale=None, alibi_slopes=None, cu_seqlens=None,
-                max_seqlen=None, dropout_p=0.0, seed=0, offset=0):
+                max_seqlen=None, dropout_p=0.0, seed=0, offset=0, window_size=(-1, -1), softcap=0.0):
         o, lse = attention(q, k, v, causal, softmax_scale, alibi_slopes, cu_seqlens, max_seqlen,
-                           dropout_p=dropout_p, seed=seed, offset=offset)
+                           dropout_p=dropout_p, seed=seed, offset=offset, window_size=window_size, softcap=softcap)
         ctx.save_for_backward(q, k, v, o, lse)
         ctx.args = (causal, softmax_scale, alibi_slopes, cu_seqlens, max_seqlen)
-        ctx.drop = dict(dropout_p=dropout_p, seed=seed, offset=offset)  # the saved generator state
+        # the saved generator state and mask variants
+        ctx.drop = dict(dropout_p=dropout_p, seed=seed, offset=offset, window_size=window_size, softcap=softcap)
         return o
 
     @staticmethod
     def backward(ctx, do):
         q, k, v, o, lse = ctx.saved_tensors
         dq, dk, dv = attention_bwd(do.contiguous(), q, k, v, o, lse, *ctx.args, **ctx.drop)
-        return dq, dk, dv, None, None, None, None, None, None, None, None
+        return dq, dk, dv, None, None, None, None, None, None, None, None, None, None

@@ -52,7 +52,34 @@ fa::Args make_args(const void* q, const void* k, const void* v, int B, int H, in
     a.N64 = round64(N);
     a.scale = scale;
     a.scale_log2 = scale * 1.4426950408889634f;
+    a.wl = a.wr = fa::kNoWindow;
     return a;
+}
+
+// Sliding window and softcapping as the kernels take them (see fa::Args).
+struct Masking {
+    int wl = fa::kNoWindow, wr = fa::kNoWindow;
+    float softcap = 0.f;  // 0: off
+};
+
+// Window bounds: -1 for an unbounded side, else >= 0; softcap: 0 (off) or a
+// finite positive cap. False for anything else.
+bool make_masking(int window_left, int window_right, float softcap, Masking& mk) {
+    if (window_left < -1 || window_right < -1) return false;
+    if (!(softcap >= 0.f) || !std::isfinite(softcap)) return false;
+    mk.wl = (window_left < 0 || window_left >= fa::kNoWindow) ? fa::kNoWindow : window_left;
+    mk.wr = (window_right < 0 || window_right >= fa::kNoWindow) ? fa::kNoWindow : window_right;
+    mk.softcap = softcap;
+    return true;
+}
+
+void set_masking(fa::Args& a, const Masking& mk, float scale) {
+    a.wl = mk.wl;
+    a.wr = mk.wr;
+    if (mk.softcap > 0.f) {
+        a.cap_in = scale / mk.softcap;
+        a.cap_out = mk.softcap * 1.4426950408889634f;
+    }
 }
 
 // Dropout arguments as the kernels take them. `on` is false when nothing is
@@ -94,7 +121,7 @@ size_t workspace_bytes_for(int B, int H, int N) {
 
 int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N, int d,
              float scale, int causal, const float* alibi_slopes, const int* cu_seqlens, fa_dtype dtype,
-             const Dropout& dr, void* stream) {
+             const Dropout& dr, void* stream, const Masking& mk = Masking{}) {
     if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
     int st = check_common(B, H, Hkv, N, d, scale, causal, (int)dtype);
     if (st != FA_OK) return st;
@@ -107,12 +134,15 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
     a.out = o;
     a.lse = lse;
     set_dropout(a, dr);
+    set_masking(a, mk, scale);
+    const bool cap = mk.softcap > 0.f;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     hipError_t e;
     if (dtype == FA_FP32)
-        e = fa::launch_fwd_f32(a, d, causal != 0, alibi_slopes != nullptr, s);
+        e = fa::launch_fwd_f32(a, d, causal != 0, alibi_slopes != nullptr, cap, s);
     else
-        e = fa::launch_fwd_mfma(a, (int)dtype, d, causal != 0, alibi_slopes != nullptr, dr.on, s);
+        e = fa::launch_fwd_mfma(a, (int)dtype, d, causal != 0, alibi_slopes != nullptr,
+                                dr.on ? fa::kDropout : (cap ? fa::kSoftcap : fa::kPlain), s);
     return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -134,6 +164,18 @@ int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* 
     if (!make_dropout(p_drop, seed, offset, dr)) return FA_ERR_INVALID_ARG;
     if (dr.on && dtype == FA_FP32) return FA_ERR_UNSUPPORTED;
     return fwd_impl(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, alibi_slopes, cu_seqlens, dtype, dr, stream);
+}
+
+int fa_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N, int d,
+               float scale, int causal, const float* alibi_slopes, const int* cu_seqlens, fa_dtype dtype,
+               int window_left, int window_right, float softcap, float p_drop, unsigned long long seed,
+               unsigned int offset, void* stream) {
+    Dropout dr;
+    Masking mk;
+    if (!make_dropout(p_drop, seed, offset, dr) || !make_masking(window_left, window_right, softcap, mk))
+        return FA_ERR_INVALID_ARG;
+    if (dr.on && (dtype == FA_FP32 || mk.softcap > 0.f)) return FA_ERR_UNSUPPORTED;
+    return fwd_impl(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, alibi_slopes, cu_seqlens, dtype, dr, stream, mk);
 }
 
 size_t fa_bwd_workspace_size(int B, int H, int Hkv, int N, int d, int causal, int varlen, fa_dtype dtype) {
@@ -188,7 +230,7 @@ int scratch_for_current_device(void** out) {
 int bwd_launch(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d, float scale, int causal,
                const float* alibi_slopes, const int* cu_seqlens, fa_dtype dtype, void* workspace, unsigned stages,
-               void* stream, const Dropout& dr = Dropout{}) {
+               void* stream, const Dropout& dr = Dropout{}, const Masking& mk = Masking{}) {
     fa::Args a = make_args(q, k, v, B, H, Hkv, N, scale, alibi_slopes, cu_seqlens);
     a.o = o;
     a.dout = dout;
@@ -199,7 +241,9 @@ int bwd_launch(const void* q, const void* k, const void* v, const void* o, const
     a.dsum = reinterpret_cast<float*>(workspace);
     a.lse2 = a.dsum + workspace_rows(B, H, N);
     set_dropout(a, dr);
-    hipError_t e = fa::launch_bwd(a, (int)dtype, d, causal != 0, alibi_slopes != nullptr, dr.on, stages,
+    set_masking(a, mk, scale);
+    const int var = dr.on ? fa::kDropout : (mk.softcap > 0.f ? fa::kSoftcap : fa::kPlain);
+    hipError_t e = fa::launch_bwd(a, (int)dtype, d, causal != 0, alibi_slopes != nullptr, var, stages,
                                   reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
@@ -332,6 +376,25 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, c
                       dtype, workspace, FA_BWD_ALL, stream, dr);
 }
 
+int fa_bwd_ext(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+               void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d, float scale, int causal,
+               const float* alibi_slopes, const int* cu_seqlens, fa_dtype dtype, int window_left, int window_right,
+               float softcap, float p_drop, unsigned long long seed, unsigned int offset, void* workspace,
+               size_t workspace_bytes, void* stream) {
+    Dropout dr;
+    Masking mk;
+    if (!make_dropout(p_drop, seed, offset, dr) || !make_masking(window_left, window_right, softcap, mk))
+        return FA_ERR_INVALID_ARG;
+    int st = check_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, Hkv, N, d, scale, causal, alibi_slopes, cu_seqlens,
+                       dtype);
+    if (st != FA_OK) return st;
+    if (dr.on && mk.softcap > 0.f) return FA_ERR_UNSUPPORTED;
+    if (!workspace || !aligned16(workspace) || workspace_bytes < workspace_bytes_for(B, H, N))
+        return FA_ERR_WORKSPACE;
+    return bwd_launch(q, k, v, o, dout, lse, dq, dk, dv, B, H, Hkv, N, d, scale, causal, alibi_slopes, cu_seqlens,
+                      dtype, workspace, FA_BWD_ALL, stream, dr, mk);
+}
+
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse, void* dq,
            void* dk, void* dv, int B, int H, int Hkv, int N, int d, float scale, int causal,
            const float* alibi_slopes, const int* cu_seqlens, fa_dtype dtype, void* workspace,
@@ -344,7 +407,9 @@ const char* fa_strerror(int status) {
     switch (status) {
         case FA_OK: return "success";
         case FA_ERR_INVALID_ARG: return "invalid argument";
-        case FA_ERR_UNSUPPORTED: return "unsupported configuration (head dim must be 64 or 128; fp32 is forward only)";
+        case FA_ERR_UNSUPPORTED:
+            return "unsupported configuration (head dim must be 64 or 128; fp32 is forward only and without "
+                   "dropout; dropout and softcapping do not combine)";
         case FA_ERR_WORKSPACE: return "workspace missing, misaligned or smaller than fa_bwd_workspace_size()";
         case FA_ERR_LAUNCH: return "kernel launch failed";
         case FA_ERR_SCRATCH: return "problem needs more backward scratch than fa_bwd_noalloc holds (fa_bwd_noalloc_max_bytes())";

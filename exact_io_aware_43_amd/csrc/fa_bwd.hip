@@ -32,6 +32,11 @@
 // row-major LDS tiles whose 16-byte chunks are XOR-swizzled per row; the
 // transposed operands (dO^T, Q^T, K^T) come from the transposing LDS read.
 //
+// Variants: a sliding window (runtime bounds) limits the visited tiles and
+// masks per key on the tiles that cross a bound; softcapping (compiled
+// instances) recomputes t = cap tanh(u / cap) and multiplies dS by the
+// derivative 1 - tanh^2 before it meets K or Q.
+//
 // Workspace: D followed by L * log2(e), fp32 [B, H, N64] each (N64 = N rounded
 // up to 64), both written by the pre-pass; positions past a sequence's end get
 // L * log2(e) = +inf and D = 0, so any row the later kernels read there
@@ -81,15 +86,15 @@ constexpr int DQ_BK = 64;  // keys per K/V tile
 // fits in 256 registers per lane. The d = 128 non-causal instances and the
 // d = 128 causal instance with both ALiBi and dropout do not (the compiler
 // spills them there) and run 4 waves, one per SIMD.
-template <int D, bool CAUSAL, bool ALIBI, bool DROP>
+template <int D, bool CAUSAL, bool ALIBI, bool DROP, bool CAP>
 constexpr int dq_waves() {
     return (D == 128 && (!CAUSAL || (ALIBI && DROP))) ? 4 : 8;
 }
 
-template <typename T, int D, bool CAUSAL, bool ALIBI, bool DROP>
-__global__ __launch_bounds__((64 * dq_waves<D, CAUSAL, ALIBI, DROP>()), 1) void bwd_dq_kernel(Args a) {
-    constexpr int DQ_NT = 64 * dq_waves<D, CAUSAL, ALIBI, DROP>();
-    constexpr int DQ_BQ = 32 * dq_waves<D, CAUSAL, ALIBI, DROP>();
+template <typename T, int D, bool CAUSAL, bool ALIBI, bool DROP, bool CAP>
+__global__ __launch_bounds__((64 * dq_waves<D, CAUSAL, ALIBI, DROP, CAP>()), 1) void bwd_dq_kernel(Args a) {
+    constexpr int DQ_NT = 64 * dq_waves<D, CAUSAL, ALIBI, DROP, CAP>();
+    constexpr int DQ_BQ = 32 * dq_waves<D, CAUSAL, ALIBI, DROP, CAP>();
     constexpr int TILE = DQ_BK * D;  // stage: K tile then V tile, swizzled
     __shared__ __attribute__((aligned(16))) uint16_t stA[2 * TILE];
     __shared__ __attribute__((aligned(16))) uint16_t stB[2 * TILE];
@@ -145,21 +150,26 @@ __global__ __launch_bounds__((64 * dq_waves<D, CAUSAL, ALIBI, DROP>()), 1) void 
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) dqacc[db] = f32x16{};
 
-    const int kend = CAUSAL ? min(len, q0 + DQ_BQ) : len;
-    const int nkt = (kend + DQ_BK - 1) / DQ_BK;
+    // window bounds (causal: nothing right of the diagonal) and the key tiles
+    // some query of the workgroup can see
+    const int wl = a.wl, wr = CAUSAL ? 0 : a.wr;
+    const int kt_lo = max(q0 - wl, 0) / DQ_BK;
+    const int kend = min(len, q0 + DQ_BQ + wr);
+    const int nkt = (kend + DQ_BK - 1) / DQ_BK - kt_lo;
     const T* Kg = reinterpret_cast<const T*>(a.k) + (size_t)row0 * ldk + (size_t)g * D;
     const T* Vg = reinterpret_cast<const T*>(a.v) + (size_t)row0 * ldk + (size_t)g * D;
 
     DmaTile<D, DQ_BK, DQ_NT / 64> dma;
     dma.init(wave, lane, ldk);
-    auto issue = [&](uint16_t* S, int kt) {
-        dma.issue(S, reinterpret_cast<const uint16_t*>(Kg), kt * DQ_BK, len, wave);
-        dma.issue(S + TILE, reinterpret_cast<const uint16_t*>(Vg), kt * DQ_BK, len, wave);
+    auto issue = [&](uint16_t* S, int it) {
+        dma.issue(S, reinterpret_cast<const uint16_t*>(Kg), (kt_lo + it) * DQ_BK, len, wave);
+        dma.issue(S + TILE, reinterpret_cast<const uint16_t*>(Vg), (kt_lo + it) * DQ_BK, len, wave);
     };
 
-    auto compute = [&](const uint16_t* S, int kt) {
-        const int k0 = kt * DQ_BK;
-        if (!(wave_live && (!CAUSAL || k0 <= qw + 31))) return;
+    auto compute = [&](const uint16_t* S, int it) {
+        const int k0 = (kt_lo + it) * DQ_BK;
+        // wave-uniform: skip tiles no query of this wave can see
+        if (!(wave_live && k0 <= qw + 31 + wr && k0 + DQ_BK - 1 >= qw - wl)) return;
         const uint16_t* Ks = S;
         const uint16_t* Vs = S + TILE;
         // Per 32-key block kb: S^T = K Q^T and dP^T = V dO^T, the softmax
@@ -171,7 +181,7 @@ __global__ __launch_bounds__((64 * dq_waves<D, CAUSAL, ALIBI, DROP>()), 1) void 
         // order.
         constexpr int NK = D / 16, ND = D / 32;
         // masked: a compile-time flag, true for tiles with keys past the end or
-        // across the diagonal
+        // outside some query's window (across the diagonal when causal)
         auto body = [&](auto masked_t) {
             constexpr bool masked = decltype(masked_t)::value;
             uint4 fk[3], fv[3], fkt[3];
@@ -211,8 +221,10 @@ __global__ __launch_bounds__((64 * dq_waves<D, CAUSAL, ALIBI, DROP>()), 1) void 
                         const float dist = (float)(qi - kj);
                         bias -= slope2 * (CAUSAL ? dist : fabsf(dist));
                     }
-                    float p = exp2_fast(fmaf(s[r], c2, bias));
-                    if (masked && (kj >= len || (CAUSAL && kj > qi))) p = 0.f;
+                    float th = 0.f;  // softcapping: tanh(u / cap), for the derivative
+                    if (CAP) th = tanh_fast(s[r] * a.cap_in);
+                    float p = exp2_fast(CAP ? fmaf(a.cap_out, th, bias) : fmaf(s[r], c2, bias));
+                    if (masked && (kj >= len || kj > qi + wr || kj < qi - wl)) p = 0.f;
                     float g = dp[r];
                     if constexpr (DROP) {
                         if ((r & 1) == 0) keepm = keep_mask2(wd[r >> 2], (r >> 1) & 1, keep2);
@@ -220,7 +232,7 @@ __global__ __launch_bounds__((64 * dq_waves<D, CAUSAL, ALIBI, DROP>()), 1) void 
                                                    : (uint32_t)((int)(keepm << 16) >> 16);
                         g = __uint_as_float(__float_as_uint(g) & m) * a.drop_scale;
                     }
-                    dp[r] = p * (g - dsum);
+                    dp[r] = CAP ? p * (g - dsum) * (1.f - th * th) : p * (g - dsum);
                 }
                 V8<T> dsb[2];
 #pragma unroll
@@ -247,7 +259,7 @@ __global__ __launch_bounds__((64 * dq_waves<D, CAUSAL, ALIBI, DROP>()), 1) void 
                 }
             }
         };
-        if ((k0 + DQ_BK > len) || (CAUSAL && k0 + DQ_BK - 1 > qw))
+        if ((k0 + DQ_BK > len) || (k0 + DQ_BK - 1 > qw + wr) || (k0 < qw + 31 - wl))
             body(std::true_type{});
         else
             body(std::false_type{});
@@ -271,7 +283,7 @@ __global__ __launch_bounds__((64 * dq_waves<D, CAUSAL, ALIBI, DROP>()), 1) void 
     }
 }
 
-template <typename T, int D, bool CAUSAL, bool ALIBI, bool DROP>
+template <typename T, int D, bool CAUSAL, bool ALIBI, bool DROP, bool CAP>
 hipError_t launch(const Args& a, unsigned stages, hipStream_t s) {
     if (stages & 1u) {
         constexpr int RPB = NT / (D / 8);
@@ -281,38 +293,42 @@ hipError_t launch(const Args& a, unsigned stages, hipStream_t s) {
         if (e != hipSuccess) return e;
     }
     if (stages & 2u) {
-        hipError_t e = launch_bwd_dkdv(a, std::is_same<T, __bf16>::value ? 2 : 1, D, CAUSAL, ALIBI, DROP, s);
+        hipError_t e = launch_bwd_dkdv(a, std::is_same<T, __bf16>::value ? 2 : 1, D, CAUSAL, ALIBI,
+                                       DROP ? kDropout : (CAP ? kSoftcap : kPlain), s);
         if (e != hipSuccess) return e;
     }
     if (stages & 4u) {
-        constexpr int nw = dq_waves<D, CAUSAL, ALIBI, DROP>();
+        constexpr int nw = dq_waves<D, CAUSAL, ALIBI, DROP, CAP>();
         dim3 grid(a.H, a.B, (a.N + 32 * nw - 1) / (32 * nw));
-        hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL, ALIBI, DROP>), grid, dim3(64 * nw), 0, s, a);
+        hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL, ALIBI, DROP, CAP>), grid, dim3(64 * nw), 0, s, a);
         return hipGetLastError();
     }
     return hipSuccess;
 }
 
-template <typename T, int D, bool DROP>
+template <typename T, int D, bool DROP, bool CAP>
 hipError_t launch_m(const Args& a, bool causal, bool alibi, unsigned st, hipStream_t s) {
-    if (causal) return alibi ? launch<T, D, true, true, DROP>(a, st, s) : launch<T, D, true, false, DROP>(a, st, s);
-    return alibi ? launch<T, D, false, true, DROP>(a, st, s) : launch<T, D, false, false, DROP>(a, st, s);
+    if (causal)
+        return alibi ? launch<T, D, true, true, DROP, CAP>(a, st, s) : launch<T, D, true, false, DROP, CAP>(a, st, s);
+    return alibi ? launch<T, D, false, true, DROP, CAP>(a, st, s) : launch<T, D, false, false, DROP, CAP>(a, st, s);
 }
 
 template <typename T, int D>
-hipError_t launch_d(const Args& a, bool causal, bool alibi, bool drop, unsigned st, hipStream_t s) {
-    return drop ? launch_m<T, D, true>(a, causal, alibi, st, s) : launch_m<T, D, false>(a, causal, alibi, st, s);
+hipError_t launch_d(const Args& a, bool causal, bool alibi, int var, unsigned st, hipStream_t s) {
+    if (var == kDropout) return launch_m<T, D, true, false>(a, causal, alibi, st, s);
+    if (var == kSoftcap) return launch_m<T, D, false, true>(a, causal, alibi, st, s);
+    return launch_m<T, D, false, false>(a, causal, alibi, st, s);
 }
 
 }  // namespace
 
-hipError_t launch_bwd(const Args& a, int dtype, int d, bool causal, bool alibi, bool drop, unsigned st,
+hipError_t launch_bwd(const Args& a, int dtype, int d, bool causal, bool alibi, int var, unsigned st,
                       hipStream_t s) {
     if (dtype == 2)
-        return d == 64 ? launch_d<__bf16, 64>(a, causal, alibi, drop, st, s)
-                       : launch_d<__bf16, 128>(a, causal, alibi, drop, st, s);
-    return d == 64 ? launch_d<_Float16, 64>(a, causal, alibi, drop, st, s)
-                   : launch_d<_Float16, 128>(a, causal, alibi, drop, st, s);
+        return d == 64 ? launch_d<__bf16, 64>(a, causal, alibi, var, st, s)
+                       : launch_d<__bf16, 128>(a, causal, alibi, var, st, s);
+    return d == 64 ? launch_d<_Float16, 64>(a, causal, alibi, var, st, s)
+                   : launch_d<_Float16, 128>(a, causal, alibi, var, st, s);
 }
 
 }  // namespace fa

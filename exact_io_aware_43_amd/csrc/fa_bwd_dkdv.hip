@@ -16,6 +16,10 @@
 //   P  = exp2(S * scale * log2 e - L * log2 e), dS = P o (dP - D)
 //   dV^T += dO^T P,  dK^T += Q^T dS    (transposed operands via ds_read_b64_tr_b16)
 //
+// A sliding window narrows the query tiles a key tile walks and masks the
+// steps that cross a bound; softcapping recomputes tanh(u / cap) per score and
+// multiplies dS by 1 - tanh^2 before dK accumulates it.
+//
 // The other wave on the SIMD fills the MFMA pipe during this one's softmax.
 // LDS operand loads run one MFMA group ahead through two-slot register rings,
 // and scheduling barriers pin the order.
@@ -33,7 +37,7 @@ constexpr int KV_BQ = 64;       // queries per step (two blocks of 32)
 
 #define FA_SB() __builtin_amdgcn_sched_barrier(0)
 
-template <typename T, int D, bool CAUSAL, bool ALIBI, bool DROP>
+template <typename T, int D, bool CAUSAL, bool ALIBI, bool DROP, bool CAP>
 __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
     // stage: Q tile, dO tile (swizzled [KV_BQ x D] each), with L*log2(e) and D
     // (fp32, KV_BQ each) in a small array of their own: the two tile stages
@@ -96,10 +100,12 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
         dvacc[db] = f32x16{};
     }
 
-    // Query tiles that can see this key tile: all of them, or (causal) those
-    // ending at or after k0; for every query head of the kv group.
-    const int qt0 = CAUSAL ? k0 / KV_BQ : 0;
-    const int nqt = (len + KV_BQ - 1) / KV_BQ;
+    // Query tiles that can see this key tile (queries i with
+    // k0 - wr <= i <= k0 + KV_BK - 1 + wl; causal: wr = 0), for every query
+    // head of the kv group.
+    const int wl = a.wl, wr = CAUSAL ? 0 : a.wr;
+    const int qt0 = max(k0 - wr, 0) / KV_BQ;
+    const int nqt = (min(len, k0 + KV_BK + wl) + KV_BQ - 1) / KV_BQ;
     const int per_head = nqt - qt0;
     const int steps = a.G * per_head;
     const float c2 = a.scale_log2;
@@ -189,7 +195,12 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
                 wd[0] = rd.x, wd[1] = rd.y, wd[2] = rd.z, wd[3] = rd.w;
             }
 
-            // ---- softmax backward, row group i = accumulator rows 4i .. 4i + 3
+            // ---- softmax backward, row group i = accumulator rows 4i .. 4i + 3.
+            // Query qi of element (i, j) has qi - key = qk + 8 i + j; the pair is
+            // masked when that offset is below -wr (key right of the window) or
+            // above wl (key left of it): two per-step limits against constants.
+            const int qk = q0 + 32 * qb + 4 * kg - key;
+            const int lim_hi = wl - qk, lim_lo = -wr - qk;
             float pv[16], dsr[16];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -200,14 +211,15 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int r = 4 * i + j;
-                    const int qi = q0 + 32 * qb + 8 * i + 4 * kg + j;
                     float bias = -lv[j];
                     if (ALIBI) {
-                        const float dist = (float)(qi - key);
+                        const float dist = (float)(qk + 8 * i + j);  // qi - key
                         bias -= slope2 * (CAUSAL ? dist : fabsf(dist));
                     }
-                    float p = exp2_fast(fmaf(sc[r], c2, bias));
-                    if (MASKED && key > qi) p = 0.f;
+                    float th = 0.f;  // softcapping: tanh(u / cap), for the derivative
+                    if (CAP) th = tanh_fast(sc[r] * a.cap_in);
+                    float p = exp2_fast(CAP ? fmaf(a.cap_out, th, bias) : fmaf(sc[r], c2, bias));
+                    if (MASKED && (8 * i + j > lim_hi || 8 * i + j < lim_lo)) p = 0.f;
                     pv[r] = p;
                     float g = dpc[r];
                     if constexpr (DROP) {  // the gradient reaching P: dP o keep * 256 / K
@@ -215,7 +227,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
                         const uint32_t m = (r & 1) ? (uint32_t)((int)m2 >> 16) : (uint32_t)((int)(m2 << 16) >> 16);
                         g = __uint_as_float(__float_as_uint(g) & m) * a.drop_scale;
                     }
-                    dsr[r] = p * (g - dv[j]);
+                    dsr[r] = CAP ? p * (g - dv[j]) * (1.f - th * th) : p * (g - dv[j]);
                 }
             }
             V8<T> pb[2], db8[2];  // P and dS per 16-query chunk, as B operands
@@ -264,11 +276,11 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
     auto compute = [&](const uint16_t* S, int st) {
         int h, q0;
         step_coords(st, h, q0);
-        // wave-uniform skips: keys past the sequence end, or (causal) a query
-        // tile entirely before this wave's first key
-        if (!((kw < len) && (!CAUSAL || q0 + KV_BQ - 1 >= kw))) return;
-        if (CAUSAL && q0 < kw + 31)
-            step(S, h, q0, std::true_type{});  // tile straddles the diagonal
+        // wave-uniform skips: keys past the sequence end, or a query tile no
+        // key of this wave is visible from (causal: entirely before the keys)
+        if (!((kw < len) && kw <= q0 + KV_BQ - 1 + wr && kw + 31 >= q0 - wl)) return;
+        if (kw + 31 > q0 + wr || kw < q0 + KV_BQ - 1 - wl)
+            step(S, h, q0, std::true_type{});  // some pair is masked (diagonal, window)
         else
             step(S, h, q0, std::false_type{});
     };
@@ -298,30 +310,32 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
 
 #undef FA_SB
 
-template <typename T, int D, bool CAUSAL, bool ALIBI, bool DROP>
+template <typename T, int D, bool CAUSAL, bool ALIBI, bool DROP, bool CAP>
 hipError_t launch(const Args& a, hipStream_t s) {
     dim3 grid(a.Hkv, a.B, (a.N + KV_BK - 1) / KV_BK);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL, ALIBI, DROP>), grid, dim3(NT), 0, s, a);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL, ALIBI, DROP, CAP>), grid, dim3(NT), 0, s, a);
     return hipGetLastError();
 }
 
-template <typename T, int D, bool DROP>
+template <typename T, int D, bool DROP, bool CAP>
 hipError_t launch_m(const Args& a, bool causal, bool alibi, hipStream_t s) {
-    if (causal) return alibi ? launch<T, D, true, true, DROP>(a, s) : launch<T, D, true, false, DROP>(a, s);
-    return alibi ? launch<T, D, false, true, DROP>(a, s) : launch<T, D, false, false, DROP>(a, s);
+    if (causal) return alibi ? launch<T, D, true, true, DROP, CAP>(a, s) : launch<T, D, true, false, DROP, CAP>(a, s);
+    return alibi ? launch<T, D, false, true, DROP, CAP>(a, s) : launch<T, D, false, false, DROP, CAP>(a, s);
 }
 
 template <typename T, int D>
-hipError_t launch_d(const Args& a, bool causal, bool alibi, bool drop, hipStream_t s) {
-    return drop ? launch_m<T, D, true>(a, causal, alibi, s) : launch_m<T, D, false>(a, causal, alibi, s);
+hipError_t launch_d(const Args& a, bool causal, bool alibi, int var, hipStream_t s) {
+    if (var == kDropout) return launch_m<T, D, true, false>(a, causal, alibi, s);
+    if (var == kSoftcap) return launch_m<T, D, false, true>(a, causal, alibi, s);
+    return launch_m<T, D, false, false>(a, causal, alibi, s);
 }
 
 }  // namespace
 
-hipError_t launch_bwd_dkdv(const Args& a, int dtype, int d, bool causal, bool alibi, bool drop, hipStream_t s) {
+hipError_t launch_bwd_dkdv(const Args& a, int dtype, int d, bool causal, bool alibi, int var, hipStream_t s) {
     if (dtype == 2)
-        return d == 64 ? launch_d<__bf16, 64>(a, causal, alibi, drop, s) : launch_d<__bf16, 128>(a, causal, alibi, drop, s);
-    return d == 64 ? launch_d<_Float16, 64>(a, causal, alibi, drop, s) : launch_d<_Float16, 128>(a, causal, alibi, drop, s);
+        return d == 64 ? launch_d<__bf16, 64>(a, causal, alibi, var, s) : launch_d<__bf16, 128>(a, causal, alibi, var, s);
+    return d == 64 ? launch_d<_Float16, 64>(a, causal, alibi, var, s) : launch_d<_Float16, 128>(a, causal, alibi, var, s);
 }
 
 }  // namespace fa

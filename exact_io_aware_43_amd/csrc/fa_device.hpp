@@ -81,6 +81,14 @@ __device__ __forceinline__ uint4 ld_s16(const uint16_t* p) { return *reinterpret
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// tanh x = 1 - 2 / (e^(2x) + 1), with e^(2x) = 2^(2x log2 e): one exponential
+// and one reciprocal. Saturates to +-1 (e^(2x) = inf or 0); near 0 the
+// subtraction leaves an absolute error of a few fp32 ulps of 1.
+__device__ __forceinline__ float tanh_fast(float x) {
+    const float e = exp2_fast(x * (2.f * kLog2e));
+    return 1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f);
+}
+
 // acc + x0 + x1 for a packed pair of 16-bit values (x0, x1), with one v_dot2
 // against (1, 1): the products are exact and the sum is taken in fp32.
 template <typename T>

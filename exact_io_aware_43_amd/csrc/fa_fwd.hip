@@ -39,6 +39,11 @@
 // arithmetic because the final division uses sums taken against the same
 // reference.
 //
+// Variants: a sliding window (runtime bounds; it sets the visited key range,
+// the per-wave skips and the edge tiles that take the mask) and softcapping
+// (compiled instances: the scaled score u becomes cap tanh(u / cap) before the
+// bias, which needs the materialised path and one tanh per score).
+//
 // Numerics: scores, sums and the O accumulator are fp32; P is rounded to the
 // input type for the second product. O is divided by the sum of exactly those
 // rounded P values (so its weights sum to one and a row dominated by one key
@@ -63,7 +68,7 @@ constexpr float sum_bound() {
     return sizeof(T) == 2 && __is_same(T, _Float16) ? 32768.f : 4294967296.f;
 }
 
-template <typename T, int D, bool CAUSAL, bool ALIBI, bool DROP>
+template <typename T, int D, bool CAUSAL, bool ALIBI, bool DROP, bool CAP>
 __global__ __launch_bounds__(NT, 1) void fwd_mfma_kernel(Args a) {
     // Two named K/V stages (swizzled [BC x D] tiles, K then V): the prefetch
     // into one overlaps the reads of the other, which the compiler can only
@@ -120,8 +125,12 @@ __global__ __launch_bounds__(NT, 1) void fwd_mfma_kernel(Args a) {
         toff[db][1] = swz_tr_off<D>(lane, db, 1);
     }
 
-    const int kend = CAUSAL ? min(len, q0 + BR) : len;
-    const int nkt = (kend + BC - 1) / BC;
+    // window bounds (causal: nothing to the right of the diagonal) and the key
+    // tiles some query of the workgroup can see
+    const int wl = a.wl, wr = CAUSAL ? 0 : a.wr;
+    const int kt_lo = max(q0 - wl, 0) / BC;
+    const int kend = min(len, q0 + BR + wr);
+    const int nkt = (kend + BC - 1) / BC - kt_lo;
 
     DmaTile<D, BC, NT / 64> dma;
     dma.init(wave, lane, ldk);
@@ -131,7 +140,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_mfma_kernel(Args a) {
     // taken on that first tile bounds every later one (ascending, each tile
     // would exceed the last and force the maximum path every time). Without a
     // bias the plain ascending order is kept.
-    auto tile_of = [&](int it) { return ALIBI ? nkt - 1 - it : it; };
+    auto tile_of = [&](int it) { return kt_lo + (ALIBI ? nkt - 1 - it : it); };
     auto issue = [&](uint16_t* st, int it) {
         const int kt = tile_of(it);
         dma.issue(st, reinterpret_cast<const uint16_t*>(Kg), kt * BC, len, wave);
@@ -155,8 +164,9 @@ __global__ __launch_bounds__(NT, 1) void fwd_mfma_kernel(Args a) {
         const int kt = tile_of(it);
         const uint16_t* Vs = Ks + TILE;
         const int k0 = kt * BC;
-        // wave-uniform: skip tiles that are entirely above this wave's diagonal
-        if (!(wave_live && (!CAUSAL || k0 <= qw + 31))) return;
+        // wave-uniform: skip tiles no query of this wave can see (above the
+        // diagonal, outside the window)
+        if (!(wave_live && k0 <= qw + 31 + wr && k0 + BC - 1 >= qw - wl)) return;
 
         // S^T = K Q^T for BC keys x 32 queries (raw, unscaled scores). The K
         // operand loads run two (kb, kk) groups ahead of the MFMAs; scheduling
@@ -204,7 +214,8 @@ __global__ __launch_bounds__(NT, 1) void fwd_mfma_kernel(Args a) {
         // slope2 * (qi - key) after it. Element (kb, r) of this lane has
         // key - qi = lin + off(kb, r) with lin = k0 + 4 kg - qi per tile and the
         // compile-time off = 32 kb + 8 (r / 4) + r % 4.
-        const bool edge = (k0 + BC > len) || (CAUSAL && k0 + BC - 1 > qw);
+        // edge: some key of the tile is past the end or outside some row's window
+        const bool edge = (k0 + BC > len) || (k0 + BC - 1 > qw + wr) || (k0 < qw + 31 - wl);
         const bool below = k0 + BC - 1 <= qw;  // every key <= every query of the wave
         const bool above = k0 >= qw + 31;      // every key >= every query of the wave
         const float lin = (float)(k0 + 4 * kg - qi);
@@ -216,14 +227,15 @@ __global__ __launch_bounds__(NT, 1) void fwd_mfma_kernel(Args a) {
         // needs anyway, bounds every element of the lane's share. Only if some
         // lane's sum exceeds sum_bound<T>() (or overflowed) does the wave recompute
         // the scores and take the maximum path for this tile. A wave's first tile
-        // always takes the maximum path; every row of a live wave sees at least
-        // one key of every tile it visits (causal: key k0 <= its query), so that
-        // sets a finite reference in each row.
+        // always takes the maximum path. Without a window every row of a live
+        // wave sees at least one key of every tile it visits (causal: key
+        // k0 <= its query), so that sets a finite reference in each row; a row
+        // whose window starts later keeps an infinite reference, overflows the
+        // next maximum-free sum and is redone on the maximum path.
         // ALiBi tiles qualify when the bias is linear in the key over the whole
         // tile (no key on both sides of any of the wave's queries).
         bool need_max = true;
-        // (in ascending order, without ALiBi, a wave's first tile is tile 0)
-        const bool first = ALIBI ? fresh : kt == 0;
+        const bool first = fresh;
         if (!first && !edge && (!ALIBI || below || above)) {
             need_max = false;
             const float sl = ALIBI ? (below ? slope2 : -slope2) : 0.f;
@@ -232,7 +244,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_mfma_kernel(Args a) {
             for (int kb = 0; kb < BC / 32; ++kb) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    float t = fmaf(s[kb][r], c2, base);
+                    float t = CAP ? fmaf(a.cap_out, tanh_fast(s[kb][r] * a.cap_in), base) : fmaf(s[kb][r], c2, base);
                     if (ALIBI) t = fmaf(sl, off(kb, r), t);
                     const float p = exp2_fast(t);
                     s[kb][r] = p;
@@ -252,21 +264,23 @@ __global__ __launch_bounds__(NT, 1) void fwd_mfma_kernel(Args a) {
             // Unmasked tiles without a bias keep raw scores (the scale goes into
             // the exponent's FMA); a negative scale reverses the order of raw
             // scores, so it materialises like the others.
-            const bool materialise = ALIBI || edge || !(c2 >= 0.f);
+            const bool materialise = ALIBI || CAP || edge || !(c2 >= 0.f);
             float mt;
             if (materialise) {
                 mt = -INFINITY;
+                // key = k0 + 4 kg + kofs: the constant kofs against per-tile limits
+                const int lim_len = len - k0 - 4 * kg, lim_r = qi + wr - k0 - 4 * kg, lim_l = qi - wl - k0 - 4 * kg;
 #pragma unroll
                 for (int kb = 0; kb < BC / 32; ++kb) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        float t = s[kb][r] * c2;
+                        float t = CAP ? a.cap_out * tanh_fast(s[kb][r] * a.cap_in) : s[kb][r] * c2;
                         if (ALIBI) {
                             const float d = lin + off(kb, r);  // key - qi, exact in fp32
                             t = fmaf(slope2, CAUSAL ? d : -fabsf(d), t);
                         }
-                        const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * kg + (r & 3);
-                        if (edge && (key >= len || (CAUSAL && key > qi))) t = -INFINITY;
+                        const int kofs = 32 * kb + 8 * (r >> 2) + (r & 3);
+                        if (edge && (kofs >= lim_len || kofs > lim_r || kofs < lim_l)) t = -INFINITY;
                         s[kb][r] = t;
                         mt = fmaxf(mt, t);
                     }
@@ -285,7 +299,9 @@ __global__ __launch_bounds__(NT, 1) void fwd_mfma_kernel(Args a) {
             const bool raise = mt > m_ref + TAU;
             if (__any(raise)) {
                 const float m_new = raise ? mt : m_ref;
-                const float alpha = exp2_fast(m_ref - m_new);  // 0 on the first tile
+                // 0 where the reference was -inf; 1 on rows that keep theirs (also
+                // a row that has seen no key yet: a window can leave one empty)
+                const float alpha = raise ? exp2_fast(m_ref - mt) : 1.f;
                 l_run *= alpha;
                 l_rnd *= alpha;
 #pragma unroll
@@ -305,7 +321,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_mfma_kernel(Args a) {
             }
         }
         l_run += ls;
-        if (ALIBI) fresh = false;
+        fresh = false;
 
         // O^T += V^T P^T, 16 keys per MFMA; transposed V loads two groups ahead
         constexpr int NG2 = BC / 16 * D / 32;
@@ -391,31 +407,33 @@ __global__ __launch_bounds__(NT, 1) void fwd_mfma_kernel(Args a) {
     }
 }
 
-template <typename T, int D, bool CAUSAL, bool ALIBI, bool DROP>
+template <typename T, int D, bool CAUSAL, bool ALIBI, bool DROP, bool CAP>
 hipError_t launch(const Args& a, hipStream_t s) {
     const int nqt = (a.N + BR - 1) / BR;
     dim3 grid(a.H, a.B, nqt);
-    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, CAUSAL, ALIBI, DROP>), grid, dim3(NT), 0, s, a);
+    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, CAUSAL, ALIBI, DROP, CAP>), grid, dim3(NT), 0, s, a);
     return hipGetLastError();
 }
 
-template <typename T, int D, bool DROP>
+template <typename T, int D, bool DROP, bool CAP>
 hipError_t launch_m(const Args& a, bool causal, bool alibi, hipStream_t s) {
-    if (causal) return alibi ? launch<T, D, true, true, DROP>(a, s) : launch<T, D, true, false, DROP>(a, s);
-    return alibi ? launch<T, D, false, true, DROP>(a, s) : launch<T, D, false, false, DROP>(a, s);
+    if (causal) return alibi ? launch<T, D, true, true, DROP, CAP>(a, s) : launch<T, D, true, false, DROP, CAP>(a, s);
+    return alibi ? launch<T, D, false, true, DROP, CAP>(a, s) : launch<T, D, false, false, DROP, CAP>(a, s);
 }
 
 template <typename T, int D>
-hipError_t launch_d(const Args& a, bool causal, bool alibi, bool drop, hipStream_t s) {
-    return drop ? launch_m<T, D, true>(a, causal, alibi, s) : launch_m<T, D, false>(a, causal, alibi, s);
+hipError_t launch_d(const Args& a, bool causal, bool alibi, int var, hipStream_t s) {
+    if (var == kDropout) return launch_m<T, D, true, false>(a, causal, alibi, s);
+    if (var == kSoftcap) return launch_m<T, D, false, true>(a, causal, alibi, s);
+    return launch_m<T, D, false, false>(a, causal, alibi, s);
 }
 
 }  // namespace
 
-hipError_t launch_fwd_mfma(const Args& a, int dtype, int d, bool causal, bool alibi, bool drop, hipStream_t s) {
+hipError_t launch_fwd_mfma(const Args& a, int dtype, int d, bool causal, bool alibi, int var, hipStream_t s) {
     if (dtype == 2)
-        return d == 64 ? launch_d<__bf16, 64>(a, causal, alibi, drop, s) : launch_d<__bf16, 128>(a, causal, alibi, drop, s);
-    return d == 64 ? launch_d<_Float16, 64>(a, causal, alibi, drop, s) : launch_d<_Float16, 128>(a, causal, alibi, drop, s);
+        return d == 64 ? launch_d<__bf16, 64>(a, causal, alibi, var, s) : launch_d<__bf16, 128>(a, causal, alibi, var, s);
+    return d == 64 ? launch_d<_Float16, 64>(a, causal, alibi, var, s) : launch_d<_Float16, 128>(a, causal, alibi, var, s);
 }
 
 }  // namespace fa

@@ -10,7 +10,10 @@
 // Work decomposition: a workgroup of 128 threads owns 64 query rows; the two
 // threads of a lane pair split the head dimension in halves, combine their
 // partial dot products with one lane exchange, and run the (identical) softmax
-// bookkeeping redundantly. Each K/V tile holds 16 keys.
+// bookkeeping redundantly. Each K/V tile holds 16 keys. A sliding window
+// limits the visited key range and masks per key; softcapping (compiled
+// instances) maps the scaled score u to cap tanh(u / cap) with the library
+// tanhf before the bias.
 #include "fa_device.hpp"
 
 namespace fa {
@@ -20,7 +23,7 @@ constexpr int F_ROWS = 64;   // query rows per workgroup
 constexpr int F_NT = 128;    // threads per workgroup
 constexpr int F_BC = 16;     // keys per tile
 
-template <int D, bool CAUSAL, bool ALIBI>
+template <int D, bool CAUSAL, bool ALIBI, bool CAP>
 __global__ __launch_bounds__(F_NT) void fwd_f32_kernel(Args a) {
     constexpr int DH = D / 2;
     __shared__ __attribute__((aligned(16))) float Ks[F_BC][D];
@@ -51,8 +54,12 @@ __global__ __launch_bounds__(F_NT) void fwd_f32_kernel(Args a) {
     const float slope2 = ALIBI ? ld_uniform(a.slopes + h) * kLog2e : 0.f;
     float m_run = -INFINITY, l_run = 0.f;
 
-    const int kend = CAUSAL ? min(len, q0 + F_ROWS) : len;
-    for (int k0 = 0; k0 < kend; k0 += F_BC) {
+    // window bounds (causal: nothing right of the diagonal) and the keys some
+    // row of the workgroup can see
+    const int wl = a.wl, wr = CAUSAL ? 0 : a.wr;
+    const int kend = min(len, q0 + F_ROWS + wr);
+    const float cap = CAP ? a.cap_out * kLn2 : 0.f;  // cap, natural units
+    for (int k0 = max(q0 - wl, 0) / F_BC * F_BC; k0 < kend; k0 += F_BC) {
         __syncthreads();
         for (int e = tid; e < F_BC * D / 4; e += F_NT) {
             const int key = e / (D / 4), c4 = e % (D / 4);
@@ -75,12 +82,12 @@ __global__ __launch_bounds__(F_NT) void fwd_f32_kernel(Args a) {
             for (int c = 0; c < DH; ++c) part = fmaf(q[c], Ks[j][half * DH + c], part);
             const float dot = part + __shfl_xor(part, 1);
             const int key = k0 + j;
-            float t = dot * c2;
+            float t = CAP ? cap * tanhf(dot * a.cap_in) * kLog2e : dot * c2;
             if (ALIBI) {
                 const float dist = (float)(qi - key);
                 t -= slope2 * (CAUSAL ? dist : fabsf(dist));
             }
-            if (key >= len || (CAUSAL && key > qi)) t = -INFINITY;
+            if (key >= len || key > qi + wr || key < qi - wl) t = -INFINITY;
             s[j] = t;
             mt = fmaxf(mt, t);
         }
@@ -113,23 +120,24 @@ __global__ __launch_bounds__(F_NT) void fwd_f32_kernel(Args a) {
     }
 }
 
-template <int D, bool CAUSAL, bool ALIBI>
+template <int D, bool CAUSAL, bool ALIBI, bool CAP>
 hipError_t launch(const Args& a, hipStream_t s) {
     dim3 grid(a.H, a.B, (a.N + F_ROWS - 1) / F_ROWS);
-    hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, ALIBI>), grid, dim3(F_NT), 0, s, a);
+    hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, ALIBI, CAP>), grid, dim3(F_NT), 0, s, a);
     return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool CAP>
 hipError_t launch_d(const Args& a, bool causal, bool alibi, hipStream_t s) {
-    if (causal) return alibi ? launch<D, true, true>(a, s) : launch<D, true, false>(a, s);
-    return alibi ? launch<D, false, true>(a, s) : launch<D, false, false>(a, s);
+    if (causal) return alibi ? launch<D, true, true, CAP>(a, s) : launch<D, true, false, CAP>(a, s);
+    return alibi ? launch<D, false, true, CAP>(a, s) : launch<D, false, false, CAP>(a, s);
 }
 
 }  // namespace
 
-hipError_t launch_fwd_f32(const Args& a, int d, bool causal, bool alibi, hipStream_t s) {
-    return d == 64 ? launch_d<64>(a, causal, alibi, s) : launch_d<128>(a, causal, alibi, s);
+hipError_t launch_fwd_f32(const Args& a, int d, bool causal, bool alibi, bool cap, hipStream_t s) {
+    if (cap) return d == 64 ? launch_d<64, true>(a, causal, alibi, s) : launch_d<128, true>(a, causal, alibi, s);
+    return d == 64 ? launch_d<64, false>(a, causal, alibi, s) : launch_d<128, false>(a, causal, alibi, s);
 }
 
 }  // namespace fa

@@ -36,7 +36,19 @@ struct Args {
     // the factor 256 / K applied to kept probabilities
     uint32_t seed_lo, seed_hi, drop_offset, keep_k;
     float drop_scale;
+    // sliding window: key j is visible from query i when i - wl <= j <= i + wr
+    // (positions within a sequence; kNoWindow for an unbounded side; causal
+    // instances use wr = 0 whatever is stored here)
+    int wl, wr;
+    // softcapping (instances with it only): the scaled score u becomes
+    // cap tanh(u / cap); the kernels take tanh(s * cap_in) with s the raw dot
+    // product (cap_in = scale / cap) and scale it by cap_out = cap * log2(e)
+    float cap_in, cap_out;
 };
+
+// An unbounded window side: larger than any position difference, small enough
+// that position +- kNoWindow stays inside int32.
+constexpr int kNoWindow = 1 << 30;
 
 // A decode problem: Nq new queries per sequence against a cache of up to Nk
 // keys (seqlens[b] valid); each sequence's keys are cut into `splits` ranges.
@@ -54,14 +66,17 @@ struct DecodeArgs {
     float scale_log2;
 };
 
+// Score variants beyond mask and bias: one per compiled instance set.
+enum Variant : int { kPlain = 0, kDropout = 1, kSoftcap = 2 };
+
 // Each returns hipSuccess or the launch error. `dtype` follows fa_dtype;
-// `drop` selects the instances with dropout (16-bit only).
-hipError_t launch_fwd_mfma(const Args& a, int dtype, int d, bool causal, bool alibi, bool drop, hipStream_t s);
-hipError_t launch_fwd_f32(const Args& a, int d, bool causal, bool alibi, hipStream_t s);
+// `var` selects the instances with dropout (16-bit only) or softcapping.
+hipError_t launch_fwd_mfma(const Args& a, int dtype, int d, bool causal, bool alibi, int var, hipStream_t s);
+hipError_t launch_fwd_f32(const Args& a, int d, bool causal, bool alibi, bool cap, hipStream_t s);
 // The dK/dV launch alone (built in its own translation unit with its own flags).
-hipError_t launch_bwd_dkdv(const Args& a, int dtype, int d, bool causal, bool alibi, bool drop, hipStream_t s);
+hipError_t launch_bwd_dkdv(const Args& a, int dtype, int d, bool causal, bool alibi, int var, hipStream_t s);
 // `stages`: bit 0 = D pre-pass, bit 1 = dK/dV, bit 2 = dQ (enqueued in that order).
-hipError_t launch_bwd(const Args& a, int dtype, int d, bool causal, bool alibi, bool drop, unsigned stages,
+hipError_t launch_bwd(const Args& a, int dtype, int d, bool causal, bool alibi, int var, unsigned stages,
                       hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int d, bool causal, bool alibi, hipStream_t s);
 

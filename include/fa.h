@@ -119,6 +119,33 @@ int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* 
                    void* stream);
 
 /*
+ * Forward pass with the mask variants of the page's usage contract (its mask
+ * row names sliding window, ALiBi and softcapping; the formulas are this
+ * library's reading) together with dropout as in fa_fwd_dropout.
+ *
+ *   window_left, window_right : key j is visible from query i when
+ *            i - window_left <= j <= i + window_right (positions within the
+ *            sequence); -1 leaves that side unbounded. causal = 1 still keeps
+ *            j <= i. Values below -1 are FA_ERR_INVALID_ARG.
+ *   softcap : 0 for none; else the scaled score u = scale * <q_i, k_j> becomes
+ *            softcap * tanh(u / softcap) before the ALiBi bias and the masks.
+ *            Must be finite and >= 0.
+ *   p_drop, seed, offset : as fa_fwd_dropout (p_drop = 0: no dropout).
+ *
+ * The window also bounds the work: only key tiles some query can see are read.
+ * Every query sees at least its own key, so lse is always finite. Dropout
+ * together with softcapping, or dropout with FA_FP32, is FA_ERR_UNSUPPORTED.
+ * Other arguments, layouts and errors as fa_fwd; with both windows -1 and
+ * softcap = 0 the result equals fa_fwd_dropout's.
+ */
+int fa_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int Hkv, int N, int d, float scale, int causal,
+               const float* alibi_slopes, const int* cu_seqlens, fa_dtype dtype,
+               int window_left, int window_right, float softcap,
+               float p_drop, unsigned long long seed, unsigned int offset,
+               void* stream);
+
+/*
  * Decode over a key/value cache: attention of Nq new queries per sequence
  * against a cache of keys and values (the inference workload the page's
  * Limitations section sets apart from training, "long context and inference
@@ -198,6 +225,20 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
                    const float* alibi_slopes, const int* cu_seqlens, fa_dtype dtype,
                    float p_drop, unsigned long long seed, unsigned int offset,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward pass of fa_fwd_ext: the same window, softcap and dropout arguments
+ * (`o` and `lse` from fa_fwd_ext with the same values). With softcapping the
+ * gradient reaching the scaled score is dS * (1 - tanh^2(u / softcap)), so dQ
+ * and dK carry that factor. Workspace, errors and guarantees as fa_bwd.
+ */
+int fa_bwd_ext(const void* q, const void* k, const void* v, const void* o,
+               const void* dout, const float* lse, void* dq, void* dk, void* dv,
+               int B, int H, int Hkv, int N, int d, float scale, int causal,
+               const float* alibi_slopes, const int* cu_seqlens, fa_dtype dtype,
+               int window_left, int window_right, float softcap,
+               float p_drop, unsigned long long seed, unsigned int offset,
+               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * The three launches of fa_bwd, selectable one by one, for callers that split

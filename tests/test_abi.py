@@ -30,7 +30,8 @@ def declared_functions():
 
 def test_header_declares_expected_api():
     assert declared_functions() == sorted(
-        ["fa_fwd", "fa_fwd_dropout", "fa_bwd", "fa_bwd_dropout", "fa_bwd_stages", "fa_bwd_workspace_size",
+        ["fa_fwd", "fa_fwd_dropout", "fa_fwd_ext", "fa_bwd", "fa_bwd_dropout", "fa_bwd_ext", "fa_bwd_stages",
+         "fa_bwd_workspace_size",
          "fa_bwd_noalloc", "fa_bwd_noalloc_max_bytes", "fa_fwd_kvcache", "fa_kvcache_workspace_size",
          "fa_strerror", "fa_version"])
 
@@ -256,6 +257,37 @@ def test_dropout_rejects_like_plain_calls():
          None, fa.FA_BF16, 0.1, 1, 0]
     assert fa.fa_bwd_dropout(*b, None, 1 << 20, None) == WORKSPACE
     assert fa.fa_bwd_dropout(*b, PTR[9], 16, None) == WORKSPACE
+
+
+@pytest.mark.parametrize("wl,wr,cap,p_drop,dtype,expect", [
+    (-2, -1, 0.0, 0.0, fa.FA_BF16, INVALID), (-1, -5, 0.0, 0.0, fa.FA_BF16, INVALID),
+    (4, 0, -1.0, 0.0, fa.FA_BF16, INVALID), (4, 0, float("inf"), 0.0, fa.FA_BF16, INVALID),
+    (4, 0, float("nan"), 0.0, fa.FA_BF16, INVALID), (-1, -1, 0.0, 1.0, fa.FA_BF16, INVALID),
+    (16, 16, 30.0, 0.1, fa.FA_BF16, UNSUPPORTED), (-1, -1, 0.0, 0.1, fa.FA_FP32, UNSUPPORTED),
+])
+def test_ext_rejects(wl, wr, cap, p_drop, dtype, expect):
+    """Window below -1, a negative or non-finite cap and out-of-range dropout are
+    invalid; dropout with softcapping (or with fp32) is unsupported. No device call
+    is made: every check runs before the first launch."""
+    a = [PTR[0], PTR[1], PTR[2], PTR[3], PTR[4], 1, 4, 2, 64, 128, 0.125, 0, None, None, dtype]
+    assert fa.fa_fwd_ext(*a, wl, wr, cap, p_drop, 1, 0, None) == expect
+    if dtype == fa.FA_FP32:
+        return
+    b = [PTR[0], PTR[1], PTR[2], PTR[3], PTR[4], PTR[5], PTR[6], PTR[7], PTR[8], 2, 4, 2, 64, 64, 0.125, 1, None,
+         None, dtype]
+    assert fa.fa_bwd_ext(*b, wl, wr, cap, p_drop, 1, 0, PTR[9], 1 << 20, None) == expect
+
+
+def test_ext_rejects_like_plain_calls():
+    assert fa.fa_fwd_ext(None, PTR[1], PTR[2], PTR[3], PTR[4], 1, 4, 2, 64, 128, 0.125, 0, None, None,
+                         fa.FA_BF16, 8, 0, 10.0, 0.0, 1, 0, None) == INVALID
+    assert fa.fa_fwd_ext(PTR[0], PTR[1], PTR[2], PTR[3], PTR[4], 1, 4, 2, 64, 96, 0.125, 0, None, None,
+                         fa.FA_BF16, 8, 0, 10.0, 0.0, 1, 0, None) == UNSUPPORTED
+    b = [PTR[0], PTR[1], PTR[2], PTR[3], PTR[4], PTR[5], PTR[6], PTR[7], PTR[8], 2, 4, 2, 64, 64, 0.125, 1, None,
+         None, fa.FA_BF16, 8, 0, 10.0, 0.0, 1, 0]
+    assert fa.fa_bwd_ext(*b, None, 1 << 20, None) == WORKSPACE
+    b32 = b[:18] + [fa.FA_FP32] + b[19:]
+    assert fa.fa_bwd_ext(*b32, PTR[9], 1 << 20, None) == UNSUPPORTED
 
 
 def test_kvcache_workspace_size():
