@@ -324,9 +324,12 @@ hipError_t launch_d(const Args& a, bool causal, bool alibi, int var, unsigned st
 
 hipError_t launch_bwd(const Args& a, int dtype, int d, bool causal, bool alibi, int var, unsigned st,
                       hipStream_t s) {
-    if (dtype == 2)
+    if (dtype == 2) {
+        if (d == 32) return launch_d<__bf16, 32>(a, causal, alibi, var, st, s);
         return d == 64 ? launch_d<__bf16, 64>(a, causal, alibi, var, st, s)
                        : launch_d<__bf16, 128>(a, causal, alibi, var, st, s);
+    }
+    if (d == 32) return launch_d<_Float16, 32>(a, causal, alibi, var, st, s);
     return d == 64 ? launch_d<_Float16, 64>(a, causal, alibi, var, st, s)
                    : launch_d<_Float16, 128>(a, causal, alibi, var, st, s);
 }

@@ -333,8 +333,11 @@ hipError_t launch_d(const Args& a, bool causal, bool alibi, int var, hipStream_t
 }  // namespace
 
 hipError_t launch_bwd_dkdv(const Args& a, int dtype, int d, bool causal, bool alibi, int var, hipStream_t s) {
-    if (dtype == 2)
+    if (dtype == 2) {
+        if (d == 32) return launch_d<__bf16, 32>(a, causal, alibi, var, s);
         return d == 64 ? launch_d<__bf16, 64>(a, causal, alibi, var, s) : launch_d<__bf16, 128>(a, causal, alibi, var, s);
+    }
+    if (d == 32) return launch_d<_Float16, 32>(a, causal, alibi, var, s);
     return d == 64 ? launch_d<_Float16, 64>(a, causal, alibi, var, s) : launch_d<_Float16, 128>(a, causal, alibi, var, s);
 }
 

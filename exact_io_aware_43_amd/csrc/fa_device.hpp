@@ -238,7 +238,9 @@ constexpr bool swz_xor_forms_hold() {
     }
     return true;
 }
-static_assert(swz_xor_forms_hold<64>() && swz_xor_forms_hold<128>(), "XOR forms of the swizzled offsets");
+static_assert(swz_xor_forms_hold<32>() && swz_xor_forms_hold<64>() && swz_xor_forms_hold<128>() &&
+                  swz_xor_forms_hold<256>(),
+              "XOR forms of the swizzled offsets");
 
 // Direct global -> LDS staging (buffer_load_dwordx4 ... lds) of a [ROWS x D]
 // 16-bit tile into a swizzled LDS tile. Each instruction of a wave fills 1 KB
@@ -249,14 +251,17 @@ static_assert(swz_xor_forms_hold<64>() && swz_xor_forms_hold<128>(), "XOR forms 
 // tile's first row and its size ends with row `nrows` - 1, so the hardware
 // range check turns the chunks of rows at or past `nrows` into zeros. Every
 // kernel masks such rows (P = 0), and zero rows contribute exactly zero. `NW`
-// waves share the tile. The loads complete asynchronously (vmcnt); callers
-// wait and barrier before reading the tile.
+// waves share the tile; a tile of fewer 1 KB instructions than waves (small
+// head dims) is issued by the first INSTR waves alone. The loads complete
+// asynchronously (vmcnt); callers wait and barrier before reading the tile.
 template <int D, int ROWS, int NW>
 struct DmaTile {
     static constexpr int INSTR = ROWS * D * 2 / 1024;
-    static constexpr int PER_WAVE = INSTR / NW;
-    static_assert(INSTR % NW == 0, "tile must split evenly over the waves");
-    static_assert(PER_WAVE <= 4, "the immediate offset field reaches 4 KB");
+    static constexpr bool PARTIAL = INSTR < NW;  // waves at or past INSTR issue nothing
+    static constexpr int PER_WAVE = PARTIAL ? 1 : INSTR / NW;
+    static_assert(INSTR >= 1 && (PARTIAL || INSTR % NW == 0), "tile must split evenly over the waves");
+    // the immediate offset field reaches 4 KB: one LDS base per 4 instructions
+    static_assert(PER_WAVE <= 4 || PER_WAVE % 4 == 0, "instructions per wave: 1..4 or a multiple of 4");
     // byte offset of this lane's chunk of instruction i from the tile's first
     // row (row stride `ld`), less the instruction's immediate offset 1024 i
     uint32_t boff[PER_WAVE];
@@ -269,7 +274,7 @@ struct DmaTile {
             const int p = (wave * PER_WAVE + i) * 64 + lane;  // chunk index in LDS order
             const int row = p / (D / 8), pos = p % (D / 8);
             const int f = ((row & 3) * (D / 32)) ^ ((row >> 2) & 3);
-            boff[i] = (uint32_t)row * ld2 + 16u * (uint32_t)(pos ^ f) - 1024u * (uint32_t)i;
+            boff[i] = (uint32_t)row * ld2 + 16u * (uint32_t)(pos ^ f) - 1024u * (uint32_t)(i % 4);
         }
     }
 
@@ -278,19 +283,25 @@ struct DmaTile {
     __device__ __forceinline__ void issue(uint16_t* tile, const uint16_t* base, int row_start, int nrows,
                                           int wave) const {
 #if defined(__HIP_DEVICE_COMPILE__)  // the buffer descriptor type exists for the GPU target only
+        if (PARTIAL && wave >= INSTR) return;
         const int valid = min(nrows - row_start, ROWS);
         const uint32_t bytes = valid > 0 ? (uint32_t)(valid - 1) * ld2 + D * 2 : 0u;
         const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint16_t*>(base) + (size_t)row_start * (ld2 / 2), (short)0, (int)bytes, kBufferWord3);
-        // One LDS base (M0) per wave and tile: the immediate offset 1024 i of
-        // instruction i moves both the global and the LDS address, so M0 is
-        // set once instead of once per instruction from a vector register.
+        // One LDS base (M0) per wave, tile and group of 4 instructions: the
+        // immediate offset 1024 (i % 4) of instruction i moves both the global
+        // and the LDS address, so M0 is set once per group instead of once per
+        // instruction from a vector register.
         typedef __attribute__((address_space(3))) void lds_void;
-        lds_void* dst = (lds_void*)((__attribute__((address_space(3))) uint16_t*)(tile + wave * PER_WAVE * 512));
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, boff[0], 0, 0, 0);
-        if constexpr (PER_WAVE > 1) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, boff[1], 0, 1024, 0);
-        if constexpr (PER_WAVE > 2) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, boff[2], 0, 2048, 0);
-        if constexpr (PER_WAVE > 3) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, boff[3], 0, 3072, 0);
+#pragma unroll
+        for (int g0 = 0; g0 < PER_WAVE; g0 += 4) {
+            lds_void* dst =
+                (lds_void*)((__attribute__((address_space(3))) uint16_t*)(tile + (wave * PER_WAVE + g0) * 512));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, boff[g0], 0, 0, 0);
+            if constexpr (PER_WAVE > 1) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, boff[g0 + 1], 0, 1024, 0);
+            if constexpr (PER_WAVE > 2) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, boff[g0 + 2], 0, 2048, 0);
+            if constexpr (PER_WAVE > 3) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, boff[g0 + 3], 0, 3072, 0);
+        }
 #else
         (void)tile, (void)base, (void)row_start, (void)nrows, (void)wave;
 #endif

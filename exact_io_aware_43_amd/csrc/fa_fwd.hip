@@ -7,7 +7,8 @@
 // one of Key design 4 (one workgroup per query tile, parallel over the
 // sequence), and only O and L = m + ln(l) are written.
 //
-// Work decomposition. One workgroup of 8 waves owns BR = 256 query rows of one
+// Work decomposition (head dims 32, 64 and 128; head dim 256 below). One
+// workgroup of 8 waves owns BR = 256 query rows of one
 // (sequence, query head); each wave owns 32 of them. K and V of the head's kv
 // head stream through LDS in tiles of BC = 128 keys, double buffered: the next
 // tile's loads are in flight while the current tile is multiplied. The 8 waves
@@ -54,9 +55,16 @@
 namespace fa {
 namespace {
 
-constexpr int BR = 256;    // query rows per workgroup
-constexpr int BC = 128;    // keys per K/V tile
-constexpr int NT = 512;    // threads per workgroup (8 waves, two per SIMD)
+// Tile shape per head dim: 8 waves (two per SIMD) and 128-key tiles; for head
+// dim 256, whose O accumulator alone takes 128 registers per lane, 4 waves (one
+// per SIMD, twice the registers each) and 64-key tiles (the two K/V stages
+// stay at 128 KB of LDS). Each wave owns 32 query rows.
+template <int D>
+struct FwdShape {
+    static constexpr int NT = D == 256 ? 256 : 512;  // threads per workgroup
+    static constexpr int BC = D == 256 ? 64 : 128;   // keys per K/V tile
+    static constexpr int BR = 32 * (NT / 64);        // query rows per workgroup
+};
 constexpr float TAU = 8.f; // lazy-rescale threshold, log2 units
 // Largest fp32 sum of one lane's 64 P values of a tile that the path without
 // a row maximum accepts. Every P is then at most this bound, which must fit the
@@ -69,7 +77,8 @@ constexpr float sum_bound() {
 }
 
 template <typename T, int D, bool CAUSAL, bool ALIBI, bool DROP, bool CAP>
-__global__ __launch_bounds__(NT, 1) void fwd_mfma_kernel(Args a) {
+__global__ __launch_bounds__(FwdShape<D>::NT, 1) void fwd_mfma_kernel(Args a) {
+    constexpr int NT = FwdShape<D>::NT, BC = FwdShape<D>::BC, BR = FwdShape<D>::BR;
     // Two named K/V stages (swizzled [BC x D] tiles, K then V): the prefetch
     // into one overlaps the reads of the other, which the compiler can only
     // prove independent when they are distinct arrays.
@@ -409,9 +418,9 @@ __global__ __launch_bounds__(NT, 1) void fwd_mfma_kernel(Args a) {
 
 template <typename T, int D, bool CAUSAL, bool ALIBI, bool DROP, bool CAP>
 hipError_t launch(const Args& a, hipStream_t s) {
-    const int nqt = (a.N + BR - 1) / BR;
+    const int nqt = (a.N + FwdShape<D>::BR - 1) / FwdShape<D>::BR;
     dim3 grid(a.H, a.B, nqt);
-    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, CAUSAL, ALIBI, DROP, CAP>), grid, dim3(NT), 0, s, a);
+    hipLaunchKernelGGL((fwd_mfma_kernel<T, D, CAUSAL, ALIBI, DROP, CAP>), grid, dim3(FwdShape<D>::NT), 0, s, a);
     return hipGetLastError();
 }
 
@@ -428,12 +437,20 @@ hipError_t launch_d(const Args& a, bool causal, bool alibi, int var, hipStream_t
     return launch_m<T, D, false, false>(a, causal, alibi, s);
 }
 
+template <typename T>
+hipError_t launch_t(const Args& a, int d, bool causal, bool alibi, int var, hipStream_t s) {
+    switch (d) {
+        case 32: return launch_d<T, 32>(a, causal, alibi, var, s);
+        case 64: return launch_d<T, 64>(a, causal, alibi, var, s);
+        case 128: return launch_d<T, 128>(a, causal, alibi, var, s);
+        default: return launch_d<T, 256>(a, causal, alibi, var, s);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_fwd_mfma(const Args& a, int dtype, int d, bool causal, bool alibi, int var, hipStream_t s) {
-    if (dtype == 2)
-        return d == 64 ? launch_d<__bf16, 64>(a, causal, alibi, var, s) : launch_d<__bf16, 128>(a, causal, alibi, var, s);
-    return d == 64 ? launch_d<_Float16, 64>(a, causal, alibi, var, s) : launch_d<_Float16, 128>(a, causal, alibi, var, s);
+    return dtype == 2 ? launch_t<__bf16>(a, d, causal, alibi, var, s) : launch_t<_Float16>(a, d, causal, alibi, var, s);
 }
 
 }  // namespace fa

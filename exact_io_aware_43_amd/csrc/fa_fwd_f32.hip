@@ -133,11 +133,20 @@ hipError_t launch_d(const Args& a, bool causal, bool alibi, hipStream_t s) {
     return alibi ? launch<D, false, true, CAP>(a, s) : launch<D, false, false, CAP>(a, s);
 }
 
+template <bool CAP>
+hipError_t launch_c(const Args& a, int d, bool causal, bool alibi, hipStream_t s) {
+    switch (d) {
+        case 32: return launch_d<32, CAP>(a, causal, alibi, s);
+        case 64: return launch_d<64, CAP>(a, causal, alibi, s);
+        case 128: return launch_d<128, CAP>(a, causal, alibi, s);
+        default: return launch_d<256, CAP>(a, causal, alibi, s);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_fwd_f32(const Args& a, int d, bool causal, bool alibi, bool cap, hipStream_t s) {
-    if (cap) return d == 64 ? launch_d<64, true>(a, causal, alibi, s) : launch_d<128, true>(a, causal, alibi, s);
-    return d == 64 ? launch_d<64, false>(a, causal, alibi, s) : launch_d<128, false>(a, causal, alibi, s);
+    return cap ? launch_c<true>(a, d, causal, alibi, s) : launch_c<false>(a, d, causal, alibi, s);
 }
 
 }  // namespace fa

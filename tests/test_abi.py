@@ -66,7 +66,7 @@ def _fwd(**kw):
     (dict(lse=None), INVALID), (dict(B=0), INVALID), (dict(H=0), INVALID), (dict(Hkv=0), INVALID),
     (dict(N=0), INVALID), (dict(N=-5), INVALID), (dict(H=6, Hkv=4), INVALID), (dict(causal=2), INVALID),
     (dict(scale=math.nan), INVALID), (dict(scale=math.inf), INVALID), (dict(dtype=3), INVALID),
-    (dict(d=96), UNSUPPORTED), (dict(d=256), UNSUPPORTED), (dict(d=0), INVALID),
+    (dict(d=96), UNSUPPORTED), (dict(d=16), UNSUPPORTED), (dict(d=512), UNSUPPORTED), (dict(d=0), INVALID),
     (dict(q=PTR[0] + 8), INVALID), (dict(o=PTR[3] + 2), INVALID), (dict(lse=PTR[4] + 4), INVALID),
     (dict(alibi=PTR[5] + 4), INVALID), (dict(cu=PTR[6] + 4), INVALID),
     (dict(B=1 << 16, N=1 << 16, H=2, Hkv=2), INVALID),
@@ -90,7 +90,7 @@ def _bwd(stages=None, **kw):
 @pytest.mark.parametrize("kw,expect", [
     (dict(q=None), INVALID), (dict(do=None), INVALID), (dict(lse=None), INVALID), (dict(dq=None), INVALID),
     (dict(dk=None), INVALID), (dict(dv=None), INVALID), (dict(H=3), INVALID), (dict(causal=-1), INVALID),
-    (dict(dtype=fa.FA_FP32), UNSUPPORTED), (dict(d=32), UNSUPPORTED),
+    (dict(dtype=fa.FA_FP32), UNSUPPORTED), (dict(d=96), UNSUPPORTED), (dict(d=256), UNSUPPORTED),
     (dict(dk=PTR[7] + 8), INVALID), (dict(ws=None), WORKSPACE), (dict(ws=PTR[9] + 8), WORKSPACE),
     (dict(ws_bytes=2 * 2 * 4 * 64 * 4 - 1), WORKSPACE),
 ])
@@ -229,7 +229,7 @@ def test_noalloc_scratch_size():
 
 @pytest.mark.parametrize("kw,expect", [
     (dict(q=None), INVALID), (dict(dv=None), INVALID), (dict(H=3), INVALID), (dict(causal=2), INVALID),
-    (dict(dtype=fa.FA_FP32), UNSUPPORTED), (dict(d=32), UNSUPPORTED), (dict(dk=PTR[7] + 8), INVALID),
+    (dict(dtype=fa.FA_FP32), UNSUPPORTED), (dict(d=256), UNSUPPORTED), (dict(dk=PTR[7] + 8), INVALID),
     # 8 bytes per (sequence, head, position) above the 16 MiB scratch: rejected before any device call
     (dict(B=1, H=64, Hkv=64, N=32768 + 1), -5), (dict(B=4, H=32, Hkv=8, N=16384 + 64), -5),
 ])
@@ -320,8 +320,8 @@ def _kv(**kw):
 @pytest.mark.parametrize("kw,expect", [
     (dict(q=None), INVALID), (dict(cl=None), INVALID), (dict(lse=None), INVALID), (dict(H=6, Hkv=4), INVALID),
     (dict(Nq=0), INVALID), (dict(Nk=0), INVALID), (dict(causal=3), INVALID), (dict(splits=-2), INVALID),
-    (dict(scale=math.nan), INVALID), (dict(d=256), UNSUPPORTED), (dict(dtype=fa.FA_FP32), UNSUPPORTED),
-    (dict(k=PTR[1] + 4), INVALID), (dict(cl=PTR[5] + 4), INVALID),
+    (dict(scale=math.nan), INVALID), (dict(d=256), UNSUPPORTED), (dict(d=32), UNSUPPORTED),
+    (dict(dtype=fa.FA_FP32), UNSUPPORTED), (dict(k=PTR[1] + 4), INVALID), (dict(cl=PTR[5] + 4), INVALID),
     (dict(ws=None), WORKSPACE), (dict(ws_bytes=100), WORKSPACE), (dict(ws=PTR[6] + 8), WORKSPACE),
 ])
 def test_kvcache_rejects(kw, expect):
