@@ -30,10 +30,12 @@ CFLAGS = [
 
 
 # MFMA results in ordinary VGPRs: avoids AGPR<->VGPR copies around the softmax.
-# The dK/dV kernel keeps its 128 accumulator registers per lane in AGPRs instead
-# (VGPRs are needed for its operand rings), so it uses the default AGPR form.
+# The backward files keep the compiler's own choice (the same VGPR form for
+# every instance of two waves per SIMD): the dK/dV kernel keeps its
+# accumulators in AGPRs where it runs one wave per SIMD, and the dQ instances
+# of one wave per SIMD at head dim 256 do not compile with the VGPR form forced.
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]
-FILE_FLAGS = {"fa_bwd_dkdv.hip": []}
+FILE_FLAGS = {"fa_bwd_dkdv.hip": [], "fa_bwd.hip": []}
 
 
 def _run(cmd):

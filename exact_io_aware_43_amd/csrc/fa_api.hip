@@ -180,7 +180,7 @@ int fa_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse,
 
 size_t fa_bwd_workspace_size(int B, int H, int Hkv, int N, int d, int causal, int varlen, fa_dtype dtype) {
     (void)varlen;
-    if (check_common(B, H, Hkv, N, d, 1.0f, causal, (int)dtype) != FA_OK || d == 256) return 0;
+    if (check_common(B, H, Hkv, N, d, 1.0f, causal, (int)dtype) != FA_OK) return 0;
     return workspace_bytes_for(B, H, N);
 }
 
@@ -195,7 +195,7 @@ int check_bwd(const void* q, const void* k, const void* v, const void* o, const 
     if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
     int st = check_common(B, H, Hkv, N, d, scale, causal, (int)dtype);
     if (st != FA_OK) return st;
-    if (dtype == FA_FP32 || d == 256) return FA_ERR_UNSUPPORTED;
+    if (dtype == FA_FP32) return FA_ERR_UNSUPPORTED;
     const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv};
     for (const void* p : ptrs)
         if (!aligned16(p)) return FA_ERR_INVALID_ARG;
@@ -409,8 +409,7 @@ const char* fa_strerror(int status) {
         case FA_ERR_INVALID_ARG: return "invalid argument";
         case FA_ERR_UNSUPPORTED:
             return "unsupported configuration (head dim must be 32, 64, 128 or 256, and 64 or 128 for decode; "
-                   "backward: 16-bit and head dim up to 128; fp32 is forward only and without dropout; dropout "
-                   "and softcapping do not combine)";
+                   "fp32 is forward only and without dropout; dropout and softcapping do not combine)";
         case FA_ERR_WORKSPACE: return "workspace missing, misaligned or smaller than fa_bwd_workspace_size()";
         case FA_ERR_LAUNCH: return "kernel launch failed";
         case FA_ERR_SCRATCH: return "problem needs more backward scratch than fa_bwd_noalloc holds (fa_bwd_noalloc_max_bytes())";

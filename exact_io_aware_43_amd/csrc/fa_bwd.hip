@@ -18,7 +18,8 @@
 //                 sequence); Q and dO stay in registers and 64-key K, V tiles
 //                 stream through LDS, shared by all 8 waves; dQ = dS K is
 //                 accumulated in registers. Two waves run on each SIMD (one
-//                 workgroup of 4 waves for d = 128 without causal mask).
+//                 workgroup of 4 waves, one per SIMD, where registers need
+//                 it: see dq_waves).
 // Splitting dQ from dK/dV recomputes S and dP twice but needs no atomic
 // reduction, so the result is bitwise reproducible (the deterministic option
 // the page's Limitations section discusses).
@@ -83,12 +84,12 @@ __global__ __launch_bounds__(NT) void bwd_dsum_kernel(Args a) {
 constexpr int DQ_BK = 64;  // keys per K/V tile
 
 // NW waves per workgroup, 32 queries each: 8 (two per SIMD) where the kernel
-// fits in 256 registers per lane. The d = 128 non-causal instances and the
-// d = 128 causal instance with both ALiBi and dropout do not (the compiler
-// spills them there) and run 4 waves, one per SIMD.
+// fits in 256 registers per lane. The d = 128 non-causal instances, the
+// d = 128 causal instance with both ALiBi and dropout, and head dim 256 do not
+// (the compiler spills them there) and run 4 waves, one per SIMD.
 template <int D, bool CAUSAL, bool ALIBI, bool DROP, bool CAP>
 constexpr int dq_waves() {
-    return (D == 128 && (!CAUSAL || (ALIBI && DROP))) ? 4 : 8;
+    return (D == 256 || (D == 128 && (!CAUSAL || (ALIBI && DROP)))) ? 4 : 8;
 }
 
 template <typename T, int D, bool CAUSAL, bool ALIBI, bool DROP, bool CAP>
@@ -320,18 +321,22 @@ hipError_t launch_d(const Args& a, bool causal, bool alibi, int var, unsigned st
     return launch_m<T, D, false, false>(a, causal, alibi, st, s);
 }
 
+template <typename T>
+hipError_t launch_t(const Args& a, int d, bool causal, bool alibi, int var, unsigned st, hipStream_t s) {
+    switch (d) {
+        case 32: return launch_d<T, 32>(a, causal, alibi, var, st, s);
+        case 64: return launch_d<T, 64>(a, causal, alibi, var, st, s);
+        case 128: return launch_d<T, 128>(a, causal, alibi, var, st, s);
+        default: return launch_d<T, 256>(a, causal, alibi, var, st, s);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_bwd(const Args& a, int dtype, int d, bool causal, bool alibi, int var, unsigned st,
                       hipStream_t s) {
-    if (dtype == 2) {
-        if (d == 32) return launch_d<__bf16, 32>(a, causal, alibi, var, st, s);
-        return d == 64 ? launch_d<__bf16, 64>(a, causal, alibi, var, st, s)
-                       : launch_d<__bf16, 128>(a, causal, alibi, var, st, s);
-    }
-    if (d == 32) return launch_d<_Float16, 32>(a, causal, alibi, var, st, s);
-    return d == 64 ? launch_d<_Float16, 64>(a, causal, alibi, var, st, s)
-                   : launch_d<_Float16, 128>(a, causal, alibi, var, st, s);
+    return dtype == 2 ? launch_t<__bf16>(a, d, causal, alibi, var, st, s)
+                      : launch_t<_Float16>(a, d, causal, alibi, var, st, s);
 }
 
 }  // namespace fa

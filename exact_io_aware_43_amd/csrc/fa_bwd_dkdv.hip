@@ -30,15 +30,23 @@
 namespace fa {
 namespace {
 
-constexpr int NW = 8;           // waves per workgroup, two per SIMD
-constexpr int NT = 64 * NW;
-constexpr int KV_BK = 32 * NW;  // keys per workgroup (32 per wave)
-constexpr int KV_BQ = 64;       // queries per step (two blocks of 32)
+// Shape per head dim: 8 waves (two per SIMD) and 64-query steps; at head dim
+// 256, whose dK and dV accumulators take 256 registers per lane, 4 waves (one
+// per SIMD) and 32-query steps, which keeps V and the two Q / dO stages within
+// LDS.
+template <int D>
+struct DkdvShape {
+    static constexpr int NW = D == 256 ? 4 : 8;    // waves per workgroup
+    static constexpr int NT = 64 * NW;
+    static constexpr int KV_BK = 32 * NW;          // keys per workgroup (32 per wave)
+    static constexpr int KV_BQ = D == 256 ? 32 : 64;  // queries per step (blocks of 32)
+};
 
 #define FA_SB() __builtin_amdgcn_sched_barrier(0)
 
 template <typename T, int D, bool CAUSAL, bool ALIBI, bool DROP, bool CAP>
-__global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
+__global__ __launch_bounds__(DkdvShape<D>::NT, 1) void bwd_dkdv_kernel(Args a) {
+    constexpr int NW = DkdvShape<D>::NW, KV_BK = DkdvShape<D>::KV_BK, KV_BQ = DkdvShape<D>::KV_BQ;
     // stage: Q tile, dO tile (swizzled [KV_BQ x D] each), with L*log2(e) and D
     // (fp32, KV_BQ each) in a small array of their own: the two tile stages
     // then span 64 KB, and every operand read reaches them from one set of
@@ -47,8 +55,9 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
     constexpr int STAGE = 2 * TILE;
     __shared__ __attribute__((aligned(16))) uint16_t stA[STAGE];
     __shared__ __attribute__((aligned(16))) uint16_t stB[STAGE];
-    __shared__ __attribute__((aligned(16))) float vecA[2 * KV_BQ];
-    __shared__ __attribute__((aligned(16))) float vecB[2 * KV_BQ];
+    // (64 values each: one direct load per wave fills 64 slots)
+    __shared__ __attribute__((aligned(16))) float vecA[2 * 64];
+    __shared__ __attribute__((aligned(16))) float vecB[2 * 64];
     __shared__ __attribute__((aligned(16))) uint16_t vt[KV_BK * D];  // V rows k0 .. k0 + KV_BK, swizzled
     // dropout: each wave's 32 x 32 block of random bytes, stored key-major
     // with the queries of one lane half (kg) contiguous (see the step below)
@@ -125,12 +134,12 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
         step_coords(st, h, q0);
         dma.issue(S, reinterpret_cast<const uint16_t*>(Qb + (size_t)h * D), q0, len, wave);
         dma.issue(S + TILE, reinterpret_cast<const uint16_t*>(Db + (size_t)h * D), q0, len, wave);
-        // the pre-pass filled positions [len, N64) with +inf / 0, so the 64
+        // the pre-pass filled positions [len, N64) with +inf / 0, so the KV_BQ
         // values from q0 are in bounds and padding rows get P = 0
         const size_t vbase = ((size_t)b * a.H + h) * a.N64 + q0;
         float* vec = S == stA ? vecA : vecB;
-        if (wave == 0) dma_vec64(vec, a.lse2 + vbase, lane);
-        if (wave == 1) dma_vec64(vec + KV_BQ, a.dsum + vbase, lane);
+        if (wave == 0) dma_vec(vec, a.lse2 + vbase, lane, KV_BQ);
+        if (wave == 1) dma_vec(vec + 64, a.dsum + vbase, lane, KV_BQ);
     };
 
     const uint32_t keep2 = a.keep_k | (a.keep_k << 16);
@@ -141,7 +150,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
         const uint16_t* Qs = S;
         const uint16_t* Ds = S + TILE;
         const float* lse2 = S == stA ? vecA : vecB;
-        const float* dsv = lse2 + KV_BQ;
+        const float* dsv = lse2 + 64;
         const float slope2 = ALIBI ? ld_uniform(a.slopes + h) * kLog2e : 0.f;
         constexpr int NK = D / 16, ND = D / 32;
         // Lane parts of the LDS operand offsets in XOR form: a base per lane,
@@ -152,7 +161,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
         const uint16_t* Vw = vt + vrow;  // this wave's 32 rows of V
 
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        for (int qb = 0; qb < KV_BQ / 32; ++qb) {
             int rb = rbase, tb = tbase;
             asm volatile("" : "+v"(rb), "+v"(tb));
             // ---- S = Q K^T and dP = dO V^T: operand groups kk = 0 .. NK - 1
@@ -312,8 +321,9 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(Args a) {
 
 template <typename T, int D, bool CAUSAL, bool ALIBI, bool DROP, bool CAP>
 hipError_t launch(const Args& a, hipStream_t s) {
+    constexpr int KV_BK = DkdvShape<D>::KV_BK;
     dim3 grid(a.Hkv, a.B, (a.N + KV_BK - 1) / KV_BK);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL, ALIBI, DROP, CAP>), grid, dim3(NT), 0, s, a);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL, ALIBI, DROP, CAP>), grid, dim3(DkdvShape<D>::NT), 0, s, a);
     return hipGetLastError();
 }
 
@@ -330,15 +340,20 @@ hipError_t launch_d(const Args& a, bool causal, bool alibi, int var, hipStream_t
     return launch_m<T, D, false, false>(a, causal, alibi, s);
 }
 
+template <typename T>
+hipError_t launch_t(const Args& a, int d, bool causal, bool alibi, int var, hipStream_t s) {
+    switch (d) {
+        case 32: return launch_d<T, 32>(a, causal, alibi, var, s);
+        case 64: return launch_d<T, 64>(a, causal, alibi, var, s);
+        case 128: return launch_d<T, 128>(a, causal, alibi, var, s);
+        default: return launch_d<T, 256>(a, causal, alibi, var, s);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_bwd_dkdv(const Args& a, int dtype, int d, bool causal, bool alibi, int var, hipStream_t s) {
-    if (dtype == 2) {
-        if (d == 32) return launch_d<__bf16, 32>(a, causal, alibi, var, s);
-        return d == 64 ? launch_d<__bf16, 64>(a, causal, alibi, var, s) : launch_d<__bf16, 128>(a, causal, alibi, var, s);
-    }
-    if (d == 32) return launch_d<_Float16, 32>(a, causal, alibi, var, s);
-    return d == 64 ? launch_d<_Float16, 64>(a, causal, alibi, var, s) : launch_d<_Float16, 128>(a, causal, alibi, var, s);
+    return dtype == 2 ? launch_t<__bf16>(a, d, causal, alibi, var, s) : launch_t<_Float16>(a, d, causal, alibi, var, s);
 }
 
 }  // namespace fa

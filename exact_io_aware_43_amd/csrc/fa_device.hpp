@@ -308,20 +308,22 @@ struct DmaTile {
     }
 };
 
-// Direct global -> LDS load of 64 consecutive fp32 values (one wave, 4 bytes per
-// lane) from `src` (all 64 in bounds) into `dst`. Buffer form, like the tiles:
-// the FLAT-encoded global_load_lds would also count against lgkmcnt, after
-// which the compiler can no longer count LDS reads exactly and waits for all
-// of them before every MFMA, defeating the operand prefetch rings.
-__device__ __forceinline__ void dma_vec64(float* dst, const float* src, int lane) {
+// Direct global -> LDS load of `count` (<= 64) consecutive fp32 values (one wave,
+// 4 bytes per lane) from `src` into dst[0 .. 64): the buffer range ends after
+// `count` values, so lanes at or past it read nothing from memory and store
+// zero. Buffer form, like the tiles: the FLAT-encoded global_load_lds would
+// also count against lgkmcnt, after which the compiler can no longer count LDS
+// reads exactly and waits for all of them before every MFMA, defeating the
+// operand prefetch rings.
+__device__ __forceinline__ void dma_vec(float* dst, const float* src, int lane, int count) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the buffer descriptor type exists for the GPU target only
     const __amdgpu_buffer_rsrc_t rsrc =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(src), (short)0, 64 * 4, kBufferWord3);
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(src), (short)0, count * 4, kBufferWord3);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rsrc, (__attribute__((address_space(3))) void*)((__attribute__((address_space(3))) float*)dst), 4,
         (uint32_t)lane * 4u, 0, 0, 0);
 #else
-    (void)dst, (void)src, (void)lane;
+    (void)dst, (void)src, (void)lane, (void)count;
 #endif
 }
 

@@ -90,7 +90,7 @@ def _bwd(stages=None, **kw):
 @pytest.mark.parametrize("kw,expect", [
     (dict(q=None), INVALID), (dict(do=None), INVALID), (dict(lse=None), INVALID), (dict(dq=None), INVALID),
     (dict(dk=None), INVALID), (dict(dv=None), INVALID), (dict(H=3), INVALID), (dict(causal=-1), INVALID),
-    (dict(dtype=fa.FA_FP32), UNSUPPORTED), (dict(d=96), UNSUPPORTED), (dict(d=256), UNSUPPORTED),
+    (dict(dtype=fa.FA_FP32), UNSUPPORTED), (dict(d=96), UNSUPPORTED), (dict(d=512), UNSUPPORTED),
     (dict(dk=PTR[7] + 8), INVALID), (dict(ws=None), WORKSPACE), (dict(ws=PTR[9] + 8), WORKSPACE),
     (dict(ws_bytes=2 * 2 * 4 * 64 * 4 - 1), WORKSPACE),
 ])
@@ -229,7 +229,7 @@ def test_noalloc_scratch_size():
 
 @pytest.mark.parametrize("kw,expect", [
     (dict(q=None), INVALID), (dict(dv=None), INVALID), (dict(H=3), INVALID), (dict(causal=2), INVALID),
-    (dict(dtype=fa.FA_FP32), UNSUPPORTED), (dict(d=256), UNSUPPORTED), (dict(dk=PTR[7] + 8), INVALID),
+    (dict(dtype=fa.FA_FP32), UNSUPPORTED), (dict(d=96), UNSUPPORTED), (dict(dk=PTR[7] + 8), INVALID),
     # 8 bytes per (sequence, head, position) above the 16 MiB scratch: rejected before any device call
     (dict(B=1, H=64, Hkv=64, N=32768 + 1), -5), (dict(B=4, H=32, Hkv=8, N=16384 + 64), -5),
 ])

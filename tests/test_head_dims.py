@@ -1,10 +1,10 @@
-"""GPU parity at head dims 32 and 256 (fwd) and 32 (bwd) against the fp64 oracle.
+"""GPU parity at head dims 32 and 256, forward and backward, against the fp64 oracle.
 
 The same kernels as head dims 64 and 128, instanced for these sizes: 32 needs
 fewer 1 KB direct-load instructions per tile than there are waves (the first
-ones issue them), and the 256 forward runs 4 waves per workgroup on 64-key
-tiles because its O accumulator alone takes 128 registers per lane. The
-backward at head dim 256 is not built and reports FA_ERR_UNSUPPORTED.
+ones issue them); at 256 the forward runs 4 waves per workgroup on 64-key
+tiles (its O accumulator alone takes 128 registers per lane), the dK/dV pass 4
+waves on 32-query steps and the dQ pass 4 waves.
 
 Whole-tensor comparisons at the usual bars over lengths that span several
 tiles with a ragged tail, causal and not, ALiBi, GQA, packed sequences, a
@@ -37,14 +37,12 @@ CASES = [
     (Workload("d32_bf16_c1_alibi_varlen", "bf16", 3, 4, 4, 600, 32, causal=True, alibi=True, varlen=(1, 600)), {}),
     (Workload("d32_bf16_c0_window_cap", "bf16", 2, 4, 2, 520, 32, std=2.0), dict(window=(70, 30), softcap=8.0)),
     (Workload("d32_bf16_c1_dropout", "bf16", 1, 4, 2, 300, 32, causal=True), dict(dropout=(0.2, 77, 1))),
-    (Workload("d256_bf16_c1", "bf16", 2, 4, 2, 450, 256, causal=True, backward=False), {}),
-    (Workload("d256_fp16_c0", "fp16", 1, 4, 1, 333, 256, backward=False), {}),
-    (Workload("d256_bf16_c1_alibi_varlen", "bf16", 3, 4, 2, 400, 256, causal=True, alibi=True, varlen=(1, 400),
-              backward=False), {}),
-    (Workload("d256_bf16_c0_window_cap", "bf16", 1, 4, 4, 300, 256, std=2.0, backward=False),
-     dict(window=(50, 90), softcap=12.0)),
-    (Workload("d256_bf16_c1_dropout", "bf16", 1, 2, 1, 260, 256, causal=True, backward=False),
-     dict(dropout=(0.3, 5, 2))),
+    (Workload("d256_bf16_c1", "bf16", 2, 4, 2, 450, 256, causal=True), {}),
+    (Workload("d256_fp16_c0", "fp16", 1, 4, 1, 333, 256), {}),
+    (Workload("d256_bf16_c1_alibi_varlen", "bf16", 3, 4, 2, 400, 256, causal=True, alibi=True, varlen=(1, 400)),
+     {}),
+    (Workload("d256_bf16_c0_window_cap", "bf16", 1, 4, 4, 300, 256, std=2.0), dict(window=(50, 90), softcap=12.0)),
+    (Workload("d256_bf16_c1_dropout", "bf16", 1, 2, 1, 260, 256, causal=True), dict(dropout=(0.3, 5, 2))),
 ]
 
 
@@ -97,11 +95,3 @@ def test_fp32_head_dims(dd):
     o_ref, lse_ref = OA.attention_fwd(inp["q"], inp["k"], inp["v"], scale=inp["scale"], causal=True,
                                       alibi_slopes=inp["alibi_slopes"])
     _banner(str(_compare_fwd(w, f64(o), o_ref, f64(lse).ravel(), lse_ref.ravel(), note=f"fp32 head dim {dd}")))
-
-
-def test_d256_backward_is_unsupported():
-    w = Workload("d256_bwd", "bf16", 1, 2, 2, 64, 256)
-    d = to_dev(make_inputs(w, 97, with_grad=True))
-    o, lse = fa.attention(d["q"], d["k"], d["v"], softmax_scale=d["scale"])
-    with pytest.raises(fa.FaError):
-        fa.attention_bwd(d["do"], d["q"], d["k"], d["v"], o, lse, softmax_scale=d["scale"])
