@@ -19,6 +19,8 @@ from ._binding import (  # noqa: F401
     LIB_PATH,
     attention,
     attention_bwd,
+    attention_fp8,
+    attention_fp8_quantized,
     attention_kvcache,
     fa_bwd,
     fa_bwd_dropout,
@@ -30,9 +32,16 @@ from ._binding import (  # noqa: F401
     fa_bwd_stages,
     fa_bwd_workspace_size,
     fa_fwd,
+    fa_fp8_v_keys,
+    fa_fwd_fp8,
     fa_fwd_kvcache,
+    fa_quantize_fp8_qk,
+    fa_quantize_fp8_v,
+    hadamard_sign_words,
     fa_kvcache_workspace_size,
     fa_strerror,
     fa_version,
     lib,
+    quantize_fp8_qk,
+    quantize_fp8_v,
 )

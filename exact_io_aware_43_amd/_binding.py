@@ -59,6 +59,14 @@ def lib() -> ctypes.CDLL:
         L.fa_bwd_noalloc.restype = ci
         L.fa_bwd_noalloc_max_bytes.argtypes = []
         L.fa_bwd_noalloc_max_bytes.restype = sz
+        L.fa_fp8_v_keys.argtypes = [ci]
+        L.fa_fp8_v_keys.restype = ci
+        L.fa_quantize_fp8_qk.argtypes = [vp, vp, vp, ci, ci, ci, ci, vp, ci, vp]
+        L.fa_quantize_fp8_qk.restype = ci
+        L.fa_quantize_fp8_v.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, vp]
+        L.fa_quantize_fp8_v.restype = ci
+        L.fa_fwd_fp8.argtypes = [vp] * 8 + [ci] * 5 + [cf, ci, ci, ci, vp]
+        L.fa_fwd_fp8.restype = ci
         L.fa_strerror.argtypes = [ci]
         L.fa_strerror.restype = ctypes.c_char_p
         L.fa_version.argtypes = []
@@ -144,6 +152,26 @@ def fa_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, B, H, Hkv, N, d, scale, ca
 
 def fa_bwd_noalloc_max_bytes() -> int:
     return lib().fa_bwd_noalloc_max_bytes()
+
+
+def fa_fp8_v_keys(N) -> int:
+    return lib().fa_fp8_v_keys(N)
+
+
+def fa_quantize_fp8_qk(x, codes, scales, B, N, H, d, hadamard_signs, dtype, stream) -> int:
+    """``fa_quantize_fp8_qk``; hadamard_signs is a host address of d / 64 uint64 words, or None."""
+    return lib().fa_quantize_fp8_qk(x, codes, scales, B, N, H, d, hadamard_signs, dtype, stream)
+
+
+def fa_quantize_fp8_v(v, codes_t, scales, B, N, Hkv, d, dtype, stream) -> int:
+    return lib().fa_quantize_fp8_v(v, codes_t, scales, B, N, Hkv, d, dtype, stream)
+
+
+def fa_fwd_fp8(q, k, v_t, q_scales, k_scales, v_scales, o, lse, B, H, Hkv, N, d, scale, causal, rotated, out_dtype,
+               stream) -> int:
+    """``fa_fwd_fp8`` with integer device pointers; returns the status."""
+    return lib().fa_fwd_fp8(q, k, v_t, q_scales, k_scales, v_scales, o, lse, B, H, Hkv, N, d, scale, causal, rotated,
+                            out_dtype, stream)
 
 
 def fa_strerror(status: int) -> str:
@@ -352,6 +380,97 @@ def attention_kvcache(q, k_cache, v_cache, cache_seqlens, causal: bool = True,
     if st != FA_OK:
         raise FaError(st)
     return o, lse
+
+
+def hadamard_sign_words(signs, d: int):
+    """+-1 signs of length d as the d / 64 uint64 words fa_quantize_fp8_qk takes
+    (bit i % 64 of word i / 64 set for a sign of -1)."""
+    s = torch.as_tensor(signs, dtype=torch.float64).cpu().reshape(-1).tolist()
+    if len(s) != d or d % 64 or any(x not in (1.0, -1.0) for x in s):
+        raise ValueError(f"hadamard signs must be {d} values of +1 or -1")
+    words = (ctypes.c_ulonglong * (d // 64))()
+    for i, x in enumerate(s):
+        if x < 0:
+            words[i // 64] |= 1 << (i % 64)
+    return words
+
+
+def quantize_fp8_qk(x, hadamard_signs=None):
+    """Q or K [B, N, H, d] (float16 / bfloat16, device) -> (codes uint8 [B, N, H, d],
+    scales float32 [B, H, ceil(N / 128)], powers of two)."""
+    if not isinstance(x, torch.Tensor) or x.dim() != 4 or not x.is_cuda:
+        raise ValueError("x must be a 4-d device tensor")
+    if x.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("fp8 quantization takes float16 or bfloat16")
+    B, N, H, d = x.shape
+    _expect(x, "x", x.shape, x.dtype, x.device)
+    codes = torch.empty((B, N, H, d), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((B, H, (N + 127) // 128), dtype=torch.float32, device=x.device)
+    words = None if hadamard_signs is None else hadamard_sign_words(hadamard_signs, d)
+    st = fa_quantize_fp8_qk(x.data_ptr(), codes.data_ptr(), scales.data_ptr(), B, N, H, d,
+                            None if words is None else ctypes.addressof(words), _DTYPE[x.dtype], _stream_handle())
+    if st != FA_OK:
+        raise FaError(st)
+    return codes, scales
+
+
+def quantize_fp8_v(v):
+    """V [B, N, Hkv, d] (float16 / bfloat16, device) -> (codes_t uint8 [B, Hkv, d, NP]
+    in the key order fa_fwd_fp8 reads, scales float32 [B, Hkv, d])."""
+    if not isinstance(v, torch.Tensor) or v.dim() != 4 or not v.is_cuda:
+        raise ValueError("v must be a 4-d device tensor")
+    if v.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("fp8 quantization takes float16 or bfloat16")
+    B, N, Hkv, d = v.shape
+    _expect(v, "v", v.shape, v.dtype, v.device)
+    npad = fa_fp8_v_keys(N)
+    codes = torch.empty((B, Hkv, d, max(npad, 1)), dtype=torch.uint8, device=v.device)
+    scales = torch.empty((B, Hkv, d), dtype=torch.float32, device=v.device)
+    st = fa_quantize_fp8_v(v.data_ptr(), codes.data_ptr(), scales.data_ptr(), B, N, Hkv, d, _DTYPE[v.dtype],
+                           _stream_handle())
+    if st != FA_OK:
+        raise FaError(st)
+    return codes, scales
+
+
+def attention_fp8_quantized(qc, qs, kc, ks, vc, vs, causal: bool = False, softmax_scale: Optional[float] = None,
+                            rotated: bool = False, out_dtype=torch.bfloat16):
+    """fa_fwd_fp8 on codes and scales from quantize_fp8_qk / quantize_fp8_v;
+    returns (o [B, N, H, d] out_dtype, lse float32 [B, H, N])."""
+    B, N, H, d = qc.shape
+    Hkv = kc.shape[2]
+    dev = qc.device
+    _expect(qc, "q codes", (B, N, H, d), torch.uint8, dev)
+    _expect(kc, "k codes", (B, N, Hkv, d), torch.uint8, dev)
+    _expect(vc, "v codes", (B, Hkv, d, fa_fp8_v_keys(N)), torch.uint8, dev)
+    nb = (N + 127) // 128
+    _expect(qs, "q scales", (B, H, nb), torch.float32, dev)
+    _expect(ks, "k scales", (B, Hkv, nb), torch.float32, dev)
+    _expect(vs, "v scales", (B, Hkv, d), torch.float32, dev)
+    if out_dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("fp8 attention returns float16 or bfloat16")
+    if Hkv == 0 or H % Hkv:
+        raise ValueError(f"query heads ({H}) must be a multiple of kv heads ({Hkv})")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    o = torch.empty((B, N, H, d), dtype=out_dtype, device=dev)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    st = fa_fwd_fp8(qc.data_ptr(), kc.data_ptr(), vc.data_ptr(), qs.data_ptr(), ks.data_ptr(), vs.data_ptr(),
+                    o.data_ptr(), lse.data_ptr(), B, H, Hkv, N, d, scale, int(bool(causal)), int(bool(rotated)),
+                    _DTYPE[out_dtype], _stream_handle())
+    if st != FA_OK:
+        raise FaError(st)
+    return o, lse
+
+
+def attention_fp8(q, k, v, causal: bool = False, softmax_scale: Optional[float] = None, hadamard_signs=None,
+                  out_dtype=None):
+    """FP8 forward from 16-bit Q, K, V: quantize (Q and K rotated when
+    hadamard_signs, d values of +-1, are given), then fa_fwd_fp8. Returns (o, lse)."""
+    qc, qs = quantize_fp8_qk(q, hadamard_signs)
+    kc, ks = quantize_fp8_qk(k, hadamard_signs)
+    vc, vs = quantize_fp8_v(v)
+    return attention_fp8_quantized(qc, qs, kc, ks, vc, vs, causal=causal, softmax_scale=softmax_scale,
+                                   rotated=hadamard_signs is not None, out_dtype=out_dtype or q.dtype)
 
 
 class FlashAttnFn(torch.autograd.Function):

@@ -403,13 +403,60 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
                          cu_seqlens, dtype, workspace, workspace_bytes, FA_BWD_ALL, stream);
 }
 
+int fa_fp8_v_keys(int N) { return N > 0 && N <= (1 << 30) ? fa::fp8_keys_padded(N) : 0; }
+
+int fa_quantize_fp8_qk(const void* x, unsigned char* codes, float* scales, int B, int N, int H, int d,
+                       const unsigned long long* hadamard_signs, fa_dtype dtype, void* stream) {
+    if (!x || !codes || !scales || B <= 0 || N <= 0 || H <= 0 || d <= 0) return FA_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return FA_ERR_INVALID_ARG;
+    if (dtype != FA_FP16 && dtype != FA_BF16) return valid_dtype(dtype) ? FA_ERR_UNSUPPORTED : FA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if ((long long)B * N * H >= (1ll << 31)) return FA_ERR_INVALID_ARG;
+    hipError_t e = fa::launch_quant_qk(x, codes, scales, B, N, H, d, hadamard_signs, (int)dtype,
+                                       reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_quantize_fp8_v(const void* v, unsigned char* codes_t, float* scales, int B, int N, int Hkv, int d,
+                      fa_dtype dtype, void* stream) {
+    if (!v || !codes_t || !scales || B <= 0 || N <= 0 || Hkv <= 0 || d <= 0) return FA_ERR_INVALID_ARG;
+    if (!aligned16(v) || !aligned16(codes_t) || !aligned16(scales)) return FA_ERR_INVALID_ARG;
+    if (dtype != FA_FP16 && dtype != FA_BF16) return valid_dtype(dtype) ? FA_ERR_UNSUPPORTED : FA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if ((long long)B * N * Hkv >= (1ll << 31) || N > (1 << 30)) return FA_ERR_INVALID_ARG;
+    hipError_t e = fa::launch_quant_v(v, codes_t, scales, B, N, Hkv, d, (int)dtype,
+                                      reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_fwd_fp8(const unsigned char* q, const unsigned char* k, const unsigned char* v_t, const float* q_scales,
+               const float* k_scales, const float* v_scales, void* o, float* lse, int B, int H, int Hkv, int N,
+               int d, float scale, int causal, int rotated, fa_dtype out_dtype, void* stream) {
+    const void* ptrs[] = {q, k, v_t, q_scales, k_scales, v_scales, o, lse};
+    for (const void* p : ptrs)
+        if (!p || !aligned16(p)) return FA_ERR_INVALID_ARG;
+    if (B <= 0 || H <= 0 || Hkv <= 0 || N <= 0 || d <= 0 || H % Hkv != 0) return FA_ERR_INVALID_ARG;
+    if ((causal != 0 && causal != 1) || (rotated != 0 && rotated != 1) || !std::isfinite(scale))
+        return FA_ERR_INVALID_ARG;
+    if (out_dtype != FA_FP16 && out_dtype != FA_BF16)
+        return valid_dtype(out_dtype) ? FA_ERR_UNSUPPORTED : FA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if ((long long)B * N * H >= (1ll << 31) || N > (1 << 30)) return FA_ERR_INVALID_ARG;
+    const float s_eff = rotated ? scale / (float)d : scale;  // exact: d is a power of two
+    hipError_t e = fa::launch_fwd_fp8(q, k, v_t, q_scales, k_scales, v_scales, o, lse, B, H, Hkv, N, d,
+                                      s_eff * 1.4426950408889634f, causal != 0, (int)out_dtype,
+                                      reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 const char* fa_strerror(int status) {
     switch (status) {
         case FA_OK: return "success";
         case FA_ERR_INVALID_ARG: return "invalid argument";
         case FA_ERR_UNSUPPORTED:
-            return "unsupported configuration (head dim must be 32, 64, 128 or 256, and 64 or 128 for decode; "
-                   "fp32 is forward only and without dropout; dropout and softcapping do not combine)";
+            return "unsupported configuration (head dim must be 32, 64, 128 or 256, and 64 or 128 for decode "
+                   "and fp8; fp32 is forward only and without dropout; dropout and softcapping do not combine; "
+                   "fp8 takes and returns fp16 or bf16)";
         case FA_ERR_WORKSPACE: return "workspace missing, misaligned or smaller than fa_bwd_workspace_size()";
         case FA_ERR_LAUNCH: return "kernel launch failed";
         case FA_ERR_SCRATCH: return "problem needs more backward scratch than fa_bwd_noalloc holds (fa_bwd_noalloc_max_bytes())";

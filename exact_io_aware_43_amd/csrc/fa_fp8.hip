@@ -1,0 +1,514 @@
+// FP8 (e4m3) forward attention with power-of-two block scales and an optional
+// Walsh-Hadamard rotation of Q and K, on the gfx950 32x32x64 f8f6f4 MFMA.
+//
+// Method: "FlashAttention: Faster Attention Without Dropping a Single
+// Interaction", Method Deep Dive, Key design 4 (the FlashAttention-3 row: FP8
+// with block quantization and incoherent processing) on top of Key designs 1
+// and 2 (tiling, the mergeable softmax state). The details are this library's
+// reading of techniques the page only names:
+//
+//   Q, K: one power-of-two scale 2^e per (sequence, head, 128 tokens), the
+//         smallest with amax <= 448 * 2^e, so x * 2^-e is exact; optionally each
+//         row first multiplied by caller-given signs and the unnormalized
+//         Walsh-Hadamard matrix (fp32 butterflies, stages h = 1, 2, 4, ...),
+//         after which Q'K'^T = d QK^T and the softmax scale is divided by d.
+//   V:    one power-of-two scale per (sequence, kv head, channel), folded into
+//         O at the end (O[:, c] = 2^e_c sum_j P_j V8[j, c]); stored transposed
+//         ([B, Hkv, d, NP], NP = N rounded up to a whole 128-key tile, keys
+//         permuted within 64-key chunks) so that each MFMA lane's 32 keys of a
+//         chunk are contiguous bytes.
+//   P:    rounded to e4m3 for the second product (P <= 448 by the sum bound of
+//         the maximum-free path); O is divided by the sum of exactly those
+//         rounded values, lse uses the fp32 sum.
+//
+// e4m3 here is the OCP "fn" encoding that v_cvt_pk_fp8_f32 produces (round to
+// nearest even; values past 464 would become NaN, which the scaling rules out).
+//
+// Forward work decomposition as the 16-bit kernel: 8 waves, 256 query rows per
+// workgroup, 32 per wave; K and V^T tiles of 128 keys double buffered in LDS
+// with direct loads (byte rows handled as 16-bit pairs by the same swizzled
+// tile code). Per tile and wave: S^T = K Q^T in 8 MFMAs of 32x32x64 (head dim
+// 128), the softmax, O^T += V^T P^T in 8 more.
+#include <type_traits>
+
+#include "fa_device.hpp"
+
+namespace fa {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+constexpr int QB = 128;  // tokens per Q / K scale block
+
+// 32x32x64 e4m3 x e4m3 -> fp32 (operand formats 0 and 0, unit E8M0 scales).
+__device__ __forceinline__ f32x16 mma_f8(v8i a, v8i b, f32x16 c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// Smallest e >= -127 with amax <= 448 * 2^e, from the bits of amax = m 2^E,
+// m in [1, 2): E - 8 when m <= 1.75, E - 7 otherwise; 0 for amax = 0. The
+// floor keeps 2^e and 2^-e finite in fp32; it also covers subnormal amax, whose
+// exponent field reads as E = -127.
+__device__ __forceinline__ int block_exp(float amax) {
+    const uint32_t u = __float_as_uint(amax);
+    if (amax == 0.f) return 0;
+    const int E = (int)((u >> 23) & 0xFF) - 127;
+    return max((u & 0x7FFFFF) <= 0x600000u ? E - 8 : E - 7, -127);
+}
+
+// e4m3 codes of (x0, x1) into bytes 0, 1 (HI = false) or 2, 3 (HI = true) of old.
+template <bool HI>
+__device__ __forceinline__ uint32_t cvt2(float x0, float x1, uint32_t old) {
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, (int)old, HI);
+}
+
+// ---------------------------------------------------------------- Q, K
+// One workgroup of 4 waves per (128-token block, head, sequence); a wave owns
+// 32 rows, a lane D / 64 consecutive dims of each. Pass 1 loads, rotates and
+// reduces |x|; pass 2 scales and stores the codes from the rows kept in
+// registers.
+template <typename T, int D, bool ROT>
+__global__ __launch_bounds__(256) void quant_qk_kernel(const T* __restrict__ x, uint8_t* __restrict__ codes,
+                                                       float* __restrict__ scales, int N, int H,
+                                                       unsigned long long s0, unsigned long long s1) {
+    constexpr int V = D / 64;  // dims per lane
+    __shared__ float wmax[4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int nb = (N + QB - 1) / QB;
+    const size_t ld = (size_t)H * D;
+    float sg[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        const int dim = lane * V + v;  // sign bit of dim: bit dim % 64 of word dim / 64
+        sg[v] = (ROT && (((dim < 64 ? s0 : s1) >> (dim & 63)) & 1ull)) ? -1.f : 1.f;
+    }
+
+    float r[32][V];
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        const int t = blk * QB + wave * 32 + i;
+#pragma unroll
+        for (int v = 0; v < V; ++v) r[i][v] = 0.f;
+        if (t < N) {
+            const T* row = x + ((size_t)b * N + t) * ld + (size_t)h * D + lane * V;
+#pragma unroll
+            for (int v = 0; v < V; ++v) r[i][v] = (float)row[v] * sg[v];
+        }
+        if (ROT) {
+            // stages inside the lane (h < V), then across lanes (partner l ^ (h / V)):
+            // the lower index of a pair takes a + b, the upper a - b
+#pragma unroll
+            for (int hh = 1; hh < V; hh *= 2) {
+#pragma unroll
+                for (int v = 0; v < V; ++v) {
+                    if (v & hh) continue;
+                    const float a = r[i][v], c = r[i][v + hh];
+                    r[i][v] = a + c;
+                    r[i][v + hh] = a - c;
+                }
+            }
+#pragma unroll
+            for (int hh = V; hh < D; hh *= 2) {
+                const int m = hh / V;
+                const bool upper = (lane & m) != 0;
+#pragma unroll
+                for (int v = 0; v < V; ++v) {
+                    const float other = __shfl_xor(r[i][v], m);
+                    r[i][v] = upper ? other - r[i][v] : r[i][v] + other;
+                }
+            }
+        }
+#pragma unroll
+        for (int v = 0; v < V; ++v) amax = fmaxf(amax, fabsf(r[i][v]));
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+    if (lane == 0) wmax[wave] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    const int e = block_exp(amax);
+    const float inv = __builtin_ldexpf(1.f, -e);
+    if (threadIdx.x == 0) scales[((size_t)b * H + h) * nb + blk] = __builtin_ldexpf(1.f, e);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        const int t = blk * QB + wave * 32 + i;
+        if (t >= N) continue;
+        uint8_t* out = codes + ((size_t)b * N + t) * ld + (size_t)h * D + lane * V;
+        if constexpr (V == 1) {
+            out[0] = (uint8_t)(cvt2<false>(r[i][0] * inv, 0.f, 0u) & 0xFF);
+        } else if constexpr (V == 2) {
+            *reinterpret_cast<uint16_t*>(out) = (uint16_t)(cvt2<false>(r[i][0] * inv, r[i][1] * inv, 0u) & 0xFFFF);
+        } else {
+            uint32_t w = cvt2<false>(r[i][0] * inv, r[i][1] * inv, 0u);
+            w = cvt2<true>(r[i][2] * inv, r[i][3] * inv, w);
+            *reinterpret_cast<uint32_t*>(out) = w;
+        }
+    }
+}
+
+// ---------------------------------------------------------------- V
+// Pass 1: per-channel |v| maximum over the sequence, as float bits (order-
+// preserving for non-negative values) with atomic max into `scales`, which the
+// clear kernel zeroed first. Pass 2 turns it into 2^e and writes the codes.
+__global__ void clear_kernel(float* p, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0.f;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void v_amax_kernel(const T* __restrict__ v, float* __restrict__ scales, int N,
+                                                     int Hkv) {
+    constexpr int RPI = 256 / D;  // rows per iteration of the workgroup
+    const int g = blockIdx.y, b = blockIdx.z;
+    const int c = threadIdx.x % D, r0 = threadIdx.x / D;
+    const int t0 = blockIdx.x * 256;
+    float m = 0.f;
+    for (int t = t0 + r0; t < min(N, t0 + 256); t += RPI)
+        m = fmaxf(m, fabsf((float)v[(((size_t)b * N + t) * Hkv + g) * D + c]));
+    atomicMax(reinterpret_cast<unsigned int*>(scales) + ((size_t)b * Hkv + g) * D + c, __float_as_uint(m));
+}
+
+// One workgroup per (64-key chunk, kv head, sequence). Key n = 32 b + 8 i + 4 kg + j
+// of a chunk goes to byte 32 kg + 16 b + 4 i + j of each channel's 64-byte
+// chunk row; keys at or past N are zero.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void v_quant_kernel(const T* __restrict__ v, uint8_t* __restrict__ codes_t,
+                                                      const float* __restrict__ amax, int N, int Hkv, int NP) {
+    __shared__ float tile[64][D + 1];
+    const int ch = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    for (int e = threadIdx.x; e < 64 * D; e += 256) {
+        const int kk = e / D, c = e % D, t = ch * 64 + kk;
+        tile[kk][c] = t < N ? (float)v[(((size_t)b * N + t) * Hkv + g) * D + c] : 0.f;
+    }
+    __syncthreads();
+    // 4-byte words of the output: (channel c, kg, b2, i) holds keys 32 b2 + 8 i + 4 kg + 0..3
+    for (int wi = threadIdx.x; wi < D * 16; wi += 256) {
+        const int c = wi / 16, p = wi % 16;  // p = 8 kg + 4 b2 + i
+        const int kg = p >> 3, b2 = (p >> 2) & 1, i = p & 3;
+        const int k0 = 32 * b2 + 8 * i + 4 * kg;
+        const int e = block_exp(amax[((size_t)b * Hkv + g) * D + c]);
+        const float inv = __builtin_ldexpf(1.f, -e);
+        uint32_t w = cvt2<false>(tile[k0][c] * inv, tile[k0 + 1][c] * inv, 0u);
+        w = cvt2<true>(tile[k0 + 2][c] * inv, tile[k0 + 3][c] * inv, w);
+        *reinterpret_cast<uint32_t*>(codes_t + (((size_t)b * Hkv + g) * D + c) * NP + ch * 64 + 4 * p) = w;
+    }
+}
+
+__global__ void v_scale_kernel(float* scales, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) scales[i] = __builtin_ldexpf(1.f, block_exp(scales[i]));
+}
+
+// ---------------------------------------------------------------- forward
+constexpr int F8_BR = 256;  // query rows per workgroup (8 waves x 32)
+constexpr int F8_BC = 128;  // keys per K / V^T tile (one K scale block)
+constexpr int F8_NT = 512;
+
+struct Fp8Args {
+    const uint8_t* q;   // [B, N, H, D]
+    const uint8_t* k;   // [B, N, Hkv, D]
+    const uint8_t* vt;  // [B, Hkv, D, NP]
+    const float* qs;    // [B, H, nb]
+    const float* ks;    // [B, Hkv, nb]
+    const float* vs;    // [B, Hkv, D]
+    void* out;          // [B, N, H, D]
+    float* lse;         // [B, H, N]
+    int B, H, Hkv, N, G, NP, nb;
+    float scale_log2;   // softmax scale * log2(e) (already divided by D under the rotation)
+};
+
+template <typename TO, int D, bool CAUSAL>
+__global__ __launch_bounds__(F8_NT, 1) void fwd_fp8_kernel(Fp8Args a) {
+    // byte tiles viewed as 16-bit rows of D / 2 (K: keys x D bytes) and
+    // F8_BC / 2 (V^T: channels x F8_BC bytes) elements, swizzled like the
+    // 16-bit tiles; two named stages
+    constexpr int KT = F8_BC * D / 2, VT = D * F8_BC / 2;  // uint16 elements
+    constexpr int DK = D / 2, DV = F8_BC / 2;               // 16-bit row lengths
+    __shared__ __attribute__((aligned(16))) uint16_t stA[KT + VT];
+    __shared__ __attribute__((aligned(16))) uint16_t stB[KT + VT];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 31, kg = lane >> 5;
+    const int h = (blockIdx.x % a.Hkv) * a.G + blockIdx.x / a.Hkv;  // kv-head-major columns
+    const int b = blockIdx.y;
+    const int qt = CAUSAL ? (int)(gridDim.z - 1 - blockIdx.z) : (int)blockIdx.z;
+    const int len = a.N;
+    const int q0 = qt * F8_BR;
+    if (q0 >= len) return;
+    const int g = h / a.G;
+    const int qw = q0 + wave * 32, qi = qw + col;
+    const bool wave_live = qw < len;
+
+    // Q^T operand: lane (query qi, kg) holds bytes 64 kk + 32 kg .. + 31 of the row
+    constexpr int NKK = D / 64;
+    v8i qf[NKK];
+    {
+        const uint8_t* qr = a.q + (((size_t)b * a.N + qi) * a.H + h) * D;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            uint4 lo = make_uint4(0, 0, 0, 0), hi = lo;
+            if (qi < len) {
+                lo = *reinterpret_cast<const uint4*>(qr + 64 * kk + 32 * kg);
+                hi = *reinterpret_cast<const uint4*>(qr + 64 * kk + 32 * kg + 16);
+            }
+            qf[kk] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
+    }
+    // the wave's 32 queries lie in one Q scale block (128 = 4 x 32, aligned)
+    const float sq = wave_live ? a.qs[((size_t)b * a.H + h) * a.nb + qw / QB] : 0.f;
+
+    // operand offsets (16-bit units) of a lane's two 16-byte chunks: K row
+    // 32 kb + col, byte column 64 kk + 32 kg; V^T row 32 db + col, byte column
+    // 64 m + 32 kg (chunk m of the tile)
+    int koff[NKK][2], voff[2][2];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+        koff[kk][0] = swz<DK>(col, 32 * kk + 16 * kg);
+        koff[kk][1] = swz<DK>(col, 32 * kk + 16 * kg + 8);
+    }
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        voff[m][0] = swz<DV>(col, 32 * m + 16 * kg);
+        voff[m][1] = swz<DV>(col, 32 * m + 16 * kg + 8);
+    }
+
+    const int kend = CAUSAL ? min(len, q0 + F8_BR) : len;
+    const int nkt = (kend + F8_BC - 1) / F8_BC;
+    const uint16_t* Kg = reinterpret_cast<const uint16_t*>(a.k + ((size_t)b * a.N * a.Hkv + g) * D);
+    const uint16_t* Vg = reinterpret_cast<const uint16_t*>(a.vt + ((size_t)b * a.Hkv + g) * D * (size_t)a.NP);
+    DmaTile<DK, F8_BC, F8_NT / 64> kdma;
+    kdma.init(wave, lane, (size_t)a.Hkv * DK);
+    DmaTile<DV, D, F8_NT / 64> vdma;
+    vdma.init(wave, lane, (size_t)a.NP / 2);
+    auto issue = [&](uint16_t* st, int kt) {
+        kdma.issue(st, Kg, kt * F8_BC, len, wave);
+        // V^T rows are channels: the tile is columns kt * F8_BC .. of every row
+        vdma.issue(st + KT, Vg + kt * (F8_BC / 2), 0, D, wave);
+    };
+
+    f32x16 oacc[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
+    float m_ref = -INFINITY, l_run = 0.f, l_rnd = 0.f;
+    const float c2q = a.scale_log2 * sq;
+    const float* ksb = a.ks + ((size_t)b * a.Hkv + g) * a.nb;
+
+    auto compute = [&](const uint16_t* S, int kt) {
+        const int k0 = kt * F8_BC;
+        if (!(wave_live && (!CAUSAL || k0 <= qw + 31))) return;
+        const uint16_t* Ks = S;
+        const uint16_t* Vs = S + KT;
+        const float c2 = c2q * ksb[kt];  // scale x log2(e) x Q block scale x K block scale
+
+        f32x16 s[F8_BC / 32];
+        auto score_product = [&]() {
+#pragma unroll
+            for (int kb = 0; kb < F8_BC / 32; ++kb) {
+                s[kb] = f32x16{};
+#pragma unroll
+                for (int kk = 0; kk < NKK; ++kk) {
+                    const uint4 lo = ld_s16(Ks + 32 * kb * DK + koff[kk][0]);
+                    const uint4 hi = ld_s16(Ks + 32 * kb * DK + koff[kk][1]);
+                    const v8i kf = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                                    (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                    s[kb] = mma_f8(kf, qf[kk], s[kb]);
+                }
+            }
+        };
+        score_product();
+
+        const bool edge = (k0 + F8_BC > len) || (CAUSAL && k0 + F8_BC - 1 > qw);
+        float ls = 0.f;
+        bool need_max = true;
+        if (kt != 0 && !edge) {
+            // maximum-free: P against the reference; every P of a lane at most
+            // its sum, which must stay within e4m3 (448)
+            need_max = false;
+#pragma unroll
+            for (int kb = 0; kb < F8_BC / 32; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float p = exp2_fast(fmaf(s[kb][r], c2, -m_ref));
+                    s[kb][r] = p;
+                    ls += p;
+                }
+            if (__any(!(ls <= 448.f))) {
+                score_product();
+                need_max = true;
+                ls = 0.f;
+            }
+        }
+        if (need_max) {
+            const int lim_len = len - k0 - 4 * kg, lim_q = qi - k0 - 4 * kg;
+            float mt = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < F8_BC / 32; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float t = s[kb][r] * c2;
+                    const int kofs = 32 * kb + 8 * (r >> 2) + (r & 3);
+                    if (edge && (kofs >= lim_len || (CAUSAL && kofs > lim_q))) t = -INFINITY;
+                    s[kb][r] = t;
+                    mt = fmaxf(mt, t);
+                }
+            mt = max_xor32(mt);
+            const bool raise = mt > m_ref + 8.f;
+            if (__any(raise)) {
+                const float m_new = raise ? mt : m_ref;
+                const float alpha = raise ? exp2_fast(m_ref - mt) : 1.f;
+                l_run *= alpha;
+                l_rnd *= alpha;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+                m_ref = m_new;
+            }
+            const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+#pragma unroll
+            for (int kb = 0; kb < F8_BC / 32; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float p = exp2_fast(s[kb][r] - m_use);
+                    s[kb][r] = p;
+                    ls += p;
+                }
+        }
+        l_run += ls;
+
+        // P^T as e4m3, chunk m of 64 keys: byte e = 16 b + r is element r of s[2m + b];
+        // the rounded values are summed back for the normalizer
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            uint32_t w[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int bb = q >> 2, r0 = 4 * (q & 3);
+                const f32x16& sv = s[2 * m + bb];
+                w[q] = cvt2<true>(sv[r0 + 2], sv[r0 + 3], cvt2<false>(sv[r0], sv[r0 + 1], 0u));
+            }
+            float r0s = 0.f, r1s = 0.f;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[q], false);
+                const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[q], true);
+                r0s += lo[0] + hi[0];
+                r1s += lo[1] + hi[1];
+            }
+            l_rnd += r0s + r1s;
+            const v8i pf = {(int)w[0], (int)w[1], (int)w[2], (int)w[3], (int)w[4], (int)w[5], (int)w[6], (int)w[7]};
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+                const uint4 lo = ld_s16(Vs + 32 * db * DV + voff[m][0]);
+                const uint4 hi = ld_s16(Vs + 32 * db * DV + voff[m][1]);
+                const v8i vf = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                                (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                oacc[db] = mma_f8(vf, pf, oacc[db]);
+            }
+        }
+    };
+
+    two_stage_loop(stA, stB, nkt, issue, compute);
+
+    const float l_tot = sum_xor32(l_run);
+    const float lr_tot = sum_xor32(l_rnd);
+    if (qi < len) {
+        const float inv = 1.f / lr_tot;
+        const float* vsc = a.vs + ((size_t)b * a.Hkv + g) * D;
+        TO* O = reinterpret_cast<TO*>(a.out) + (((size_t)b * a.N + qi) * a.H + h) * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int d0 = 32 * db + 8 * i + 4 * kg;
+                const float4 sc = *reinterpret_cast<const float4*>(vsc + d0);
+                *reinterpret_cast<uint2*>(O + d0) =
+                    pack4<TO>(oacc[db][4 * i] * inv * sc.x, oacc[db][4 * i + 1] * inv * sc.y,
+                              oacc[db][4 * i + 2] * inv * sc.z, oacc[db][4 * i + 3] * inv * sc.w);
+            }
+        }
+        if (kg == 0) a.lse[((size_t)b * a.H + h) * a.N + qi] = (m_ref + __log2f(l_tot)) * kLn2;
+    }
+}
+
+template <typename T, int D>
+hipError_t quant_qk_d(const void* x, uint8_t* codes, float* scales, int B, int N, int H,
+                      const unsigned long long* signs, hipStream_t s) {
+    dim3 grid((N + QB - 1) / QB, H, B);
+    if (signs)
+        hipLaunchKernelGGL((quant_qk_kernel<T, D, true>), grid, dim3(256), 0, s, reinterpret_cast<const T*>(x), codes,
+                           scales, N, H, signs[0], D > 64 ? signs[1] : 0ull);
+    else
+        hipLaunchKernelGGL((quant_qk_kernel<T, D, false>), grid, dim3(256), 0, s, reinterpret_cast<const T*>(x),
+                           codes, scales, N, H, 0ull, 0ull);
+    return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t quant_v_d(const void* v, uint8_t* codes_t, float* scales, int B, int N, int Hkv, hipStream_t s) {
+    const int n = B * Hkv * D;
+    const int NP = fp8_keys_padded(N);
+    hipLaunchKernelGGL(clear_kernel, dim3((n + 255) / 256), dim3(256), 0, s, scales, n);
+    hipLaunchKernelGGL((v_amax_kernel<T, D>), dim3((N + 255) / 256, Hkv, B), dim3(256), 0, s,
+                       reinterpret_cast<const T*>(v), scales, N, Hkv);
+    hipLaunchKernelGGL((v_quant_kernel<T, D>), dim3(NP / 64, Hkv, B), dim3(256), 0, s,
+                       reinterpret_cast<const T*>(v), codes_t, scales, N, Hkv, NP);
+    hipLaunchKernelGGL(v_scale_kernel, dim3((n + 255) / 256), dim3(256), 0, s, scales, n);
+    return hipGetLastError();
+}
+
+template <typename TO, int D>
+hipError_t fwd_d(const Fp8Args& a, bool causal, hipStream_t s) {
+    dim3 grid(a.H, a.B, (a.N + F8_BR - 1) / F8_BR);
+    if (causal)
+        hipLaunchKernelGGL((fwd_fp8_kernel<TO, D, true>), grid, dim3(F8_NT), 0, s, a);
+    else
+        hipLaunchKernelGGL((fwd_fp8_kernel<TO, D, false>), grid, dim3(F8_NT), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quant_qk(const void* x, uint8_t* codes, float* scales, int B, int N, int H, int d,
+                           const unsigned long long* signs, int dtype, hipStream_t s) {
+    if (dtype == 2)
+        return d == 64 ? quant_qk_d<__bf16, 64>(x, codes, scales, B, N, H, signs, s)
+                       : quant_qk_d<__bf16, 128>(x, codes, scales, B, N, H, signs, s);
+    return d == 64 ? quant_qk_d<_Float16, 64>(x, codes, scales, B, N, H, signs, s)
+                   : quant_qk_d<_Float16, 128>(x, codes, scales, B, N, H, signs, s);
+}
+
+hipError_t launch_quant_v(const void* v, uint8_t* codes_t, float* scales, int B, int N, int Hkv, int d, int dtype,
+                          hipStream_t s) {
+    if (dtype == 2)
+        return d == 64 ? quant_v_d<__bf16, 64>(v, codes_t, scales, B, N, Hkv, s)
+                       : quant_v_d<__bf16, 128>(v, codes_t, scales, B, N, Hkv, s);
+    return d == 64 ? quant_v_d<_Float16, 64>(v, codes_t, scales, B, N, Hkv, s)
+                   : quant_v_d<_Float16, 128>(v, codes_t, scales, B, N, Hkv, s);
+}
+
+hipError_t launch_fwd_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* vt, const float* qs, const float* ks,
+                          const float* vs, void* out, float* lse, int B, int H, int Hkv, int N, int d,
+                          float scale_log2, bool causal, int out_dtype, hipStream_t s) {
+    Fp8Args a{};
+    a.q = q;
+    a.k = k;
+    a.vt = vt;
+    a.qs = qs;
+    a.ks = ks;
+    a.vs = vs;
+    a.out = out;
+    a.lse = lse;
+    a.B = B;
+    a.H = H;
+    a.Hkv = Hkv;
+    a.N = N;
+    a.G = H / Hkv;
+    a.NP = fp8_keys_padded(N);
+    a.nb = (N + QB - 1) / QB;
+    a.scale_log2 = scale_log2;
+    if (out_dtype == 2) return d == 64 ? fwd_d<__bf16, 64>(a, causal, s) : fwd_d<__bf16, 128>(a, causal, s);
+    return d == 64 ? fwd_d<_Float16, 64>(a, causal, s) : fwd_d<_Float16, 128>(a, causal, s);
+}
+
+}  // namespace fa

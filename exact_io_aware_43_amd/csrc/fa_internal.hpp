@@ -80,4 +80,14 @@ hipError_t launch_bwd(const Args& a, int dtype, int d, bool causal, bool alibi, 
                       hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int d, bool causal, bool alibi, hipStream_t s);
 
+// FP8 path: keys of the transposed V codes, padded to whole 128-key tiles.
+inline int fp8_keys_padded(int N) { return (N + 127) & ~127; }
+hipError_t launch_quant_qk(const void* x, uint8_t* codes, float* scales, int B, int N, int H, int d,
+                           const unsigned long long* signs, int dtype, hipStream_t s);
+hipError_t launch_quant_v(const void* v, uint8_t* codes_t, float* scales, int B, int N, int Hkv, int d, int dtype,
+                          hipStream_t s);
+hipError_t launch_fwd_fp8(const uint8_t* q, const uint8_t* k, const uint8_t* vt, const float* qs, const float* ks,
+                          const float* vs, void* out, float* lse, int B, int H, int Hkv, int N, int d,
+                          float scale_log2, bool causal, int out_dtype, hipStream_t s);
+
 }  // namespace fa

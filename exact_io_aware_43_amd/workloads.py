@@ -139,6 +139,28 @@ def make_decode_inputs(w: Workload, Nq: int, lengths=None, seed: int = 0) -> dic
     }
 
 
+def make_outlier_inputs(w: Workload, seed: int = 0, frac: float = 1e-3, mag: float = 10.0) -> dict:
+    """Dense Q, K, V like :func:`make_inputs` (no dO), except that a fraction
+    ``frac`` of the entries of each, drawn at random, is multiplied by ``mag``:
+    unit-normal features with rare large outliers, the kind of input the FP8
+    path's rotation is meant for."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = {}
+    for name, heads in (("q", w.H), ("k", w.Hkv), ("v", w.Hkv)):
+        x = rng.standard_normal(size=(w.B, w.N, heads, w.d), dtype=np.float32)
+        x[rng.random(size=x.shape) < frac] *= np.float32(mag)
+        out[name] = torch.from_numpy(x).to(_TORCH_DTYPE[w.dtype])
+    out.update(do=None, cu_seqlens=None, alibi_slopes=None, scale=1.0 / math.sqrt(w.d), max_seqlen=w.N)
+    return out
+
+
+def hadamard_signs(d: int, seed: int = 0) -> np.ndarray:
+    """d random signs (+1 or -1, float64), the diagonal that precedes the
+    Walsh-Hadamard rotation of the FP8 path."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return np.where(rng.random(d) < 0.5, -1.0, 1.0)
+
+
 def seq_lengths(inputs: dict, w: Workload) -> list:
     """Per-sequence lengths of a drawn batch (all N for dense inputs)."""
     cu = inputs["cu_seqlens"]

@@ -65,7 +65,7 @@ typedef enum fa_dtype {
 typedef enum fa_status {
     FA_OK = 0,
     FA_ERR_INVALID_ARG = -1, /* null pointer, bad size, H % Hkv != 0, non-finite scale, misalignment */
-    FA_ERR_UNSUPPORTED = -2, /* head dim not in {64, 128}; fp32 backward */
+    FA_ERR_UNSUPPORTED = -2, /* head dim or type combination not built (see fa_strerror) */
     FA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than fa_bwd_workspace_size() */
     FA_ERR_LAUNCH = -4,      /* the kernel launch itself failed */
     FA_ERR_SCRATCH = -5      /* fa_bwd_noalloc: problem larger than its built-in scratch */
@@ -79,7 +79,7 @@ typedef enum fa_status {
  *
  *   B, H, Hkv, N, d : batch (number of sequences), query heads, kv heads
  *                     (H % Hkv == 0), sequence length (maximum length when
- *                     packed), head dimension (64 or 128).
+ *                     packed), head dimension (32, 64, 128 or 256).
  *   scale           : multiplies Q K^T before the softmax (1/sqrt(d) is usual).
  *   causal          : 0 or 1; 1 keeps key j <= query i.
  */
@@ -294,6 +294,66 @@ const char* fa_strerror(int status);
 
 /* Library version as MAJOR * 10000 + MINOR * 100 + PATCH. */
 int fa_version(void);
+
+/*
+ * FP8 forward: attention computed on e4m3 codes with power-of-two block
+ * scales, optionally after a random-sign Walsh-Hadamard rotation of Q and K
+ * (page "FlashAttention: Faster Attention Without Dropping a Single
+ * Interaction", Method Deep Dive, Key design 4, the FP8 row of the version
+ * table: block quantization and incoherent processing; its Limitations
+ * section, "Numerical exactness, low precision, and reproducibility", gives
+ * the error of FP8 against an exact reference with and without them).
+ *
+ * Format: OCP e4m3 "fn" (bias 7, largest finite 448, round to nearest even).
+ * A block's scale is 2^e, the smallest power of two with amax <= 448 2^e, so
+ * a code is the rounding of x / 2^e alone and x ~ decode(code) * 2^e.
+ *
+ * Three calls: quantize Q and K (fa_quantize_fp8_qk), quantize V
+ * (fa_quantize_fp8_v), then fa_fwd_fp8. Every buffer is caller-owned device
+ * memory, 16-byte aligned; calls enqueue on `stream` and return at once.
+ * FA_FP16 / FA_BF16 inputs and outputs; d in {64, 128} (other head dims and
+ * FA_FP32 are FA_ERR_UNSUPPORTED). No ALiBi, window, packed sequences or
+ * backward on this path.
+ *
+ * fa_quantize_fp8_qk: x [B, N, H, d] (H = Hkv for K) -> codes uint8
+ *   [B, N, H, d] and scales float [B, H, ceil(N / 128)]: one scale per
+ *   sequence, head and block of 128 tokens. hadamard_signs: NULL, or host
+ *   memory holding d / 64 words whose bit i % 64 of word i / 64 set means a
+ *   sign of -1 for dim i; each row is then multiplied by those signs and by
+ *   the unnormalized d x d Walsh-Hadamard matrix (Sylvester order; fp32
+ *   butterflies over strides 1, 2, 4, ...) before quantization. Q and K must
+ *   use the same signs. The words are read during the call.
+ *
+ * fa_quantize_fp8_v: v [B, N, Hkv, d] -> codes_t uint8 [B, Hkv, d, NP] with
+ *   NP = fa_fp8_v_keys(N) (N rounded up to a multiple of 128; keys past N are
+ *   zero codes), and scales float [B, Hkv, d]: one scale per sequence, kv head
+ *   and channel over the whole sequence. Inside each 64-key chunk of a
+ *   channel row, key 32 b + 8 i + 4 g + j (b, g in {0, 1}; i, j in 0..3) sits
+ *   at byte 32 g + 16 b + 4 i + j, the order the matrix-core operands read.
+ *
+ * fa_fwd_fp8: O [B, N, H, d] (out_dtype) and lse float [B, H, N] (natural
+ *   log) of softmax(scale Q K^T) V on the dequantized inputs, the softmax
+ *   probabilities themselves rounded to e4m3 (in [0, 448]) before they
+ *   multiply V, and O divided by the sum of those rounded values (lse uses
+ *   the unrounded ones). rotated = 1 when Q and K were quantized with
+ *   hadamard_signs: the scale is then divided by d (the rotation multiplies
+ *   every score by d). causal as fa_fwd; GQA when H > Hkv.
+ */
+int fa_fp8_v_keys(int N);
+
+int fa_quantize_fp8_qk(const void* x, unsigned char* codes, float* scales,
+                       int B, int N, int H, int d,
+                       const unsigned long long* hadamard_signs, fa_dtype dtype,
+                       void* stream);
+
+int fa_quantize_fp8_v(const void* v, unsigned char* codes_t, float* scales,
+                      int B, int N, int Hkv, int d, fa_dtype dtype, void* stream);
+
+int fa_fwd_fp8(const unsigned char* q, const unsigned char* k, const unsigned char* v_t,
+               const float* q_scales, const float* k_scales, const float* v_scales,
+               void* o, float* lse, int B, int H, int Hkv, int N, int d,
+               float scale, int causal, int rotated, fa_dtype out_dtype,
+               void* stream);
 
 #ifdef __cplusplus
 }

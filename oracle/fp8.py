@@ -17,7 +17,9 @@ name the techniques without fixing their details; the readings taken here:
    nothing saturates.
 2. Block scales are powers of two: the scale exponent of a block is the
    smallest e with amax <= 448 * 2^e, so x * 2^-e is exact and the code of an
-   element depends on x alone. Q and K: one exponent per (sequence, head,
+   element depends on x alone; e is at least -127, so that the scale and its
+   reciprocal are finite fp32 numbers (only blocks with amax below
+   448 * 2^-128, about 1.3e-36, are affected). Q and K: one exponent per (sequence, head,
    block of 128 tokens). V: one exponent per (sequence, kv head, channel) over
    the whole sequence, which folds into the output exactly
    (O[:, c] = 2^e_c * sum_j P_j V8[j, c]).
@@ -114,13 +116,17 @@ def fwht_f32(x: np.ndarray) -> np.ndarray:
     return y
 
 
+E_MIN = -127
+
+
 def block_exponent(amax) -> np.ndarray:
-    """Smallest integer e with amax <= 448 * 2^e (0 where amax = 0). Exact: with
-    amax = m 2^E, m in [1, 2), it is E - 8 if m <= 1.75 and E - 7 otherwise."""
+    """Smallest integer e >= -127 with amax <= 448 * 2^e (0 where amax = 0).
+    Exact: with amax = m 2^E, m in [1, 2), it is E - 8 if m <= 1.75 and E - 7
+    otherwise, raised to -127 if lower (reading 2)."""
     a = np.asarray(amax, dtype=np.float64)
     m, E = np.frexp(np.where(a > 0, a, 1.0))  # a = m 2^E, m in [0.5, 1)
     m, E = 2 * m, E - 1
-    e = np.where(m <= 1.75, E - 8, E - 7)
+    e = np.maximum(np.where(m <= 1.75, E - 8, E - 7), E_MIN)
     return np.where(a > 0, e, 0).astype(np.int64)
 
 

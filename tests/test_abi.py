@@ -33,6 +33,7 @@ def test_header_declares_expected_api():
         ["fa_fwd", "fa_fwd_dropout", "fa_fwd_ext", "fa_bwd", "fa_bwd_dropout", "fa_bwd_ext", "fa_bwd_stages",
          "fa_bwd_workspace_size",
          "fa_bwd_noalloc", "fa_bwd_noalloc_max_bytes", "fa_fwd_kvcache", "fa_kvcache_workspace_size",
+         "fa_fp8_v_keys", "fa_quantize_fp8_qk", "fa_quantize_fp8_v", "fa_fwd_fp8",
          "fa_strerror", "fa_version"])
 
 
@@ -326,3 +327,59 @@ def _kv(**kw):
 ])
 def test_kvcache_rejects(kw, expect):
     assert _kv(**kw) == expect
+
+
+def test_fp8_v_keys():
+    """Transposed V codes are padded to whole 128-key tiles."""
+    assert [fa.fa_fp8_v_keys(n) for n in (1, 127, 128, 129, 1000, 16384)] == [128, 128, 128, 256, 1024, 16384]
+    assert fa.fa_fp8_v_keys(0) == 0 and fa.fa_fp8_v_keys(-3) == 0
+
+
+def _q8(**kw):
+    a = dict(x=PTR[0], codes=PTR[1], scales=PTR[2], B=1, N=300, H=4, d=128, signs=None, dtype=fa.FA_BF16)
+    a.update(kw)
+    return fa.fa_quantize_fp8_qk(a["x"], a["codes"], a["scales"], a["B"], a["N"], a["H"], a["d"], a["signs"],
+                                 a["dtype"], None)
+
+
+def _v8(**kw):
+    a = dict(v=PTR[0], codes=PTR[1], scales=PTR[2], B=1, N=300, Hkv=2, d=64, dtype=fa.FA_FP16)
+    a.update(kw)
+    return fa.fa_quantize_fp8_v(a["v"], a["codes"], a["scales"], a["B"], a["N"], a["Hkv"], a["d"], a["dtype"], None)
+
+
+def _f8(**kw):
+    a = dict(q=PTR[0], k=PTR[1], v=PTR[2], qs=PTR[3], ks=PTR[4], vs=PTR[5], o=PTR[6], lse=PTR[7], B=1, H=4, Hkv=2,
+             N=300, d=128, scale=0.1, causal=1, rotated=0, dtype=fa.FA_BF16)
+    a.update(kw)
+    return fa.fa_fwd_fp8(a["q"], a["k"], a["v"], a["qs"], a["ks"], a["vs"], a["o"], a["lse"], a["B"], a["H"],
+                         a["Hkv"], a["N"], a["d"], a["scale"], a["causal"], a["rotated"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("call,kw,expect", [
+    (_q8, dict(x=None), INVALID), (_q8, dict(codes=PTR[1] + 4), INVALID), (_q8, dict(N=0), INVALID),
+    (_q8, dict(H=0), INVALID), (_q8, dict(d=32), UNSUPPORTED), (_q8, dict(d=256), UNSUPPORTED),
+    (_q8, dict(dtype=fa.FA_FP32), UNSUPPORTED), (_q8, dict(dtype=7), INVALID),
+    (_q8, dict(B=1 << 12, N=1 << 12, H=1 << 8), INVALID),
+    (_v8, dict(scales=None), INVALID), (_v8, dict(v=PTR[0] + 2), INVALID), (_v8, dict(Hkv=-1), INVALID),
+    (_v8, dict(d=96), UNSUPPORTED), (_v8, dict(dtype=fa.FA_FP32), UNSUPPORTED),
+    (_f8, dict(vs=None), INVALID), (_f8, dict(lse=PTR[7] + 4), INVALID), (_f8, dict(H=6, Hkv=4), INVALID),
+    (_f8, dict(causal=2), INVALID), (_f8, dict(rotated=5), INVALID), (_f8, dict(scale=math.inf), INVALID),
+    (_f8, dict(d=256), UNSUPPORTED), (_f8, dict(dtype=fa.FA_FP32), UNSUPPORTED), (_f8, dict(dtype=-1), INVALID),
+    (_f8, dict(N=0), INVALID),
+])
+def test_fp8_rejects(call, kw, expect):
+    """FP8 entry points check every argument before any launch (no device call here)."""
+    assert call(**kw) == expect
+
+
+def test_hadamard_sign_words():
+    signs = [1.0] * 128
+    for i in (0, 5, 63, 64, 127):
+        signs[i] = -1.0
+    w = fa.hadamard_sign_words(signs, 128)
+    assert list(w) == [(1 << 0) | (1 << 5) | (1 << 63), (1 << 0) | (1 << 63)]
+    with pytest.raises(ValueError):
+        fa.hadamard_sign_words([1.0] * 127 + [0.5], 128)
+    with pytest.raises(ValueError):
+        fa.hadamard_sign_words([1.0] * 64, 128)

@@ -109,6 +109,18 @@ def test_block_exponent():
         e = int(F8.block_exponent(v))
         assert v <= 448 * 2.0 ** e and not (v <= 448 * 2.0 ** (e - 1)), (v, e)
     assert int(F8.block_exponent(0.0)) == 0
+    # the floor at -127: tinier blocks keep it, 449 * 2^-127 needs -126
+    assert int(F8.block_exponent(448.0 * 2.0 ** -127)) == -127
+    assert int(F8.block_exponent(449.0 * 2.0 ** -127)) == -126
+    for tiny in (448.0 * 2.0 ** -128, 1e-38, 2.0 ** -140, 2.0 ** -149):
+        assert int(F8.block_exponent(tiny)) == -127
+    # a block of subnormal-range values: scaled by 2^127, still within range and exact
+    x = np.zeros((1, 128, 1, 64), dtype=np.float32)
+    x[0, :, 0, 0] = 2.0 ** -130
+    x[0, 3, 0, 5] = -3 * 2.0 ** -133
+    c, e = F8.quantize_qk(x)
+    assert int(e[0, 0, 0]) == -127
+    np.testing.assert_array_equal(F8.dequantize_qk(c, e), x.astype(np.float64))
 
 
 def test_quantize_qk_blocks():
