@@ -46,6 +46,7 @@ sys.path.insert(0, ROOT)
 METRIC = "attention fwd/bwd TFLOP/s, bf16 causal d=128, and % of MI355X MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 4096 dense bf16 FLOP/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
+PEAK_FP8_TFLOPS = 5033.2  # 256 CU x 8192 dense fp8 FLOP/clk x 2.4 GHz
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = os.path.join(ROOT, "exact_io_aware_43_amd", "csrc")
 KERNEL_SOURCES = {  # what each kernel's machine code depends on (the build flags included)
@@ -116,6 +117,9 @@ def main():
 
     if args.workload == "decode":
         bench_decode(args)
+        return
+    if args.workload.startswith("fp8"):
+        bench_fp8(args)
         return
     w = WORKLOADS[args.workload]
     if w.dtype == "fp32":
@@ -415,6 +419,110 @@ def bench_decode(args):
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
                      "avg_launch_ms": round(ms, 4), "work_per_launch": int(alg_bytes)},
         "splits": int(splits),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_fp8(args):
+    """The FP8 forward (fa_quantize_fp8_qk for Q and K with the Hadamard rotation,
+    fa_quantize_fp8_v, fa_fwd_fp8) on the shape of the long causal workload
+    (``--workload fp8``) or of another named one (``--workload fp8:gqa``). A step
+    quantizes the 16-bit Q, K, V resident in device memory and runs the
+    attention; ``value`` counts the attention FLOPs of the step (4 B H N^2 d,
+    halved for causal) over the whole step. The roofline is the attention
+    kernel alone against the dense fp8 MFMA peak; the quantizers are HBM-bound
+    and listed with their byte rate; the 16-bit forward on the same inputs is
+    timed beside it."""
+    import torch
+
+    import exact_io_aware_43_amd as fa
+    from exact_io_aware_43_amd.workloads import WORKLOADS, flops, hadamard_signs, make_inputs
+
+    base = args.workload.split(":", 1)[1] if ":" in args.workload else "long_causal"
+    w = WORKLOADS[base]
+    if w.varlen is not None or w.alibi or w.d not in (64, 128):
+        raise SystemExit(f"the fp8 path takes dense inputs without ALiBi and d in (64, 128); {base} is not")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = make_inputs(w, args.seed, with_grad=False)
+    q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
+    B, H, Hkv, N, d = w.B, w.H, w.Hkv, w.N, w.d
+    dt = {"bf16": fa.FA_BF16, "fp16": fa.FA_FP16}[w.dtype]
+    causal = int(w.causal)
+    print(f"[bench] fp8 forward on {w}", file=sys.stderr, flush=True)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    words = fa.hadamard_sign_words(hadamard_signs(d, args.seed + 5), d)
+    import ctypes
+    sp = ctypes.addressof(words)
+    nb = (N + 127) // 128
+    npad = fa.fa_fp8_v_keys(N)
+    qc = torch.empty((B, N, H, d), dtype=torch.uint8, device=dev)
+    kc = torch.empty((B, N, Hkv, d), dtype=torch.uint8, device=dev)
+    vc = torch.empty((B, Hkv, d, npad), dtype=torch.uint8, device=dev)
+    qs = torch.empty((B, H, nb), dtype=torch.float32, device=dev)
+    ks = torch.empty((B, Hkv, nb), dtype=torch.float32, device=dev)
+    vs = torch.empty((B, Hkv, d), dtype=torch.float32, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+
+    def check(st):
+        if st:
+            raise fa.FaError(st)
+
+    def quant():
+        check(fa.fa_quantize_fp8_qk(q.data_ptr(), qc.data_ptr(), qs.data_ptr(), B, N, H, d, sp, dt, sh))
+        check(fa.fa_quantize_fp8_qk(k.data_ptr(), kc.data_ptr(), ks.data_ptr(), B, N, Hkv, d, sp, dt, sh))
+        check(fa.fa_quantize_fp8_v(v.data_ptr(), vc.data_ptr(), vs.data_ptr(), B, N, Hkv, d, dt, sh))
+
+    def attn():
+        check(fa.fa_fwd_fp8(qc.data_ptr(), kc.data_ptr(), vc.data_ptr(), qs.data_ptr(), ks.data_ptr(),
+                            vs.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, Hkv, N, d, inp["scale"], causal, 1,
+                            dt, sh))
+
+    def fwd16():
+        check(fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, Hkv, N, d,
+                        inp["scale"], causal, None, None, dt, sh))
+
+    def timed(fn, reps):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(reps):
+            fn()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / reps
+
+    for _ in range(args.warmup + 1):
+        quant()
+        attn()
+        fwd16()
+    torch.cuda.synchronize()
+    step_ms = timed(lambda: (quant(), attn()), args.steps)
+    print(f"[bench] {args.steps} steps: {step_ms:.4f} ms/step", file=sys.stderr, flush=True)
+    quant_ms = timed(quant, args.kernel_reps)
+    attn_ms = timed(attn, args.kernel_reps)
+    fwd16_ms = timed(fwd16, args.kernel_reps)
+    flop = flops(w)
+    tf = lambda ms: flop / (ms * 1e-3) / 1e12  # noqa: E731
+    qbytes = (B * N * (H + 2 * Hkv) * d) * 3 + 4 * (B * (H + Hkv) * nb + B * Hkv * d)
+    out = {
+        "metric": "attention fwd TFLOP/s, fp8 e4m3 with block scales and Hadamard rotation, causal d=128, "
+                  "and % of MI355X fp8 MFMA peak",
+        "value": round(tf(step_ms), 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(step_ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8-e4m3 (fp32 accumulate)", "data": "synthetic",
+        "config": {"workload": f"fp8:{base}", "B": B, "H": H, "Hkv": Hkv, "N": N, "d": d, "causal": bool(causal),
+                   "input_dtype": w.dtype, "pass": "quantize Q, K (rotated), V + forward"},
+        "kernels": {
+            "quantize_qkv": {"ms": round(quant_ms, 4), "hbm_gbs": round(qbytes / (quant_ms * 1e-3) / 1e9, 1),
+                             "bytes": int(qbytes)},
+            "fwd_fp8": {"ms": round(attn_ms, 4), "tflops": round(tf(attn_ms), 1)},
+            "fwd_bf16_same_inputs": {"ms": round(fwd16_ms, 4), "tflops": round(tf(fwd16_ms), 1)},
+        },
+        "roofline": {"kernel": "fwd_fp8_kernel", "bound": "mfma", "achieved": round(tf(attn_ms), 1),
+                     "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(tf(attn_ms) / PEAK_FP8_TFLOPS, 4),
+                     "traffic": None, "avg_launch_ms": round(attn_ms, 4), "work_per_launch": flop},
     }
     print(json.dumps(out), flush=True)
 

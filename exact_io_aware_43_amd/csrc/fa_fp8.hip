@@ -19,7 +19,9 @@
 //         chunk are contiguous bytes.
 //   P:    rounded to e4m3 for the second product (P <= 448 by the sum bound of
 //         the maximum-free path); O is divided by the sum of exactly those
-//         rounded values, lse uses the fp32 sum.
+//         rounded values, lse uses the fp32 sum. The rounded sums come from the
+//         matrix cores as well: one 16x16x128 product per 64-key chunk of a
+//         constant 0 / 1 operand with the P operand as it stands.
 //
 // e4m3 here is the OCP "fn" encoding that v_cvt_pk_fp8_f32 produces (round to
 // nearest even; values past 464 would become NaN, which the scaling rules out).
@@ -37,12 +39,18 @@ namespace fa {
 namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int QB = 128;  // tokens per Q / K scale block
 
 // 32x32x64 e4m3 x e4m3 -> fp32 (operand formats 0 and 0, unit E8M0 scales).
 __device__ __forceinline__ f32x16 mma_f8(v8i a, v8i b, f32x16 c) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// 16x16x128 e4m3 x e4m3 -> fp32.
+__device__ __forceinline__ f32x4 mma_f8_16(v8i a, v8i b, f32x4 c) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
 // Smallest e >= -127 with amax <= 448 * 2^e, from the bits of amax = m 2^E,
@@ -62,90 +70,90 @@ __device__ __forceinline__ uint32_t cvt2(float x0, float x1, uint32_t old) {
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, (int)old, HI);
 }
 
+// Eight 16-bit values of one 16-byte load as fp32 (exact).
+template <typename T>
+__device__ __forceinline__ void unpack8(const uint4 u, float* f) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if constexpr (std::is_same_v<T, __bf16>) {
+            f[2 * i] = __uint_as_float(w[i] << 16);
+            f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        } else {
+            f[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] & 0xFFFF));
+            f[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] >> 16));
+        }
+    }
+}
+
+// 16 fp32 values (already scaled into e4m3 range) as 16 codes in one uint4.
+__device__ __forceinline__ uint4 pack16(const float* x) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = cvt2<true>(x[4 * i + 2], x[4 * i + 3], cvt2<false>(x[4 * i], x[4 * i + 1], 0u));
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // ---------------------------------------------------------------- Q, K
-// One workgroup of 4 waves per (128-token block, head, sequence); a wave owns
-// 32 rows, a lane D / 64 consecutive dims of each. Pass 1 loads, rotates and
-// reduces |x|; pass 2 scales and stores the codes from the rows kept in
-// registers.
+// One workgroup of 2 waves per (128-token block, head, sequence); each lane owns
+// one row: D / 8 loads of 16 bytes, the sign flips and all log2(D) butterfly
+// stages in registers (no cross-lane traffic), then the block maximum over
+// both waves, the scale and D / 16 stores of 16 codes.
 template <typename T, int D, bool ROT>
-__global__ __launch_bounds__(256) void quant_qk_kernel(const T* __restrict__ x, uint8_t* __restrict__ codes,
+__global__ __launch_bounds__(128) void quant_qk_kernel(const T* __restrict__ x, uint8_t* __restrict__ codes,
                                                        float* __restrict__ scales, int N, int H,
                                                        unsigned long long s0, unsigned long long s1) {
-    constexpr int V = D / 64;  // dims per lane
-    __shared__ float wmax[4];
+    __shared__ float wmax[2];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int nb = (N + QB - 1) / QB;
-    const size_t ld = (size_t)H * D;
-    float sg[V];
+    const int t = blk * QB + threadIdx.x;
+    const size_t row = ((size_t)b * N + t) * H + h;  // row index of [B, N, H]
+    float r[D];
+    if (t < N) {
+        const uint4* src = reinterpret_cast<const uint4*>(x + row * D);
 #pragma unroll
-    for (int v = 0; v < V; ++v) {
-        const int dim = lane * V + v;  // sign bit of dim: bit dim % 64 of word dim / 64
-        sg[v] = (ROT && (((dim < 64 ? s0 : s1) >> (dim & 63)) & 1ull)) ? -1.f : 1.f;
+        for (int c = 0; c < D / 8; ++c) unpack8<T>(src[c], r + 8 * c);
+    } else {
+#pragma unroll
+        for (int i = 0; i < D; ++i) r[i] = 0.f;
     }
-
-    float r[32][V];
+    if (ROT) {
+        // signs (bit i % 64 of word i / 64 set: -1), then stages h = 1, 2, 4, ...:
+        // the pair (i, i + h) of every 2h-block becomes (a + b, a - b)
+#pragma unroll
+        for (int i = 0; i < D; ++i) {
+            const unsigned long long wd = i < 64 ? s0 : s1;
+            r[i] = __uint_as_float(__float_as_uint(r[i]) ^ ((uint32_t)((wd >> (i & 63)) & 1ull) << 31));
+        }
+#pragma unroll
+        for (int hh = 1; hh < D; hh *= 2) {
+#pragma unroll
+            for (int i = 0; i < D; ++i) {
+                if (i & hh) continue;
+                const float p = r[i], q = r[i + hh];
+                r[i] = p + q;
+                r[i + hh] = p - q;
+            }
+        }
+    }
     float amax = 0.f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-        const int t = blk * QB + wave * 32 + i;
-#pragma unroll
-        for (int v = 0; v < V; ++v) r[i][v] = 0.f;
-        if (t < N) {
-            const T* row = x + ((size_t)b * N + t) * ld + (size_t)h * D + lane * V;
-#pragma unroll
-            for (int v = 0; v < V; ++v) r[i][v] = (float)row[v] * sg[v];
-        }
-        if (ROT) {
-            // stages inside the lane (h < V), then across lanes (partner l ^ (h / V)):
-            // the lower index of a pair takes a + b, the upper a - b
-#pragma unroll
-            for (int hh = 1; hh < V; hh *= 2) {
-#pragma unroll
-                for (int v = 0; v < V; ++v) {
-                    if (v & hh) continue;
-                    const float a = r[i][v], c = r[i][v + hh];
-                    r[i][v] = a + c;
-                    r[i][v + hh] = a - c;
-                }
-            }
-#pragma unroll
-            for (int hh = V; hh < D; hh *= 2) {
-                const int m = hh / V;
-                const bool upper = (lane & m) != 0;
-#pragma unroll
-                for (int v = 0; v < V; ++v) {
-                    const float other = __shfl_xor(r[i][v], m);
-                    r[i][v] = upper ? other - r[i][v] : r[i][v] + other;
-                }
-            }
-        }
-#pragma unroll
-        for (int v = 0; v < V; ++v) amax = fmaxf(amax, fabsf(r[i][v]));
-    }
+    for (int i = 0; i < D; ++i) amax = fmaxf(amax, fabsf(r[i]));
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
     if (lane == 0) wmax[wave] = amax;
     __syncthreads();
-    amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    amax = fmaxf(wmax[0], wmax[1]);
     const int e = block_exp(amax);
     const float inv = __builtin_ldexpf(1.f, -e);
     if (threadIdx.x == 0) scales[((size_t)b * H + h) * nb + blk] = __builtin_ldexpf(1.f, e);
+    if (t >= N) return;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-        const int t = blk * QB + wave * 32 + i;
-        if (t >= N) continue;
-        uint8_t* out = codes + ((size_t)b * N + t) * ld + (size_t)h * D + lane * V;
-        if constexpr (V == 1) {
-            out[0] = (uint8_t)(cvt2<false>(r[i][0] * inv, 0.f, 0u) & 0xFF);
-        } else if constexpr (V == 2) {
-            *reinterpret_cast<uint16_t*>(out) = (uint16_t)(cvt2<false>(r[i][0] * inv, r[i][1] * inv, 0u) & 0xFFFF);
-        } else {
-            uint32_t w = cvt2<false>(r[i][0] * inv, r[i][1] * inv, 0u);
-            w = cvt2<true>(r[i][2] * inv, r[i][3] * inv, w);
-            *reinterpret_cast<uint32_t*>(out) = w;
-        }
-    }
+    for (int i = 0; i < D; ++i) r[i] *= inv;
+    uint4* dst = reinterpret_cast<uint4*>(codes + row * D);
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) dst[c] = pack16(r + 16 * c);
 }
 
 // ---------------------------------------------------------------- V
@@ -157,42 +165,77 @@ __global__ void clear_kernel(float* p, int n) {
     if (i < n) p[i] = 0.f;
 }
 
+// One workgroup per (256 rows, kv head, sequence): a thread reads 8 channels of
+// every (256 / (D / 8))-th row with 16-byte loads; lanes of equal channels
+// reduce by shuffles, the four waves through LDS, then one atomic per channel.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void v_amax_kernel(const T* __restrict__ v, float* __restrict__ scales, int N,
                                                      int Hkv) {
-    constexpr int RPI = 256 / D;  // rows per iteration of the workgroup
+    constexpr int CG = D / 8;        // 16-byte chunks per row
+    constexpr int RPI = 256 / CG;    // rows per iteration of the workgroup
+    __shared__ float part[4][D];
     const int g = blockIdx.y, b = blockIdx.z;
-    const int c = threadIdx.x % D, r0 = threadIdx.x / D;
-    const int t0 = blockIdx.x * 256;
-    float m = 0.f;
-    for (int t = t0 + r0; t < min(N, t0 + 256); t += RPI)
-        m = fmaxf(m, fabsf((float)v[(((size_t)b * N + t) * Hkv + g) * D + c]));
-    atomicMax(reinterpret_cast<unsigned int*>(scales) + ((size_t)b * Hkv + g) * D + c, __float_as_uint(m));
+    const int cg = threadIdx.x % CG, r0 = threadIdx.x / CG;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int t0 = blockIdx.x * 256, t1 = min(N, t0 + 256);
+    float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int t = t0 + r0; t < t1; t += RPI) {
+        float f[8];
+        unpack8<T>(*reinterpret_cast<const uint4*>(v + (((size_t)b * N + t) * Hkv + g) * D + 8 * cg), f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m[i] = fmaxf(m[i], fabsf(f[i]));
+    }
+#pragma unroll
+    for (int msk = CG; msk < 64; msk *= 2)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m[i] = fmaxf(m[i], __shfl_xor(m[i], msk));
+    if (lane < CG)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) part[wave][8 * lane + i] = m[i];
+    __syncthreads();
+    if (threadIdx.x < D) {
+        const int c = threadIdx.x;
+        const float mm = fmaxf(fmaxf(part[0][c], part[1][c]), fmaxf(part[2][c], part[3][c]));
+        atomicMax(reinterpret_cast<unsigned int*>(scales) + ((size_t)b * Hkv + g) * D + c, __float_as_uint(mm));
+    }
 }
 
-// One workgroup per (64-key chunk, kv head, sequence). Key n = 32 b + 8 i + 4 kg + j
-// of a chunk goes to byte 32 kg + 16 b + 4 i + j of each channel's 64-byte
-// chunk row; keys at or past N are zero.
+// One workgroup per (128-key tile, kv head, sequence). Key n = 32 b + 8 i + 4 kg + j
+// of a 64-key chunk goes to byte 32 kg + 16 b + 4 i + j of each channel's
+// 64-byte chunk row; keys at or past N are zero. The tile goes through LDS as
+// fp32 (rows padded to keep 16-byte alignment; column reads are conflict-free);
+// each thread then writes 16 codes of one channel with one 16-byte store.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void v_quant_kernel(const T* __restrict__ v, uint8_t* __restrict__ codes_t,
                                                       const float* __restrict__ amax, int N, int Hkv, int NP) {
-    __shared__ float tile[64][D + 1];
-    const int ch = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-    for (int e = threadIdx.x; e < 64 * D; e += 256) {
-        const int kk = e / D, c = e % D, t = ch * 64 + kk;
-        tile[kk][c] = t < N ? (float)v[(((size_t)b * N + t) * Hkv + g) * D + c] : 0.f;
+    constexpr int CG = D / 8, LD = D + 4;
+    __shared__ __attribute__((aligned(16))) float tile[128 * LD];
+    const int tt = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int k0 = tt * 128;
+#pragma unroll
+    for (int it = 0; it < 128 * CG / 256; ++it) {
+        const int ci = threadIdx.x + 256 * it, kk = ci / CG, cg = ci % CG, t = k0 + kk;
+        float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (t < N) unpack8<T>(*reinterpret_cast<const uint4*>(v + (((size_t)b * N + t) * Hkv + g) * D + 8 * cg), f);
+        *reinterpret_cast<float4*>(tile + kk * LD + 8 * cg) = make_float4(f[0], f[1], f[2], f[3]);
+        *reinterpret_cast<float4*>(tile + kk * LD + 8 * cg + 4) = make_float4(f[4], f[5], f[6], f[7]);
     }
     __syncthreads();
-    // 4-byte words of the output: (channel c, kg, b2, i) holds keys 32 b2 + 8 i + 4 kg + 0..3
-    for (int wi = threadIdx.x; wi < D * 16; wi += 256) {
-        const int c = wi / 16, p = wi % 16;  // p = 8 kg + 4 b2 + i
-        const int kg = p >> 3, b2 = (p >> 2) & 1, i = p & 3;
-        const int k0 = 32 * b2 + 8 * i + 4 * kg;
-        const int e = block_exp(amax[((size_t)b * Hkv + g) * D + c]);
-        const float inv = __builtin_ldexpf(1.f, -e);
-        uint32_t w = cvt2<false>(tile[k0][c] * inv, tile[k0 + 1][c] * inv, 0u);
-        w = cvt2<true>(tile[k0 + 2][c] * inv, tile[k0 + 3][c] * inv, w);
-        *reinterpret_cast<uint32_t*>(codes_t + (((size_t)b * Hkv + g) * D + c) * NP + ch * 64 + 4 * p) = w;
+    // group gi: channel gi / 8, 16-byte group gi % 8 of the channel's 128 bytes
+    // (64-key chunk ch2 = group / 4, bytes 16 q .. 16 q + 15 of it, q = group % 4:
+    // kg = q / 2, b = q % 2)
+#pragma unroll
+    for (int it = 0; it < D * 8 / 256; ++it) {
+        const int gi = threadIdx.x + 256 * it, c = gi / 8, grp = gi % 8;
+        const int ch2 = grp >> 2, kg = (grp >> 1) & 1, b2 = grp & 1;
+        const float inv = __builtin_ldexpf(1.f, -block_exp(amax[((size_t)b * Hkv + g) * D + c]));
+        float x[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int key = 64 * ch2 + 32 * b2 + 8 * (u >> 2) + 4 * kg + (u & 3);
+            x[u] = tile[key * LD + c] * inv;
+        }
+        *reinterpret_cast<uint4*>(codes_t + (((size_t)b * Hkv + g) * D + c) * NP + k0 + 16 * grp) = pack16(x);
     }
 }
 
@@ -282,7 +325,15 @@ __global__ __launch_bounds__(F8_NT, 1) void fwd_fp8_kernel(Fp8Args a) {
     kdma.init(wave, lane, (size_t)a.Hkv * DK);
     DmaTile<DV, D, F8_NT / 64> vdma;
     vdma.init(wave, lane, (size_t)a.NP / 2);
+    // K block scale of each stage's tile, read when the tile is issued (a read
+    // inside the compute step would wait on the next tile's loads as well)
+    const float* ksb = a.ks + ((size_t)b * a.Hkv + g) * a.nb;
+    float ksA = 0.f, ksB = 0.f;
     auto issue = [&](uint16_t* st, int kt) {
+        if (st == stA)
+            ksA = ksb[kt];
+        else
+            ksB = ksb[kt];
         kdma.issue(st, Kg, kt * F8_BC, len, wave);
         // V^T rows are channels: the tile is columns kt * F8_BC .. of every row
         vdma.issue(st + KT, Vg + kt * (F8_BC / 2), 0, D, wave);
@@ -291,16 +342,23 @@ __global__ __launch_bounds__(F8_NT, 1) void fwd_fp8_kernel(Fp8Args a) {
     f32x16 oacc[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
-    float m_ref = -INFINITY, l_run = 0.f, l_rnd = 0.f;
+    float m_ref = -INFINITY, l_run = 0.f;
     const float c2q = a.scale_log2 * sq;
-    const float* ksb = a.ks + ((size_t)b * a.Hkv + g) * a.nb;
+    // Row sums of the rounded P: A = 1 where (row < 8) == (lane group even),
+    // so output rows 0-7 sum the lanes c, c + 32 (query c) and rows 8-15 the
+    // lanes c + 16, c + 48 (query c + 16) of column c. Lane L then holds the sum
+    // of query L for L < 16 or L >= 48 and that of lane L ^ 48 for 16 <= L < 48.
+    const int onew = (((lane & 15) < 8) == (((lane >> 4) & 1) == 0)) ? 0x38383838 : 0;  // e4m3 1.0 = 0x38
+    const v8i ones = {onew, onew, onew, onew, onew, onew, onew, onew};
+    const int xlane = ((lane >> 4) == 1 || (lane >> 4) == 2) ? lane ^ 48 : lane;
+    f32x4 lacc = {};
 
     auto compute = [&](const uint16_t* S, int kt) {
         const int k0 = kt * F8_BC;
         if (!(wave_live && (!CAUSAL || k0 <= qw + 31))) return;
         const uint16_t* Ks = S;
         const uint16_t* Vs = S + KT;
-        const float c2 = c2q * ksb[kt];  // scale x log2(e) x Q block scale x K block scale
+        const float c2 = c2q * (S == stA ? ksA : ksB);  // scale x log2(e) x Q block scale x K block scale
 
         f32x16 s[F8_BC / 32];
         auto score_product = [&]() {
@@ -335,6 +393,9 @@ __global__ __launch_bounds__(F8_NT, 1) void fwd_fp8_kernel(Fp8Args a) {
                     ls += p;
                 }
             if (__any(!(ls <= 448.f))) {
+                // a fresh product from LDS: without the clobber the compiler keeps
+                // partial products of the first one live across the exponentials
+                asm volatile("" ::: "memory");
                 score_product();
                 need_max = true;
                 ls = 0.f;
@@ -359,7 +420,7 @@ __global__ __launch_bounds__(F8_NT, 1) void fwd_fp8_kernel(Fp8Args a) {
                 const float m_new = raise ? mt : m_ref;
                 const float alpha = raise ? exp2_fast(m_ref - mt) : 1.f;
                 l_run *= alpha;
-                l_rnd *= alpha;
+                lacc *= __shfl(alpha, xlane);
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
                 m_ref = m_new;
@@ -376,8 +437,7 @@ __global__ __launch_bounds__(F8_NT, 1) void fwd_fp8_kernel(Fp8Args a) {
         }
         l_run += ls;
 
-        // P^T as e4m3, chunk m of 64 keys: byte e = 16 b + r is element r of s[2m + b];
-        // the rounded values are summed back for the normalizer
+        // P^T as e4m3, chunk m of 64 keys: byte e = 16 b + r is element r of s[2m + b]
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             uint32_t w[8];
@@ -385,18 +445,13 @@ __global__ __launch_bounds__(F8_NT, 1) void fwd_fp8_kernel(Fp8Args a) {
             for (int q = 0; q < 8; ++q) {
                 const int bb = q >> 2, r0 = 4 * (q & 3);
                 const f32x16& sv = s[2 * m + bb];
-                w[q] = cvt2<true>(sv[r0 + 2], sv[r0 + 3], cvt2<false>(sv[r0], sv[r0 + 1], 0u));
+                // word q is written over element q of s[2m], an input already
+                // converted by then: the eight words land in eight consecutive
+                // registers, as the MFMA operand needs, without moves or zeroing
+                w[q] = cvt2<true>(sv[r0 + 2], sv[r0 + 3], cvt2<false>(sv[r0], sv[r0 + 1], __float_as_uint(s[2 * m][q])));
             }
-            float r0s = 0.f, r1s = 0.f;
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[q], false);
-                const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[q], true);
-                r0s += lo[0] + hi[0];
-                r1s += lo[1] + hi[1];
-            }
-            l_rnd += r0s + r1s;
             const v8i pf = {(int)w[0], (int)w[1], (int)w[2], (int)w[3], (int)w[4], (int)w[5], (int)w[6], (int)w[7]};
+            lacc = mma_f8_16(ones, pf, lacc);
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
                 const uint4 lo = ld_s16(Vs + 32 * db * DV + voff[m][0]);
@@ -411,7 +466,7 @@ __global__ __launch_bounds__(F8_NT, 1) void fwd_fp8_kernel(Fp8Args a) {
     two_stage_loop(stA, stB, nkt, issue, compute);
 
     const float l_tot = sum_xor32(l_run);
-    const float lr_tot = sum_xor32(l_rnd);
+    const float lr_tot = __shfl(lacc[0], xlane);
     if (qi < len) {
         const float inv = 1.f / lr_tot;
         const float* vsc = a.vs + ((size_t)b * a.Hkv + g) * D;
@@ -436,10 +491,10 @@ hipError_t quant_qk_d(const void* x, uint8_t* codes, float* scales, int B, int N
                       const unsigned long long* signs, hipStream_t s) {
     dim3 grid((N + QB - 1) / QB, H, B);
     if (signs)
-        hipLaunchKernelGGL((quant_qk_kernel<T, D, true>), grid, dim3(256), 0, s, reinterpret_cast<const T*>(x), codes,
+        hipLaunchKernelGGL((quant_qk_kernel<T, D, true>), grid, dim3(QB), 0, s, reinterpret_cast<const T*>(x), codes,
                            scales, N, H, signs[0], D > 64 ? signs[1] : 0ull);
     else
-        hipLaunchKernelGGL((quant_qk_kernel<T, D, false>), grid, dim3(256), 0, s, reinterpret_cast<const T*>(x),
+        hipLaunchKernelGGL((quant_qk_kernel<T, D, false>), grid, dim3(QB), 0, s, reinterpret_cast<const T*>(x),
                            codes, scales, N, H, 0ull, 0ull);
     return hipGetLastError();
 }
@@ -451,7 +506,7 @@ hipError_t quant_v_d(const void* v, uint8_t* codes_t, float* scales, int B, int 
     hipLaunchKernelGGL(clear_kernel, dim3((n + 255) / 256), dim3(256), 0, s, scales, n);
     hipLaunchKernelGGL((v_amax_kernel<T, D>), dim3((N + 255) / 256, Hkv, B), dim3(256), 0, s,
                        reinterpret_cast<const T*>(v), scales, N, Hkv);
-    hipLaunchKernelGGL((v_quant_kernel<T, D>), dim3(NP / 64, Hkv, B), dim3(256), 0, s,
+    hipLaunchKernelGGL((v_quant_kernel<T, D>), dim3(NP / 128, Hkv, B), dim3(256), 0, s,
                        reinterpret_cast<const T*>(v), codes_t, scales, N, Hkv, NP);
     hipLaunchKernelGGL(v_scale_kernel, dim3((n + 255) / 256), dim3(256), 0, s, scales, n);
     return hipGetLastError();
