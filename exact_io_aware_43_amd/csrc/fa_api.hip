@@ -28,7 +28,7 @@ int check_common(int B, int H, int Hkv, int N, int d, float scale, int causal, i
     if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
     if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
     if (!valid_dtype(dtype)) return FA_ERR_INVALID_ARG;
-    if (d != 32 && d != 64 && d != 128 && d != 256) return FA_ERR_UNSUPPORTED;
+    if (d != 16 && d != 32 && d != 64 && d != 128 && d != 256) return FA_ERR_UNSUPPORTED;
     // element offsets of one row-block are computed in 64 bits, but per-head row
     // counts, lse indices and grid sizes are 32-bit
     const long long rows = (long long)B * N;
@@ -55,6 +55,10 @@ fa::Args make_args(const void* q, const void* k, const void* v, int B, int H, in
     a.wl = a.wr = fa::kNoWindow;
     return a;
 }
+
+// Head dim of the 16-bit kernel instance that runs a head dim: 16 runs in the
+// 32 instances with Args::dl = 16 (zero-padded tiles and fragments).
+int kernel_d(int d) { return d == 16 ? 32 : d; }
 
 // Sliding window and softcapping as the kernels take them (see fa::Args).
 struct Masking {
@@ -133,6 +137,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
     fa::Args a = make_args(q, k, v, B, H, Hkv, N, scale, alibi_slopes, cu_seqlens);
     a.out = o;
     a.lse = lse;
+    a.dl = d;
     set_dropout(a, dr);
     set_masking(a, mk, scale);
     const bool cap = mk.softcap > 0.f;
@@ -141,7 +146,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
     if (dtype == FA_FP32)
         e = fa::launch_fwd_f32(a, d, causal != 0, alibi_slopes != nullptr, cap, s);
     else
-        e = fa::launch_fwd_mfma(a, (int)dtype, d, causal != 0, alibi_slopes != nullptr,
+        e = fa::launch_fwd_mfma(a, (int)dtype, kernel_d(d), causal != 0, alibi_slopes != nullptr,
                                 dr.on ? fa::kDropout : (cap ? fa::kSoftcap : fa::kPlain), s);
     return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
@@ -240,10 +245,11 @@ int bwd_launch(const void* q, const void* k, const void* v, const void* o, const
     a.dv = dv;
     a.dsum = reinterpret_cast<float*>(workspace);
     a.lse2 = a.dsum + workspace_rows(B, H, N);
+    a.dl = d;
     set_dropout(a, dr);
     set_masking(a, mk, scale);
     const int var = dr.on ? fa::kDropout : (mk.softcap > 0.f ? fa::kSoftcap : fa::kPlain);
-    hipError_t e = fa::launch_bwd(a, (int)dtype, d, causal != 0, alibi_slopes != nullptr, var, stages,
+    hipError_t e = fa::launch_bwd(a, (int)dtype, kernel_d(d), causal != 0, alibi_slopes != nullptr, var, stages,
                                   reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
@@ -454,7 +460,7 @@ const char* fa_strerror(int status) {
         case FA_OK: return "success";
         case FA_ERR_INVALID_ARG: return "invalid argument";
         case FA_ERR_UNSUPPORTED:
-            return "unsupported configuration (head dim must be 32, 64, 128 or 256, and 64 or 128 for decode "
+            return "unsupported configuration (head dim must be 16, 32, 64, 128 or 256, and 64 or 128 for decode "
                    "and fp8; fp32 is forward only and without dropout; dropout and softcapping do not combine; "
                    "fp8 takes and returns fp16 or bf16)";
         case FA_ERR_WORKSPACE: return "workspace missing, misaligned or smaller than fa_bwd_workspace_size()";

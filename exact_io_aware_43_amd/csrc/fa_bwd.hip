@@ -62,9 +62,10 @@ __global__ __launch_bounds__(NT) void bwd_dsum_kernel(Args a) {
     const int i = blockIdx.z * RPB + threadIdx.x / LPR;
     const int part = threadIdx.x % LPR;
     if (i >= a.N64) return;
+    const int DL = D == 32 ? a.dl : D;  // head dim in memory
     float acc = 0.f;
-    if (i < len) {
-        const size_t off = ((size_t)(row0 + i) * a.H + h) * D + part * 8;
+    if (i < len && part * 8 < DL) {
+        const size_t off = ((size_t)(row0 + i) * a.H + h) * DL + part * 8;
         const uint4 uo = ld_g16(reinterpret_cast<const T*>(a.o) + off);
         const uint4 ud = ld_g16(reinterpret_cast<const T*>(a.dout) + off);
         const V8<T> vo = as_v8<T>(uo), vd = as_v8<T>(ud);
@@ -110,19 +111,20 @@ __global__ __launch_bounds__((64 * dq_waves<D, CAUSAL, ALIBI, DROP, CAP>()), 1) 
     if (q0 >= len) return;
 
     const int g = h / a.G;
-    const size_t ldq = (size_t)a.H * D, ldk = (size_t)a.Hkv * D;
+    const int DL = D == 32 ? a.dl : D;  // head dim in memory (16 runs here, zero-padded)
+    const size_t ldq = (size_t)a.H * DL, ldk = (size_t)a.Hkv * DL;
     const int qw = q0 + wave * 32;
     const int qi = qw + col;
     const bool wave_live = qw < len;
 
     V8<T> qf[D / 16], df[D / 16];
     {
-        const T* Qp = reinterpret_cast<const T*>(a.q) + (size_t)(row0 + qi) * ldq + (size_t)h * D;
-        const T* Dp = reinterpret_cast<const T*>(a.dout) + (size_t)(row0 + qi) * ldq + (size_t)h * D;
+        const T* Qp = reinterpret_cast<const T*>(a.q) + (size_t)(row0 + qi) * ldq + (size_t)h * DL;
+        const T* Dp = reinterpret_cast<const T*>(a.dout) + (size_t)(row0 + qi) * ldq + (size_t)h * DL;
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
             uint4 uq = make_uint4(0, 0, 0, 0), ud = uq;
-            if (qi < len) {
+            if (qi < len && 16 * kk + 8 * kg < DL) {
                 uq = ld_g16(Qp + 16 * kk + 8 * kg);
                 ud = ld_g16(Dp + 16 * kk + 8 * kg);
             }
@@ -157,11 +159,11 @@ __global__ __launch_bounds__((64 * dq_waves<D, CAUSAL, ALIBI, DROP, CAP>()), 1) 
     const int kt_lo = max(q0 - wl, 0) / DQ_BK;
     const int kend = min(len, q0 + DQ_BQ + wr);
     const int nkt = (kend + DQ_BK - 1) / DQ_BK - kt_lo;
-    const T* Kg = reinterpret_cast<const T*>(a.k) + (size_t)row0 * ldk + (size_t)g * D;
-    const T* Vg = reinterpret_cast<const T*>(a.v) + (size_t)row0 * ldk + (size_t)g * D;
+    const T* Kg = reinterpret_cast<const T*>(a.k) + (size_t)row0 * ldk + (size_t)g * DL;
+    const T* Vg = reinterpret_cast<const T*>(a.v) + (size_t)row0 * ldk + (size_t)g * DL;
 
     DmaTile<D, DQ_BK, DQ_NT / 64> dma;
-    dma.init(wave, lane, ldk);
+    dma.init(wave, lane, ldk, DL);
     auto issue = [&](uint16_t* S, int it) {
         dma.issue(S, reinterpret_cast<const uint16_t*>(Kg), (kt_lo + it) * DQ_BK, len, wave);
         dma.issue(S + TILE, reinterpret_cast<const uint16_t*>(Vg), (kt_lo + it) * DQ_BK, len, wave);
@@ -269,13 +271,14 @@ __global__ __launch_bounds__((64 * dq_waves<D, CAUSAL, ALIBI, DROP, CAP>()), 1) 
     two_stage_loop(stA, stB, nkt, issue, compute);
 
     if (qi < len) {
-        T* dQ = reinterpret_cast<T*>(a.dq) + (size_t)(row0 + qi) * ldq + (size_t)h * D;
+        T* dQ = reinterpret_cast<T*>(a.dq) + (size_t)(row0 + qi) * ldq + (size_t)h * DL;
         const float sc = a.scale;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int d0 = 32 * db + 8 * i + 4 * kg;
+                if (d0 >= DL) continue;
                 const int r = 4 * i;
                 *reinterpret_cast<uint2*>(dQ + d0) = pack4<T>(dqacc[db][r] * sc, dqacc[db][r + 1] * sc,
                                                               dqacc[db][r + 2] * sc, dqacc[db][r + 3] * sc);

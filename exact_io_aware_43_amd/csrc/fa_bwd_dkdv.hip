@@ -72,18 +72,19 @@ __global__ __launch_bounds__(DkdvShape<D>::NT, 1) void bwd_dkdv_kernel(Args a) {
     const int k0 = kt * KV_BK;
     if (k0 >= len) return;
 
-    const size_t ldq = (size_t)a.H * D, ldk = (size_t)a.Hkv * D;
+    const int DL = D == 32 ? a.dl : D;  // head dim in memory (16 runs here, zero-padded)
+    const size_t ldq = (size_t)a.H * DL, ldk = (size_t)a.Hkv * DL;
     const int kw = k0 + wave * 32;     // first key of this wave
     const int key = kw + (lane & 31);  // this lane's key (column of S)
 
     // K^T fragments as B operands: lane holds key `key`, dims 16*kk + 8*kg + 0..7.
     V8<T> kf[D / 16];
     {
-        const T* Kp = reinterpret_cast<const T*>(a.k) + (size_t)(row0 + key) * ldk + (size_t)g * D;
+        const T* Kp = reinterpret_cast<const T*>(a.k) + (size_t)(row0 + key) * ldk + (size_t)g * DL;
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
             uint4 uk = make_uint4(0, 0, 0, 0);
-            if (key < len) uk = ld_g16(Kp + 16 * kk + 8 * kg);
+            if (key < len && 16 * kk + 8 * kg < DL) uk = ld_g16(Kp + 16 * kk + 8 * kg);
             kf[kk] = as_v8<T>(uk);
         }
     }
@@ -93,8 +94,8 @@ __global__ __launch_bounds__(DkdvShape<D>::NT, 1) void bwd_dkdv_kernel(Args a) {
     // below covers these loads.
     {
         DmaTile<D, KV_BK / 2, NW> vdma;
-        vdma.init(wave, lane, ldk);
-        const uint16_t* Vg = reinterpret_cast<const uint16_t*>(a.v) + (size_t)row0 * ldk + (size_t)g * D;
+        vdma.init(wave, lane, ldk, DL);
+        const uint16_t* Vg = reinterpret_cast<const uint16_t*>(a.v) + (size_t)row0 * ldk + (size_t)g * DL;
         vdma.issue(vt, Vg, k0, len, wave);
         vdma.issue(vt + (KV_BK / 2) * D, Vg, k0 + KV_BK / 2, len, wave);
     }
@@ -128,12 +129,12 @@ __global__ __launch_bounds__(DkdvShape<D>::NT, 1) void bwd_dkdv_kernel(Args a) {
     };
 
     DmaTile<D, KV_BQ, NW> dma;
-    dma.init(wave, lane, ldq);
+    dma.init(wave, lane, ldq, DL);
     auto issue = [&](uint16_t* S, int st) {
         int h, q0;
         step_coords(st, h, q0);
-        dma.issue(S, reinterpret_cast<const uint16_t*>(Qb + (size_t)h * D), q0, len, wave);
-        dma.issue(S + TILE, reinterpret_cast<const uint16_t*>(Db + (size_t)h * D), q0, len, wave);
+        dma.issue(S, reinterpret_cast<const uint16_t*>(Qb + (size_t)h * DL), q0, len, wave);
+        dma.issue(S + TILE, reinterpret_cast<const uint16_t*>(Db + (size_t)h * DL), q0, len, wave);
         // the pre-pass filled positions [len, N64) with +inf / 0, so the KV_BQ
         // values from q0 are in bounds and padding rows get P = 0
         const size_t vbase = ((size_t)b * a.H + h) * a.N64 + q0;
@@ -298,8 +299,8 @@ __global__ __launch_bounds__(DkdvShape<D>::NT, 1) void bwd_dkdv_kernel(Args a) {
 
     // epilogue: lane owns key `key`; accumulator rows are dims 32*db + 8*i + 4*kg + 0..3
     if (key < len) {
-        T* dK = reinterpret_cast<T*>(a.dk) + (size_t)(row0 + key) * ldk + (size_t)g * D;
-        T* dV = reinterpret_cast<T*>(a.dv) + (size_t)(row0 + key) * ldk + (size_t)g * D;
+        T* dK = reinterpret_cast<T*>(a.dk) + (size_t)(row0 + key) * ldk + (size_t)g * DL;
+        T* dV = reinterpret_cast<T*>(a.dv) + (size_t)(row0 + key) * ldk + (size_t)g * DL;
         const float sc = a.scale;
         const float vs = DROP ? a.drop_scale : 1.f;
 #pragma unroll
@@ -308,6 +309,7 @@ __global__ __launch_bounds__(DkdvShape<D>::NT, 1) void bwd_dkdv_kernel(Args a) {
             for (int i = 0; i < 4; ++i) {
                 const int d0 = 32 * db + 8 * i + 4 * kg;
                 const int r = 4 * i;
+                if (d0 >= DL) continue;
                 *reinterpret_cast<uint2*>(dK + d0) = pack4<T>(dkacc[db][r] * sc, dkacc[db][r + 1] * sc,
                                                               dkacc[db][r + 2] * sc, dkacc[db][r + 3] * sc);
                 *reinterpret_cast<uint2*>(dV + d0) = pack4<T>(dvacc[db][r] * vs, dvacc[db][r + 1] * vs,

@@ -267,14 +267,18 @@ struct DmaTile {
     uint32_t boff[PER_WAVE];
     uint32_t ld2;             // row stride in bytes
 
-    __device__ __forceinline__ void init(int wave, int lane, size_t ld) {
+    // `dl`: elements per row in memory (D, or fewer for a tile whose upper
+    // columns are padding): chunks at or past it take an offset beyond any
+    // buffer range, so the range check stores zeros there and nothing is read.
+    __device__ __forceinline__ void init(int wave, int lane, size_t ld, int dl = D) {
         ld2 = (uint32_t)(ld * 2);
 #pragma unroll
         for (int i = 0; i < PER_WAVE; ++i) {
             const int p = (wave * PER_WAVE + i) * 64 + lane;  // chunk index in LDS order
             const int row = p / (D / 8), pos = p % (D / 8);
             const int f = ((row & 3) * (D / 32)) ^ ((row >> 2) & 3);
-            boff[i] = (uint32_t)row * ld2 + 16u * (uint32_t)(pos ^ f) - 1024u * (uint32_t)(i % 4);
+            const int gc = pos ^ f;  // chunk of the row in memory
+            boff[i] = 8 * gc < dl ? (uint32_t)row * ld2 + 16u * (uint32_t)gc - 1024u * (uint32_t)(i % 4) : 0x80000000u;
         }
     }
 

@@ -105,11 +105,12 @@ __global__ __launch_bounds__(FwdShape<D>::NT, 1) void fwd_mfma_kernel(Args a) {
     if (q0 >= len) return;
 
     const int g = h / a.G;
-    const size_t ldq = (size_t)a.H * D;
-    const size_t ldk = (size_t)a.Hkv * D;
-    const T* Q = reinterpret_cast<const T*>(a.q) + (size_t)row0 * ldq + (size_t)h * D;
-    const T* Kg = reinterpret_cast<const T*>(a.k) + (size_t)row0 * ldk + (size_t)g * D;
-    const T* Vg = reinterpret_cast<const T*>(a.v) + (size_t)row0 * ldk + (size_t)g * D;
+    const int DL = D == 32 ? a.dl : D;  // head dim in memory (16 runs here, zero-padded)
+    const size_t ldq = (size_t)a.H * DL;
+    const size_t ldk = (size_t)a.Hkv * DL;
+    const T* Q = reinterpret_cast<const T*>(a.q) + (size_t)row0 * ldq + (size_t)h * DL;
+    const T* Kg = reinterpret_cast<const T*>(a.k) + (size_t)row0 * ldk + (size_t)g * DL;
+    const T* Vg = reinterpret_cast<const T*>(a.v) + (size_t)row0 * ldk + (size_t)g * DL;
 
     const int qw = q0 + wave * 32;  // first query of this wave
     const int qi = qw + col;        // this lane's query
@@ -120,7 +121,7 @@ __global__ __launch_bounds__(FwdShape<D>::NT, 1) void fwd_mfma_kernel(Args a) {
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
         uint4 u = make_uint4(0, 0, 0, 0);
-        if (qi < len) u = ld_g16(Q + (size_t)qi * ldq + 16 * kk + 8 * kg);
+        if (qi < len && 16 * kk + 8 * kg < DL) u = ld_g16(Q + (size_t)qi * ldq + 16 * kk + 8 * kg);
         qf[kk] = as_v8<T>(u);
     }
 
@@ -142,7 +143,7 @@ __global__ __launch_bounds__(FwdShape<D>::NT, 1) void fwd_mfma_kernel(Args a) {
     const int nkt = (kend + BC - 1) / BC - kt_lo;
 
     DmaTile<D, BC, NT / 64> dma;
-    dma.init(wave, lane, ldk);
+    dma.init(wave, lane, ldk, DL);
     // With ALiBi, key tiles are visited from the last (the diagonal one under
     // the causal mask) down to the first: the bias falls with distance, so the
     // tile of a row's nearest keys holds its largest scores, and the maximum
@@ -401,12 +402,13 @@ __global__ __launch_bounds__(FwdShape<D>::NT, 1) void fwd_mfma_kernel(Args a) {
     const float lr_tot = sum_xor32(l_rnd);
     if (qi < len) {
         const float inv = (DROP ? a.drop_scale : 1.f) / lr_tot;
-        T* O = reinterpret_cast<T*>(a.out) + (size_t)row0 * ldq + (size_t)h * D + (size_t)qi * ldq;
+        T* O = reinterpret_cast<T*>(a.out) + (size_t)row0 * ldq + (size_t)h * DL + (size_t)qi * ldq;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int d0 = 32 * db + 8 * i + 4 * kg;
+                if (d0 >= DL) continue;
                 *reinterpret_cast<uint2*>(O + d0) =
                     pack4<T>(oacc[db][4 * i] * inv, oacc[db][4 * i + 1] * inv, oacc[db][4 * i + 2] * inv,
                              oacc[db][4 * i + 3] * inv);

@@ -136,6 +136,7 @@ hipError_t launch_d(const Args& a, bool causal, bool alibi, hipStream_t s) {
 template <bool CAP>
 hipError_t launch_c(const Args& a, int d, bool causal, bool alibi, hipStream_t s) {
     switch (d) {
+        case 16: return launch_d<16, CAP>(a, causal, alibi, s);
         case 32: return launch_d<32, CAP>(a, causal, alibi, s);
         case 64: return launch_d<64, CAP>(a, causal, alibi, s);
         case 128: return launch_d<128, CAP>(a, causal, alibi, s);

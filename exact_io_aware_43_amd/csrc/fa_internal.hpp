@@ -44,6 +44,11 @@ struct Args {
     // cap tanh(u / cap); the kernels take tanh(s * cap_in) with s the raw dot
     // product (cap_in = scale / cap) and scale it by cap_out = cap * log2(e)
     float cap_in, cap_out;
+    // head dim as stored in memory: equal to the kernel's tile head dim, except
+    // for head dim 16, which runs in the head-dim-32 instances with the upper
+    // 16 columns of every staged tile and register fragment zero (row pitches,
+    // loads and stores use this value)
+    int dl;
 };
 
 // An unbounded window side: larger than any position difference, small enough

@@ -79,7 +79,9 @@ typedef enum fa_status {
  *
  *   B, H, Hkv, N, d : batch (number of sequences), query heads, kv heads
  *                     (H % Hkv == 0), sequence length (maximum length when
- *                     packed), head dimension (32, 64, 128 or 256).
+ *                     packed), head dimension (16, 32, 64, 128 or 256; the
+                     usage contract's list, "paper lists 16/32/64/128", up to
+                     256).
  *   scale           : multiplies Q K^T before the softmax (1/sqrt(d) is usual).
  *   causal          : 0 or 1; 1 keeps key j <= query i.
  */

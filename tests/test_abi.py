@@ -67,7 +67,7 @@ def _fwd(**kw):
     (dict(lse=None), INVALID), (dict(B=0), INVALID), (dict(H=0), INVALID), (dict(Hkv=0), INVALID),
     (dict(N=0), INVALID), (dict(N=-5), INVALID), (dict(H=6, Hkv=4), INVALID), (dict(causal=2), INVALID),
     (dict(scale=math.nan), INVALID), (dict(scale=math.inf), INVALID), (dict(dtype=3), INVALID),
-    (dict(d=96), UNSUPPORTED), (dict(d=16), UNSUPPORTED), (dict(d=512), UNSUPPORTED), (dict(d=0), INVALID),
+    (dict(d=96), UNSUPPORTED), (dict(d=8), UNSUPPORTED), (dict(d=48), UNSUPPORTED), (dict(d=512), UNSUPPORTED), (dict(d=0), INVALID),
     (dict(q=PTR[0] + 8), INVALID), (dict(o=PTR[3] + 2), INVALID), (dict(lse=PTR[4] + 4), INVALID),
     (dict(alibi=PTR[5] + 4), INVALID), (dict(cu=PTR[6] + 4), INVALID),
     (dict(B=1 << 16, N=1 << 16, H=2, Hkv=2), INVALID),
