@@ -95,7 +95,7 @@ __device__ __forceinline__ uint4 pack16(const float* x) {
 }
 
 // ---------------------------------------------------------------- Q, K
-// One workgroup of 2 waves per (128-token block, head, sequence); each lane owns
+// One workgroup of 2 waves per (head, 128-token block, sequence); each lane owns
 // one row: D / 8 loads of 16 bytes, the sign flips and all log2(D) butterfly
 // stages in registers (no cross-lane traffic), then the block maximum over
 // both waves, the scale and D / 16 stores of 16 codes.
@@ -105,7 +105,10 @@ __global__ __launch_bounds__(128) void quant_qk_kernel(const T* __restrict__ x, 
                                                        unsigned long long s0, unsigned long long s1) {
     __shared__ float wmax[2];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    // grid x = head: workgroups dispatched together read the neighbouring head
+    // slices of the same token rows (contiguous memory) rather than rows H d
+    // elements apart
+    const int h = blockIdx.x, blk = blockIdx.y, b = blockIdx.z;
     const int nb = (N + QB - 1) / QB;
     const int t = blk * QB + threadIdx.x;
     const size_t row = ((size_t)b * N + t) * H + h;  // row index of [B, N, H]
@@ -165,7 +168,7 @@ __global__ void clear_kernel(float* p, int n) {
     if (i < n) p[i] = 0.f;
 }
 
-// One workgroup per (256 rows, kv head, sequence): a thread reads 8 channels of
+// One workgroup per (kv head, 256 rows, sequence): a thread reads 8 channels of
 // every (256 / (D / 8))-th row with 16-byte loads; lanes of equal channels
 // reduce by shuffles, the four waves through LDS, then one atomic per channel.
 template <typename T, int D>
@@ -174,10 +177,10 @@ __global__ __launch_bounds__(256) void v_amax_kernel(const T* __restrict__ v, fl
     constexpr int CG = D / 8;        // 16-byte chunks per row
     constexpr int RPI = 256 / CG;    // rows per iteration of the workgroup
     __shared__ float part[4][D];
-    const int g = blockIdx.y, b = blockIdx.z;
+    const int g = blockIdx.x, b = blockIdx.z;  // grid x = kv head (as the Q/K quantizer)
     const int cg = threadIdx.x % CG, r0 = threadIdx.x / CG;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int t0 = blockIdx.x * 256, t1 = min(N, t0 + 256);
+    const int t0 = blockIdx.y * 256, t1 = min(N, t0 + 256);
     float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int t = t0 + r0; t < t1; t += RPI) {
         float f[8];
@@ -200,7 +203,7 @@ __global__ __launch_bounds__(256) void v_amax_kernel(const T* __restrict__ v, fl
     }
 }
 
-// One workgroup per (128-key tile, kv head, sequence). Key n = 32 b + 8 i + 4 kg + j
+// One workgroup per (kv head, 128-key tile, sequence). Key n = 32 b + 8 i + 4 kg + j
 // of a 64-key chunk goes to byte 32 kg + 16 b + 4 i + j of each channel's
 // 64-byte chunk row; keys at or past N are zero. The tile goes through LDS as
 // fp32 (rows padded to keep 16-byte alignment; column reads are conflict-free);
@@ -210,7 +213,7 @@ __global__ __launch_bounds__(256) void v_quant_kernel(const T* __restrict__ v, u
                                                       const float* __restrict__ amax, int N, int Hkv, int NP) {
     constexpr int CG = D / 8, LD = D + 4;
     __shared__ __attribute__((aligned(16))) float tile[128 * LD];
-    const int tt = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int g = blockIdx.x, tt = blockIdx.y, b = blockIdx.z;  // grid x = kv head
     const int k0 = tt * 128;
 #pragma unroll
     for (int it = 0; it < 128 * CG / 256; ++it) {
@@ -489,7 +492,7 @@ __global__ __launch_bounds__(F8_NT, 1) void fwd_fp8_kernel(Fp8Args a) {
 template <typename T, int D>
 hipError_t quant_qk_d(const void* x, uint8_t* codes, float* scales, int B, int N, int H,
                       const unsigned long long* signs, hipStream_t s) {
-    dim3 grid((N + QB - 1) / QB, H, B);
+    dim3 grid(H, (N + QB - 1) / QB, B);
     if (signs)
         hipLaunchKernelGGL((quant_qk_kernel<T, D, true>), grid, dim3(QB), 0, s, reinterpret_cast<const T*>(x), codes,
                            scales, N, H, signs[0], D > 64 ? signs[1] : 0ull);
@@ -504,9 +507,9 @@ hipError_t quant_v_d(const void* v, uint8_t* codes_t, float* scales, int B, int 
     const int n = B * Hkv * D;
     const int NP = fp8_keys_padded(N);
     hipLaunchKernelGGL(clear_kernel, dim3((n + 255) / 256), dim3(256), 0, s, scales, n);
-    hipLaunchKernelGGL((v_amax_kernel<T, D>), dim3((N + 255) / 256, Hkv, B), dim3(256), 0, s,
+    hipLaunchKernelGGL((v_amax_kernel<T, D>), dim3(Hkv, (N + 255) / 256, B), dim3(256), 0, s,
                        reinterpret_cast<const T*>(v), scales, N, Hkv);
-    hipLaunchKernelGGL((v_quant_kernel<T, D>), dim3(NP / 128, Hkv, B), dim3(256), 0, s,
+    hipLaunchKernelGGL((v_quant_kernel<T, D>), dim3(Hkv, NP / 128, B), dim3(256), 0, s,
                        reinterpret_cast<const T*>(v), codes_t, scales, N, Hkv, NP);
     hipLaunchKernelGGL(v_scale_kernel, dim3((n + 255) / 256), dim3(256), 0, s, scales, n);
     return hipGetLastError();
