@@ -437,6 +437,12 @@ def attention_fp8_quantized(qc, qs, kc, ks, vc, vs, causal: bool = False, softma
                             rotated: bool = False, out_dtype=torch.bfloat16):
     """fa_fwd_fp8 on codes and scales from quantize_fp8_qk / quantize_fp8_v;
     returns (o [B, N, H, d] out_dtype, lse float32 [B, H, N])."""
+    for name, t in (("q codes", qc), ("q scales", qs), ("k codes", kc), ("k scales", ks), ("v codes", vc),
+                    ("v scales", vs)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+    if qc.dim() != 4 or kc.dim() != 4:
+        raise ValueError("q and k codes must be 4-d [B, N, heads, d]")
     B, N, H, d = qc.shape
     Hkv = kc.shape[2]
     dev = qc.device

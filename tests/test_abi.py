@@ -383,3 +383,22 @@ def test_hadamard_sign_words():
         fa.hadamard_sign_words([1.0] * 127 + [0.5], 128)
     with pytest.raises(ValueError):
         fa.hadamard_sign_words([1.0] * 64, 128)
+
+
+def test_fp8_binding_validation():
+    """The FP8 helpers refuse host tensors, 32-bit inputs and mismatched shapes
+    before any call into the library."""
+    import torch
+
+    x = torch.zeros(1, 8, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device"):
+        fa.quantize_fp8_qk(x)
+    with pytest.raises(ValueError, match="device"):
+        fa.quantize_fp8_v(x)
+    codes = torch.zeros(1, 8, 2, 64, dtype=torch.uint8)
+    sc = torch.zeros(1, 2, 1)
+    with pytest.raises(ValueError, match="device"):
+        fa.attention_fp8_quantized(codes, sc, codes, sc, torch.zeros(1, 2, 64, 128, dtype=torch.uint8),
+                                   torch.zeros(1, 2, 64))
+    with pytest.raises(ValueError):
+        fa.hadamard_sign_words([1.0, -1.0] * 32, 128)
