@@ -21,6 +21,9 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool valid_dtype(int dt) { return dt == FA_FP32 || dt == FA_FP16 || dt == FA_BF16; }
 
+// Largest grid y / z extent of a launch.
+constexpr long long kMaxTiles = 65535;
+
 // Checks shared by forward and backward. Returns FA_OK or the status to report.
 int check_common(int B, int H, int Hkv, int N, int d, float scale, int causal, int dtype) {
     if (B <= 0 || H <= 0 || Hkv <= 0 || N <= 0 || d <= 0) return FA_ERR_INVALID_ARG;
@@ -33,6 +36,9 @@ int check_common(int B, int H, int Hkv, int N, int d, float scale, int causal, i
     // counts, lse indices and grid sizes are 32-bit
     const long long rows = (long long)B * N;
     if (rows * H >= (1ll << 31) || rows * Hkv >= (1ll << 31)) return FA_ERR_INVALID_ARG;
+    // query and key tiles run along grid z (at most 65535 blocks): 128 rows per
+    // block in the smallest 16-bit tile, 64 in the fp32 forward
+    if (N > kMaxTiles * (dtype == FA_FP32 ? 64 : 128) || B > kMaxTiles) return FA_ERR_INVALID_ARG;
     return FA_OK;
 }
 
@@ -272,7 +278,7 @@ int decode_splits(int B, int H, int Hkv, int Nq, int Nk, int num_splits) {
         S = (int)((kComputeUnits + base - 1) / base);
         S = std::min(S, std::max(1, Nk / 512));
     }
-    return std::max(1, std::min(S, tiles));
+    return std::max(1, std::min({S, tiles, (int)kMaxTiles}));
 }
 
 size_t decode_workspace_bytes(int B, int H, int Nq, int d, int splits) {
@@ -288,6 +294,7 @@ int check_decode(int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int 
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
     if (dtype == FA_FP32) return FA_ERR_UNSUPPORTED;
     if ((long long)B * Nk * Hkv >= (1ll << 31) || (long long)B * Nq * H >= (1ll << 31)) return FA_ERR_INVALID_ARG;
+    if (B > kMaxTiles) return FA_ERR_INVALID_ARG;
     return FA_OK;
 }
 
@@ -417,7 +424,7 @@ int fa_quantize_fp8_qk(const void* x, unsigned char* codes, float* scales, int B
     if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return FA_ERR_INVALID_ARG;
     if (dtype != FA_FP16 && dtype != FA_BF16) return valid_dtype(dtype) ? FA_ERR_UNSUPPORTED : FA_ERR_INVALID_ARG;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-    if ((long long)B * N * H >= (1ll << 31)) return FA_ERR_INVALID_ARG;
+    if ((long long)B * N * H >= (1ll << 31) || N > kMaxTiles * 128 || B > kMaxTiles) return FA_ERR_INVALID_ARG;
     hipError_t e = fa::launch_quant_qk(x, codes, scales, B, N, H, d, hadamard_signs, (int)dtype,
                                        reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
@@ -429,7 +436,7 @@ int fa_quantize_fp8_v(const void* v, unsigned char* codes_t, float* scales, int 
     if (!aligned16(v) || !aligned16(codes_t) || !aligned16(scales)) return FA_ERR_INVALID_ARG;
     if (dtype != FA_FP16 && dtype != FA_BF16) return valid_dtype(dtype) ? FA_ERR_UNSUPPORTED : FA_ERR_INVALID_ARG;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-    if ((long long)B * N * Hkv >= (1ll << 31) || N > (1 << 30)) return FA_ERR_INVALID_ARG;
+    if ((long long)B * N * Hkv >= (1ll << 31) || N > kMaxTiles * 128 || B > kMaxTiles) return FA_ERR_INVALID_ARG;
     hipError_t e = fa::launch_quant_v(v, codes_t, scales, B, N, Hkv, d, (int)dtype,
                                       reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
@@ -447,7 +454,7 @@ int fa_fwd_fp8(const unsigned char* q, const unsigned char* k, const unsigned ch
     if (out_dtype != FA_FP16 && out_dtype != FA_BF16)
         return valid_dtype(out_dtype) ? FA_ERR_UNSUPPORTED : FA_ERR_INVALID_ARG;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-    if ((long long)B * N * H >= (1ll << 31) || N > (1 << 30)) return FA_ERR_INVALID_ARG;
+    if ((long long)B * N * H >= (1ll << 31) || N > kMaxTiles * 128 || B > kMaxTiles) return FA_ERR_INVALID_ARG;
     const float s_eff = rotated ? scale / (float)d : scale;  // exact: d is a power of two
     hipError_t e = fa::launch_fwd_fp8(q, k, v_t, q_scales, k_scales, v_scales, o, lse, B, H, Hkv, N, d,
                                       s_eff * 1.4426950408889634f, causal != 0, (int)out_dtype,

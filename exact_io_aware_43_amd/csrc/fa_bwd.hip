@@ -56,10 +56,12 @@ template <typename T, int D>
 __global__ __launch_bounds__(NT) void bwd_dsum_kernel(Args a) {
     constexpr int LPR = D / 8;        // lanes per (row, head)
     constexpr int RPB = NT / LPR;     // rows per block
-    const int h = blockIdx.x, b = blockIdx.y;
+    // grid x = row block (up to N64 / RPB, beyond the 65535 limit of y and z),
+    // y = head, z = sequence
+    const int h = blockIdx.y, b = blockIdx.z;
     int row0, len;
     seq_bounds(a, b, row0, len);
-    const int i = blockIdx.z * RPB + threadIdx.x / LPR;
+    const int i = blockIdx.x * RPB + threadIdx.x / LPR;
     const int part = threadIdx.x % LPR;
     if (i >= a.N64) return;
     const int DL = D == 32 ? a.dl : D;  // head dim in memory
@@ -291,7 +293,7 @@ template <typename T, int D, bool CAUSAL, bool ALIBI, bool DROP, bool CAP>
 hipError_t launch(const Args& a, unsigned stages, hipStream_t s) {
     if (stages & 1u) {
         constexpr int RPB = NT / (D / 8);
-        dim3 grid(a.H, a.B, (a.N64 + RPB - 1) / RPB);
+        dim3 grid((a.N64 + RPB - 1) / RPB, a.H, a.B);
         hipLaunchKernelGGL((bwd_dsum_kernel<T, D>), grid, dim3(NT), 0, s, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

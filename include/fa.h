@@ -64,7 +64,9 @@ typedef enum fa_dtype {
 
 typedef enum fa_status {
     FA_OK = 0,
-    FA_ERR_INVALID_ARG = -1, /* null pointer, bad size, H % Hkv != 0, non-finite scale, misalignment */
+    FA_ERR_INVALID_ARG = -1, /* null pointer, bad size, H % Hkv != 0, non-finite scale, misalignment;
+                                sizes: B * N * H < 2^31, B <= 65535, N <= 8388480 (65535 tiles of 128
+                                rows; 4194240 for FA_FP32) */
     FA_ERR_UNSUPPORTED = -2, /* head dim or type combination not built (see fa_strerror) */
     FA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than fa_bwd_workspace_size() */
     FA_ERR_LAUNCH = -4,      /* the kernel launch itself failed */

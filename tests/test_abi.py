@@ -71,6 +71,9 @@ def _fwd(**kw):
     (dict(q=PTR[0] + 8), INVALID), (dict(o=PTR[3] + 2), INVALID), (dict(lse=PTR[4] + 4), INVALID),
     (dict(alibi=PTR[5] + 4), INVALID), (dict(cu=PTR[6] + 4), INVALID),
     (dict(B=1 << 16, N=1 << 16, H=2, Hkv=2), INVALID),
+    # grid limits: at most 65535 tiles of 128 rows (64 for fp32) and 65535 sequences
+    (dict(B=1, N=65535 * 128 + 1, H=1, Hkv=1), INVALID), (dict(B=65536, N=1, H=1, Hkv=1), INVALID),
+    (dict(B=1, N=65535 * 64 + 1, H=1, Hkv=1, dtype=fa.FA_FP32), INVALID),
 ])
 def test_fwd_rejects(kw, expect):
     assert _fwd(**kw) == expect
@@ -360,7 +363,8 @@ def _f8(**kw):
     (_q8, dict(x=None), INVALID), (_q8, dict(codes=PTR[1] + 4), INVALID), (_q8, dict(N=0), INVALID),
     (_q8, dict(H=0), INVALID), (_q8, dict(d=32), UNSUPPORTED), (_q8, dict(d=256), UNSUPPORTED),
     (_q8, dict(dtype=fa.FA_FP32), UNSUPPORTED), (_q8, dict(dtype=7), INVALID),
-    (_q8, dict(B=1 << 12, N=1 << 12, H=1 << 8), INVALID),
+    (_q8, dict(B=1 << 12, N=1 << 12, H=1 << 8), INVALID), (_q8, dict(N=65535 * 128 + 1, H=1), INVALID),
+    (_v8, dict(B=65536, N=1, Hkv=1), INVALID), (_f8, dict(N=65535 * 128 + 1, H=1, Hkv=1), INVALID),
     (_v8, dict(scales=None), INVALID), (_v8, dict(v=PTR[0] + 2), INVALID), (_v8, dict(Hkv=-1), INVALID),
     (_v8, dict(d=96), UNSUPPORTED), (_v8, dict(dtype=fa.FA_FP32), UNSUPPORTED),
     (_f8, dict(vs=None), INVALID), (_f8, dict(lse=PTR[7] + 4), INVALID), (_f8, dict(H=6, Hkv=4), INVALID),
