@@ -309,8 +309,11 @@ int fa_version(void);
  * the error of FP8 against an exact reference with and without them).
  *
  * Format: OCP e4m3 "fn" (bias 7, largest finite 448, round to nearest even).
- * A block's scale is 2^e, the smallest power of two with amax <= 448 2^e, so
- * a code is the rounding of x / 2^e alone and x ~ decode(code) * 2^e.
+ * A block's scale is 2^e, the smallest power of two with amax <= 448 2^e
+ * (e >= -127; an all-zero block gets 2^0), so a code is the rounding of
+ * x / 2^e alone and x ~ decode(code) * 2^e. Inputs must be finite: a NaN or
+ * infinity in a block gives that block undefined codes and scale (not
+ * checked; the values are in device memory).
  *
  * Three calls: quantize Q and K (fa_quantize_fp8_qk), quantize V
  * (fa_quantize_fp8_v), then fa_fwd_fp8. Every buffer is caller-owned device
