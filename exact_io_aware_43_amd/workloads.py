@@ -60,6 +60,9 @@ WORKLOADS = {
     "varlen_alibi": Workload("varlen_alibi", "bf16", 32, 16, 16, 8192, 128, causal=True,
                              alibi=True, backward=False, varlen=(64, 8192)),
     "gqa": Workload("gqa", "bf16", 2, 32, 8, 8192, 128, causal=True),
+    # the long-context shape in fp16 (same draws, rounded to fp16)
+    "long_causal_fp16": Workload("long_causal_fp16", "fp16", 1, 32, 32, 16384, 128, causal=True,
+                                 std=1.0 / math.sqrt(2.0)),
 }
 
 _TORCH_DTYPE = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}
