@@ -248,9 +248,7 @@ __global__ void v_scale_kernel(float* scales, int n) {
 }
 
 // ---------------------------------------------------------------- forward
-constexpr int F8_BR = 256;  // query rows per workgroup (8 waves x 32)
 constexpr int F8_BC = 128;  // keys per K / V^T tile (one K scale block)
-constexpr int F8_NT = 512;
 
 struct Fp8Args {
     const uint8_t* q;   // [B, N, H, D]
@@ -265,8 +263,10 @@ struct Fp8Args {
     float scale_log2;   // softmax scale * log2(e) (already divided by D under the rotation)
 };
 
-template <typename TO, int D, bool CAUSAL>
-__global__ __launch_bounds__(F8_NT, 1) void fwd_fp8_kernel(Fp8Args a) {
+// NW waves of 32 query rows each; with NW = 4 two workgroups share a CU
+template <typename TO, int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void fwd_fp8_kernel(Fp8Args a) {
+    constexpr int F8_BR = 32 * NW, F8_NT = 64 * NW;
     // byte tiles viewed as 16-bit rows of D / 2 (K: keys x D bytes) and
     // F8_BC / 2 (V^T: channels x F8_BC bytes) elements, swizzled like the
     // 16-bit tiles; two named stages
@@ -515,14 +515,24 @@ hipError_t quant_v_d(const void* v, uint8_t* codes_t, float* scales, int B, int 
     return hipGetLastError();
 }
 
+template <typename TO, int D, bool CAUSAL, int NW>
+hipError_t fwd_nw(const Fp8Args& a, hipStream_t s) {
+    dim3 grid(a.H, a.B, (a.N + 32 * NW - 1) / (32 * NW));
+    hipLaunchKernelGGL((fwd_fp8_kernel<TO, D, CAUSAL, NW>), grid, dim3(64 * NW), 0, s, a);
+    return hipGetLastError();
+}
+
+// Four waves (two workgroups per CU) at head dim 64 and for causal masks, eight
+// for non-causal head dim 128; outputs are the same either way. Measured on
+// the GPT-2-medium shape (d 64): 4 waves 15% faster; causal d 128 at 8192 keys
+// with GQA: 6% faster, at 16384 keys even; non-causal d 128: 4% slower.
 template <typename TO, int D>
 hipError_t fwd_d(const Fp8Args& a, bool causal, hipStream_t s) {
-    dim3 grid(a.H, a.B, (a.N + F8_BR - 1) / F8_BR);
-    if (causal)
-        hipLaunchKernelGGL((fwd_fp8_kernel<TO, D, true>), grid, dim3(F8_NT), 0, s, a);
+    if (causal) return fwd_nw<TO, D, true, 4>(a, s);
+    if constexpr (D == 64)
+        return fwd_nw<TO, D, false, 4>(a, s);
     else
-        hipLaunchKernelGGL((fwd_fp8_kernel<TO, D, false>), grid, dim3(F8_NT), 0, s, a);
-    return hipGetLastError();
+        return fwd_nw<TO, D, false, 8>(a, s);
 }
 
 }  // namespace
