@@ -106,3 +106,16 @@ def test_counter_summary_means_per_dispatch(tmp_path):
     assert "| fwd | 2 | — | 50 |" in out.replace("50.0", "50")
     assert "| bwd_dq | 1 | 70 | — |" in out
     assert "neg" not in out
+
+
+def test_metric_labels_name_their_workload():
+    b = _bench()
+    sys.path.insert(0, ROOT)
+    from exact_io_aware_43_amd.workloads import WORKLOADS
+
+    assert b.metric_label(WORKLOADS["long_causal"], True) == b.METRIC
+    for name in ("gpt2m", "gqa", "varlen_alibi", "long_causal_fp16"):
+        w = WORKLOADS[name]
+        label = b.metric_label(w, bool(w.backward))
+        assert label != b.METRIC and f"({name})" in label
+        assert ("fwd/bwd" in label) == bool(w.backward)
