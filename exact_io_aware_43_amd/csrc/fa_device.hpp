@@ -248,8 +248,9 @@ static_assert(swz_xor_forms_hold<32>() && swz_xor_forms_hold<64>() && swz_xor_fo
 // memory the 16-byte chunk that belongs at that position, at a byte offset
 // from the tile's first row that is fixed for the kernel (precomputed once).
 // Per tile only a buffer descriptor is built (scalar code): its base is the
-// tile's first row and its size ends with row `nrows` - 1, so the hardware
-// range check turns the chunks of rows at or past `nrows` into zeros. Every
+// tile's first row and its size ends with the last element of row `nrows` - 1
+// in memory, so the hardware range check turns the chunks of rows at or past
+// `nrows` into zeros. Every
 // kernel masks such rows (P = 0), and zero rows contribute exactly zero. `NW`
 // waves share the tile; a tile of fewer 1 KB instructions than waves (small
 // head dims) is issued by the first INSTR waves alone. The loads complete
@@ -266,12 +267,18 @@ struct DmaTile {
     // row (row stride `ld`), less the instruction's immediate offset 1024 i
     uint32_t boff[PER_WAVE];
     uint32_t ld2;             // row stride in bytes
+    uint32_t rowb;            // bytes of one row in memory (2 dl)
 
     // `dl`: elements per row in memory (D, or fewer for a tile whose upper
     // columns are padding): chunks at or past it take an offset beyond any
     // buffer range, so the range check stores zeros there and nothing is read.
+    // The range ends after the last valid row's dl elements: with a row stride
+    // below 2 D bytes (head dim 16 in the 32-wide tiles, one head) an end at D
+    // elements would take in the first chunks of the row after it, past the
+    // end of the tensor for the last row.
     __device__ __forceinline__ void init(int wave, int lane, size_t ld, int dl = D) {
         ld2 = (uint32_t)(ld * 2);
+        rowb = 2u * (uint32_t)dl;
 #pragma unroll
         for (int i = 0; i < PER_WAVE; ++i) {
             const int p = (wave * PER_WAVE + i) * 64 + lane;  // chunk index in LDS order
@@ -289,7 +296,7 @@ struct DmaTile {
 #if defined(__HIP_DEVICE_COMPILE__)  // the buffer descriptor type exists for the GPU target only
         if (PARTIAL && wave >= INSTR) return;
         const int valid = min(nrows - row_start, ROWS);
-        const uint32_t bytes = valid > 0 ? (uint32_t)(valid - 1) * ld2 + D * 2 : 0u;
+        const uint32_t bytes = valid > 0 ? (uint32_t)(valid - 1) * ld2 + rowb : 0u;
         const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint16_t*>(base) + (size_t)row_start * (ld2 / 2), (short)0, (int)bytes, kBufferWord3);
         // One LDS base (M0) per wave, tile and group of 4 instructions: the

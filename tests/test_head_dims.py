@@ -160,3 +160,41 @@ def test_head_dim_16_leaves_neighbours_alone():
     ref0 = OA.attention_bwd(sub["q"], sub["k"], sub["v"], sub["do"], scale=inp["scale"], causal=True)
     _banner(str(_compare_bwd(w0, [f64(g2[0][:, :, :2]), f64(g2[1][:, :, :1]), f64(g2[2][:, :, :1])], ref0,
                              note="head dim 16 beside NaN heads")))
+
+
+@pytest.mark.parametrize("H,Hkv,packed", [(1, 1, False), (4, 1, True), (1, 1, True)],
+                         ids=["mha1_dense", "mqa_packed", "mha1_packed"])
+def test_head_dim_16_reads_no_row_past_the_end(H, Hkv, packed):
+    """Head dim 16 with a single kv head (or a single query head): a 16-bit row
+    of the tensor is 32 bytes, less than a row of the 32-wide staged tiles. The
+    tiles that hold a tensor's last row must not take in the row after it. Each
+    input sits at the start of a buffer whose next row is NaN; a read of that
+    row would reach O, dQ, dK or dV through a zero weight (0 x NaN), so forward
+    and backward must still match the oracle on every element."""
+    w = Workload(f"d16_end_{H}_{Hkv}_{int(packed)}", "bf16", 3 if packed else 2, H, Hkv, 300, 16, causal=True,
+                 varlen=(1, 300) if packed else None)
+    lengths = [300, 17, 129] if packed else None
+    inp = make_inputs(w, 11, lengths=lengths, with_grad=True)
+    d = to_dev(inp)
+
+    def before_nan_row(t):
+        rows = t.shape[0]
+        buf = torch.full((rows + 1,) + tuple(t.shape[1:]), float("nan"), dtype=t.dtype, device=t.device)
+        buf[:rows] = t
+        return buf[:rows]
+
+    q, k, v, do = (before_nan_row(d[x]) for x in ("q", "k", "v", "do"))
+    args = dict(causal=True, softmax_scale=inp["scale"], cu_seqlens=d["cu_seqlens"], max_seqlen=inp["max_seqlen"])
+    o, lse = fa.attention(q, k, v, **args)
+    g = fa.attention_bwd(do, q, k, v, o, lse, **args)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = OA.attention_fwd(inp["q"], inp["k"], inp["v"], scale=inp["scale"], causal=True,
+                                      cu_seqlens=inp["cu_seqlens"])
+    lens = seq_lengths(inp, w)
+    mask = np.zeros(tuple(lse.shape), dtype=bool)
+    for b, n in enumerate(lens):
+        mask[b, :, :n] = True
+    _banner(str(_compare_fwd(w, f64(o), o_ref, f64(lse)[mask], lse_ref[mask], note="head dim 16 before a NaN row")))
+    ref = OA.attention_bwd(inp["q"], inp["k"], inp["v"], inp["do"], scale=inp["scale"], causal=True,
+                           cu_seqlens=inp["cu_seqlens"])
+    _banner(str(_compare_bwd(w, [f64(x) for x in g], ref, note="head dim 16 before a NaN row")))
