@@ -235,6 +235,10 @@ def _fmt(x):
     return "—" if x is None else (f"{x:.2e}" if isinstance(x, float) else str(x))
 
 
+def _in_grid(r) -> bool:
+    return "::test_sweep_case[" in (r.get("test") or "")
+
+
 def write_report(path: str) -> None:
     """RECORDS as JSON at ``path`` and as Markdown tables at ``path + '.md'``: the
     named workloads at full size first (worst value of each metric over their
@@ -266,10 +270,24 @@ def write_report(path: str) -> None:
             vals = {k: max((r[k] for r in rs if k in r), default=None) for k in keys}
             cells = [_fmt(vals.get(k)) if k in keys else "" for k in fwd_keys + bwd_keys]
             lines.append(f"| {name} | {kind} | {len(rs)} | " + " | ".join(cells) + " |")
-    lines += ["", "## Every comparison", "",
+    # the randomized grid: one row per pass, worst value over its cases
+    grid = [r for r in RECORDS if _in_grid(r)]
+    if grid:
+        lines += ["", "## Randomized instance grid (tests/test_sweep.py, worst over its cases)", "",
+                  "| pass | cases | " + " | ".join(fwd_keys) + " | " + " | ".join(b + " rel-RMS" for b in bwd_keys) + " |",
+                  "|" + "---|" * (2 + len(fwd_keys) + len(bwd_keys))]
+        for kind in ("fwd", "bwd"):
+            rs = [r for r in grid if r["kind"] == kind]
+            keys = fwd_keys if kind == "fwd" else bwd_keys
+            vals = {k: max((r[k] for r in rs if k in r), default=None) for k in keys}
+            cells = [_fmt(vals.get(k)) if k in keys else "" for k in fwd_keys + bwd_keys]
+            lines.append(f"| {kind} | {len(rs)} | " + " | ".join(cells) + " |")
+    lines += ["", "## Every other comparison", "",
               "| test | workload | pass | note | metrics |", "|---|---|---|---|---|"]
     skip = {"test", "kind", "workload", "note", "dtype", "B", "H", "Hkv", "N", "d", "causal", "alibi"}
     for r in RECORDS:
+        if _in_grid(r):
+            continue
         shape = f"{r['dtype']} B{r['B']} H{r['H']}/{r['Hkv']} N{r['N']} d{r['d']} c{int(r['causal'])} a{int(r['alibi'])}"
         m = ", ".join(f"{k}={_fmt(v)}" for k, v in r.items() if k not in skip)
         lines.append(f"| {r['test']} | {r['workload']} ({shape}) | {r['kind']} | {r.get('note', '')} | {m} |")

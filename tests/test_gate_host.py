@@ -66,3 +66,20 @@ def test_records_and_report(tmp_path):
     gu.write_report(str(tmp_path / "parity.json"))
     assert (tmp_path / "parity.json.md").read_text().startswith("# GPU parity")
     del gu.RECORDS[n0:]
+
+
+def test_report_folds_the_randomized_grid(tmp_path):
+    n0 = len(gu.RECORDS)
+    saved = gu.CURRENT_TEST["id"]
+    try:
+        gu.CURRENT_TEST["id"] = "tests/test_sweep.py::test_sweep_case[s1_case]"
+        _fwd(W16, [1.0], [1.0])
+        gu.CURRENT_TEST["id"] = "tests/test_other.py::test_one"
+        _fwd(W16, [1.0], [1.0])
+    finally:
+        gu.CURRENT_TEST["id"] = saved
+    gu.write_report(str(tmp_path / "parity.json"))
+    text = (tmp_path / "parity.json.md").read_text()
+    assert "## Randomized instance grid" in text and "| fwd | 1 |" in text
+    assert "test_sweep_case[s1_case]" not in text and "tests/test_other.py::test_one" in text
+    del gu.RECORDS[n0:]
