@@ -236,7 +236,7 @@ def _fmt(x):
 
 
 def _in_grid(r) -> bool:
-    return "::test_sweep_case[" in (r.get("test") or "")
+    return "::test_sweep_" in (r.get("test") or "")
 
 
 def write_report(path: str) -> None:
@@ -273,7 +273,7 @@ def write_report(path: str) -> None:
     # the randomized grid: one row per pass, worst value over its cases
     grid = [r for r in RECORDS if _in_grid(r)]
     if grid:
-        lines += ["", "## Randomized instance grid (tests/test_sweep.py, worst over its cases)", "",
+        lines += ["", "## Randomized instance grids (tests/test_sweep.py: plain, and window / softcap / dropout; worst over their cases)", "",
                   "| pass | cases | " + " | ".join(fwd_keys) + " | " + " | ".join(b + " rel-RMS" for b in bwd_keys) + " |",
                   "|" + "---|" * (2 + len(fwd_keys) + len(bwd_keys))]
         for kind in ("fwd", "bwd"):

@@ -80,6 +80,6 @@ def test_report_folds_the_randomized_grid(tmp_path):
         gu.CURRENT_TEST["id"] = saved
     gu.write_report(str(tmp_path / "parity.json"))
     text = (tmp_path / "parity.json.md").read_text()
-    assert "## Randomized instance grid" in text and "| fwd | 1 |" in text
+    assert "## Randomized instance grids" in text and "| fwd | 1 |" in text
     assert "test_sweep_case[s1_case]" not in text and "tests/test_other.py::test_one" in text
     del gu.RECORDS[n0:]

@@ -51,3 +51,71 @@ def test_sweep_case(case):
     G.check_fwd_full(w, inp, o, lse)
     grads = G.gpu_bwd(w, dinp, o, lse)
     G.check_bwd_full(w, inp, grads)
+
+
+def _ext_cases():
+    """The same grid through fa_fwd_ext / fa_bwd_ext and the dropout entry
+    points: a sliding window (each bound unbounded or drawn in [0, N + 64)),
+    softcapping (cap 5 or 20, Q and K at twice the spread so that it bites),
+    dropout (p 0.1 or 0.3, with or without a window), or window and softcap."""
+    out = []
+    rng = np.random.default_rng(3001)
+    for dt in ("bf16", "fp16"):
+        for d in (16, 32, 64, 128, 256):
+            for variant in ("window", "softcap", "dropout", "window_softcap"):
+                N = int(rng.integers(1, 600))
+                Hkv = int(rng.choice([4, 2, 1]))
+                causal = bool(rng.random() < 0.5)
+                alibi = bool(rng.random() < 0.3)
+                packed = bool(rng.random() < 0.3)
+                window = (-1, -1)
+                if "window" in variant or (variant == "dropout" and rng.random() < 0.5):
+                    bound = lambda: -1 if rng.random() < 0.25 else int(rng.integers(0, N + 64))
+                    window = (bound(), bound())
+                cap = float(rng.choice([5.0, 20.0])) if "softcap" in variant else 0.0
+                p = float(rng.choice([0.1, 0.3])) if variant == "dropout" else 0.0
+                name = (f"{dt}_d{d}_{variant}_c{int(causal)}_a{int(alibi)}_N{N}_g{Hkv}{'_packed' if packed else ''}"
+                        f"_w{window[0]}_{window[1]}")
+                w = Workload(name, dt, 3 if packed else 2, 4, Hkv, N, d, causal=causal, alibi=alibi,
+                             std=2.0 if cap else 1.0, varlen=(1, N) if packed else None)
+                out.append((name, w, window, cap, p))
+    return out
+
+
+EXT_CASES = _ext_cases()
+
+
+@pytest.mark.parametrize("case", EXT_CASES, ids=[c[0] for c in EXT_CASES])
+def test_sweep_ext_case(case):
+    import exact_io_aware_43_amd as fa
+    import oracle.attention as OA
+    import oracle.philox as PX
+    import torch
+
+    name, w, window, cap, p = case
+    print(f"[sweep-ext] {name} softcap {cap} p {p}", flush=True)
+    inp = make_inputs(w, 5, with_grad=True)
+    if w.std != 1.0:
+        # wide scores for the cap; V and dO back to unit spread (exact division)
+        inp["v"], inp["do"] = inp["v"] / w.std, inp["do"] / w.std
+    d = G.to_dev(inp)
+    seed, offset = 987654321, 3
+    args = dict(causal=w.causal, softmax_scale=inp["scale"], alibi_slopes=d["alibi_slopes"],
+                cu_seqlens=d["cu_seqlens"], max_seqlen=inp["max_seqlen"], window_size=window, softcap=cap,
+                dropout_p=p, seed=seed, offset=offset)
+    o, lse = fa.attention(d["q"], d["k"], d["v"], **args)
+    torch.cuda.synchronize()
+    kw = dict(scale=inp["scale"], causal=w.causal, alibi_slopes=inp["alibi_slopes"], cu_seqlens=inp["cu_seqlens"],
+              window=window, softcap=cap, dropout=(p, seed, offset) if p else None)
+    o_ref, lse_ref = OA.attention_fwd(inp["q"], inp["k"], inp["v"], **kw)
+    lg = G.f64(lse)
+    mask = np.zeros(lg.shape, dtype=bool)
+    for b, n in enumerate(G.seq_lengths(inp, w)):
+        mask[b, :, :n] = True
+    bar = 256.0 / PX.keep_threshold(p) if p else 1.0
+    G._compare_fwd(w, G.f64(o), o_ref, lg[mask], lse_ref[mask], note=f"window {window} softcap {cap} p {p}",
+                   o_bar_scale=bar)
+    g = fa.attention_bwd(d["do"], d["q"], d["k"], d["v"], o, lse, **args)
+    torch.cuda.synchronize()
+    ref = OA.attention_bwd(inp["q"], inp["k"], inp["v"], inp["do"], **kw)
+    G._compare_bwd(w, [G.f64(x) for x in g], ref, note=f"window {window} softcap {cap} p {p}")
