@@ -137,6 +137,27 @@ FWD_CASES = [
 ]
 
 
+def _random_fwd_cases(n=16):
+    """Shapes drawn from a fixed generator: dtype, head dim, mask, rotation,
+    batch, heads and query heads per kv head, and a length in [1, 1500) (both
+    wave counts of the attention kernel, ragged tiles, GQA and MQA)."""
+    rng = np.random.default_rng(4001)
+    out = []
+    for i in range(n):
+        dtype = str(rng.choice(["bf16", "fp16"]))
+        d = int(rng.choice([64, 128]))
+        causal, rot = bool(rng.random() < 0.5), bool(rng.random() < 0.5)
+        H = int(rng.choice([2, 4, 8]))
+        Hkv = int(rng.choice([h for h in (1, 2, 4, 8) if H % h == 0]))
+        B, N = int(rng.integers(1, 4)), int(rng.integers(1, 1500))
+        out.append((f"rand{i}_{dtype}_d{d}_c{int(causal)}_r{int(rot)}_B{B}H{H}kv{Hkv}_N{N}", dtype, B, H, Hkv, N, d,
+                    causal, rot))
+    return out
+
+
+FWD_CASES += _random_fwd_cases()
+
+
 def _fwd_fp8(d_in, causal, signs, scale, out_dtype):
     o, lse = fa.attention_fp8(d_in["q"], d_in["k"], d_in["v"], causal=causal, softmax_scale=scale,
                               hadamard_signs=signs, out_dtype=out_dtype)
