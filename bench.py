@@ -420,7 +420,9 @@ def bench_decode(args):
     flop = 4.0 * H * Nq * keys * d
     alg_bytes = 2 * keys * Hkv * d * 2 + 2 * B * Nq * H * d * 2 + 4 * B * H * Nq
     gbs = alg_bytes / (ms * 1e-3) / 1e9
-    splits = ws_bytes // (B * H * Nq * (d + 1) * 4) if ws_bytes else 1
+    # partial states per query row: the key ranges per kv head (balanced over
+    # the caches laid end to end whenever the automatic choice uses several)
+    ranges = ws_bytes // (B * H * Nq * (d + 1) * 4) if ws_bytes else 1
     out = {
         "metric": "decode attention HBM GB/s (every cached K/V byte read once, queries and output once), "
                   "bf16 d=128, and % of MI355X HBM peak",
@@ -433,7 +435,7 @@ def bench_decode(args):
         "roofline": {"kernel": "decode_split+merge", "bound": "hbm", "achieved": round(gbs, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
                      "avg_launch_ms": round(ms, 4), "work_per_launch": int(alg_bytes)},
-        "splits": int(splits),
+        "key_ranges_per_kv_head": int(ranges), "balanced_ranges": bool(ws_bytes),
     }
     print(json.dumps(out), flush=True)
 

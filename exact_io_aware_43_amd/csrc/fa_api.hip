@@ -281,6 +281,18 @@ int decode_splits(int B, int H, int Hkv, int Nq, int Nk, int num_splits) {
     return std::max(1, std::min({S, tiles, (int)kMaxTiles}));
 }
 
+// The split kernel's grid: `parts` ranges and whether they are flat ranges of
+// the caches laid end to end. The automatic choice with more than one range
+// per sequence goes flat (B * S equal ranges per kv head: with caches of
+// different lengths, ranges of each sequence's own length leave the
+// workgroups of the longest cache running alone at the end); an explicit
+// count keeps `num_splits` ranges of every sequence.
+void decode_plan(int B, int H, int Hkv, int Nq, int Nk, int num_splits, int& parts, int& flat) {
+    const int S = decode_splits(B, H, Hkv, Nq, Nk, num_splits);
+    flat = (num_splits == 0 && S > 1) ? 1 : 0;
+    parts = flat ? B * S : S;
+}
+
 size_t decode_workspace_bytes(int B, int H, int Nq, int d, int splits) {
     if (splits <= 1) return 0;
     const size_t rows = (size_t)B * H * Nq * splits;
@@ -304,7 +316,9 @@ extern "C" {
 
 size_t fa_kvcache_workspace_size(int B, int H, int Hkv, int Nq, int Nk, int d, int num_splits) {
     if (check_decode(B, H, Hkv, Nq, Nk, d, 1.0f, 0, FA_BF16) != FA_OK || num_splits < 0) return 0;
-    return decode_workspace_bytes(B, H, Nq, d, decode_splits(B, H, Hkv, Nq, Nk, num_splits));
+    int parts, flat;
+    decode_plan(B, H, Hkv, Nq, Nk, num_splits, parts, flat);
+    return decode_workspace_bytes(B, H, Nq, d, parts);
 }
 
 int fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
@@ -319,7 +333,7 @@ int fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, void
         if (!aligned16(p)) return FA_ERR_INVALID_ARG;
     if (!aligned16(cache_seqlens) || (alibi_slopes && !aligned16(alibi_slopes))) return FA_ERR_INVALID_ARG;
     fa::DecodeArgs a{};
-    a.splits = decode_splits(B, H, Hkv, Nq, Nk, num_splits);
+    decode_plan(B, H, Hkv, Nq, Nk, num_splits, a.splits, a.flat);
     const size_t need = decode_workspace_bytes(B, H, Nq, d, a.splits);
     if (need > 0 && (!workspace || !aligned16(workspace) || workspace_bytes < need)) return FA_ERR_WORKSPACE;
     a.q = q;

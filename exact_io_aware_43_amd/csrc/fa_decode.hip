@@ -37,32 +37,31 @@ constexpr int DNW = 4;           // waves per split workgroup
 constexpr int DNT = 64 * DNW;
 constexpr int DBC = 32 * DNW;    // keys per staged tile (32 per wave)
 
-template <typename T, int D, bool CAUSAL, bool ALIBI>
-__global__ __launch_bounds__(DNT, 1) void decode_split_kernel(DecodeArgs a) {
-    constexpr int TILE = DBC * D;
-    __shared__ __attribute__((aligned(16))) uint16_t stA[2 * TILE];
-    __shared__ __attribute__((aligned(16))) uint16_t stB[2 * TILE];
+// Sequence b's cache length, clamped to [0, Nk].
+__device__ __forceinline__ int cache_len(const DecodeArgs& a, int b) {
+    const int L = a.seqlens[b];
+    return L < 0 ? 0 : (L > a.Nk ? a.Nk : L);
+}
 
+// Keys [kbeg, kend) of sequence b (L cached keys) for the query rows of row
+// group rg of kv head g: the tile loop, the merge of the four waves' states,
+// then O and lse of the range, final (direct) or as partial `slot` of the
+// sequence's rows. Every wave of the workgroup calls it with the same
+// arguments (it holds barriers), and it leaves the staging buffers free.
+template <typename T, int D, bool CAUSAL, bool ALIBI>
+__device__ __forceinline__ void decode_range(const DecodeArgs& a, uint16_t* stA, uint16_t* stB, int g, int rg, int b,
+                                             int L, int kbeg, int kend, int slot, bool direct) {
+    constexpr int TILE = DBC * D;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int col = lane & 31, kg = lane >> 5;
-    const int g = blockIdx.x % a.Hkv, rg = blockIdx.x / a.Hkv;  // kv head, row group
-    const int b = blockIdx.y, sp = blockIdx.z;
     const int G = a.H / a.Hkv;
     const int R = G * a.Nq;  // query rows of this kv head
 
-    int L = a.seqlens[b];
-    L = L < 0 ? 0 : (L > a.Nk ? a.Nk : L);
     const int rr = rg * 32 + col;  // this lane's row
     const bool row_live = rr < R;
     const int hh = row_live ? rr / a.Nq : 0, t = row_live ? rr % a.Nq : 0;
     const int h = g * G + hh;
     const int pos = L - a.Nq + t;  // position of this lane's query in its sequence
-
-    // keys of this split: the sequence's L keys cut into `splits` ranges of
-    // ceil(L / splits) keys rounded up to 32 (trailing ranges may be empty)
-    const int chunk = ((L + a.splits - 1) / a.splits + 31) & ~31;
-    const int kbeg = min(L, sp * chunk);
-    const int kend = min(L, kbeg + chunk);
     const int ntile = kend > kbeg ? (kend - kbeg + DBC - 1) / DBC : 0;
 
     const size_t ldq = (size_t)a.H * D, ldk = (size_t)a.Hkv * D;
@@ -213,21 +212,66 @@ __global__ __launch_bounds__(DNT, 1) void decode_split_kernel(DecodeArgs a) {
                 o[e] = acc * inv;
             }
             const size_t orow = ((size_t)b * a.Nq + tq) * a.H + hq;  // row of O in [B, Nq, H, d]
-            if (a.splits == 1) {
+            if (direct) {
                 T* O = reinterpret_cast<T*>(a.o) + orow * D + 32 * part;
 #pragma unroll
                 for (int e = 0; e < 32; e += 4)
                     *reinterpret_cast<uint2*>(O + e) = pack4<T>(o[e], o[e + 1], o[e + 2], o[e + 3]);
                 if (part == 0) a.lse[((size_t)b * a.H + hq) * a.Nq + tq] = lse;
             } else {
-                // partial of split sp: [B, H, Nq, splits] lse and [B, H, Nq, splits, D] O
-                const size_t prow = (((size_t)b * a.H + hq) * a.Nq + tq) * a.splits + sp;
+                // partial `slot`: [B, H, Nq, splits] lse and [B, H, Nq, splits, D] O
+                const size_t prow = (((size_t)b * a.H + hq) * a.Nq + tq) * a.splits + slot;
                 float* Op = a.part_o + prow * D + 32 * part;
 #pragma unroll
                 for (int e = 0; e < 32; e += 4) *reinterpret_cast<float4*>(Op + e) = make_float4(o[e], o[e + 1], o[e + 2], o[e + 3]);
                 if (part == 0) a.part_lse[prow] = lse;
             }
         }
+    }
+    __syncthreads();  // the merge buffers are the staging buffers of a next range
+}
+
+// Key ranges of the concatenated caches in flat mode: the T keys of all
+// sequences (kv head by kv head the same) cut into `parts` ranges of C keys
+// (C a multiple of 32); returns C, 0 when every cache is empty.
+__device__ __forceinline__ long long flat_chunk(long long T, int parts) {
+    return ((T + parts - 1) / parts + 31) & ~31ll;
+}
+
+template <typename T, int D, bool CAUSAL, bool ALIBI>
+__global__ __launch_bounds__(DNT, 1) void decode_split_kernel(DecodeArgs a) {
+    constexpr int TILE = DBC * D;
+    __shared__ __attribute__((aligned(16))) uint16_t stA[2 * TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t stB[2 * TILE];
+    const int g = blockIdx.x % a.Hkv, rg = blockIdx.x / a.Hkv;  // kv head, row group
+    if (a.flat) {
+        // Balanced ranges: workgroup p takes keys [p C, (p + 1) C) of the
+        // caches laid end to end, one piece per sequence its range meets, so
+        // every workgroup streams the same number of keys whatever the mix of
+        // cache lengths. A piece's state is partial p of its sequence.
+        const int p = blockIdx.y;
+        long long total = 0;
+        for (int b = 0; b < a.B; ++b) total += cache_len(a, b);
+        const long long C = flat_chunk(total, a.splits);
+        const long long lo = (long long)p * C, hi = min(total, lo + C);
+        long long off = 0;
+        for (int b = 0; b < a.B && off < hi; ++b) {
+            const int L = cache_len(a, b);
+            const long long s0 = max(lo, off), s1 = min(hi, off + L);
+            if (s1 > s0)
+                decode_range<T, D, CAUSAL, ALIBI>(a, stA, stB, g, rg, b, L, (int)(s0 - off), (int)(s1 - off), p,
+                                                  false);
+            off += L;
+        }
+    } else {
+        // keys of split sp: sequence b's L keys cut into `splits` ranges of
+        // ceil(L / splits) keys rounded up to 32 (trailing ranges may be empty)
+        const int b = blockIdx.y, sp = blockIdx.z;
+        const int L = cache_len(a, b);
+        const int chunk = ((L + a.splits - 1) / a.splits + 31) & ~31;
+        const int kbeg = min(L, sp * chunk);
+        const int kend = min(L, kbeg + chunk);
+        decode_range<T, D, CAUSAL, ALIBI>(a, stA, stB, g, rg, b, L, kbeg, kend, sp, a.splits == 1);
     }
 }
 
@@ -239,11 +283,27 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
     const int e = threadIdx.x;
     const int S = a.splits;
     const float* pl = a.part_lse + (size_t)row * S;
+    // partials written for this row: all S ranges of its sequence, or in flat
+    // mode the ranges [s_lo, s_hi] that met it (none for an empty cache)
+    int s_lo = 0, s_hi = S - 1;
+    if (a.flat) {
+        const int bq = row / (a.H * a.Nq);
+        long long total = 0, off = 0;
+        for (int b = 0; b < a.B; ++b) {
+            const int L = cache_len(a, b);
+            if (b < bq) off += L;
+            total += L;
+        }
+        const int L = cache_len(a, bq);
+        const long long C = flat_chunk(total, S);
+        s_lo = L > 0 ? (int)(off / C) : 0;
+        s_hi = L > 0 ? (int)((off + L - 1) / C) : -1;
+    }
     float m = -INFINITY;
-    for (int s = 0; s < S; ++s) m = fmaxf(m, pl[s]);
+    for (int s = s_lo; s <= s_hi; ++s) m = fmaxf(m, pl[s]);
     float total = 0.f, acc = 0.f;
     if (m != -INFINITY) {
-        for (int s = 0; s < S; ++s) {
+        for (int s = s_lo; s <= s_hi; ++s) {
             const float ws = pl[s] == -INFINITY ? 0.f : __expf(pl[s] - m);
             total += ws;
             acc = fmaf(ws, a.part_o[((size_t)row * S + s) * D + e], acc);
@@ -259,10 +319,10 @@ template <typename T, int D, bool CAUSAL, bool ALIBI>
 hipError_t launch(const DecodeArgs& a, hipStream_t s) {
     const int G = a.H / a.Hkv;
     const int rgroups = (G * a.Nq + 31) / 32;
-    dim3 grid(a.Hkv * rgroups, a.B, a.splits);
+    const dim3 grid = a.flat ? dim3(a.Hkv * rgroups, a.splits, 1) : dim3(a.Hkv * rgroups, a.B, a.splits);
     hipLaunchKernelGGL((decode_split_kernel<T, D, CAUSAL, ALIBI>), grid, dim3(DNT), 0, s, a);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || a.splits == 1) return e;
+    if (e != hipSuccess || (a.splits == 1 && !a.flat)) return e;
     hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(a.B * a.H * a.Nq), dim3(D), 0, s, a);
     return hipGetLastError();
 }

@@ -65,9 +65,11 @@ struct DecodeArgs {
     float* lse;           // [B, H, Nq]
     const int* seqlens;   // [B], device
     const float* slopes;  // [H] or NULL
-    float* part_o;        // splits > 1: [B, H, Nq, splits, d] fp32
-    float* part_lse;      //             [B, H, Nq, splits]
+    float* part_o;        // splits > 1 or flat: [B, H, Nq, splits, d] fp32
+    float* part_lse;      //                     [B, H, Nq, splits]
     int B, H, Hkv, Nq, Nk, splits;
+    int flat;             // 1: `splits` equal ranges of the caches laid end to end
+                          // (per kv head), 0: `splits` ranges of each sequence
     float scale_log2;
 };
 

@@ -170,9 +170,14 @@ int fa_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse,
  *   num_splits    : key ranges per sequence and kv head (each sequence's
  *                   L_b keys are cut into that many ranges of ceil(L_b / S)
  *                   keys rounded up to 32); 0 lets the library pick from the
- *                   sizes (about one workgroup per compute unit, at least
- *                   512 keys per range of an Nk-key cache). At most one range
- *                   per 128 keys of Nk is used.
+ *                   sizes: about one workgroup per compute unit, at least
+ *                   512 keys per range of an Nk-key cache, and, when that
+ *                   gives S > 1 ranges per sequence, B * S equal ranges per
+ *                   kv head over the B caches laid end to end (a range may
+ *                   cover the end of one sequence and the start of the
+ *                   next), so caches of different lengths take equal work
+ *                   per workgroup. At most one range per 128 keys of Nk is
+ *                   used per sequence.
  *   workspace     : fp32 partial results when more than one range is used,
  *                   fa_kvcache_workspace_size(...) bytes (0: NULL allowed).
  *
