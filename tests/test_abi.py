@@ -301,8 +301,9 @@ def test_kvcache_workspace_size():
     assert fa.fa_kvcache_workspace_size(2, 8, 2, 3, 4096, 128, 4) == ((2 * 8 * 3 * 4 * 129 * 4 + 255) & ~255)
     # at most one split per 128 keys of the capacity
     assert fa.fa_kvcache_workspace_size(1, 4, 4, 1, 300, 64, 64) == ((1 * 4 * 1 * 3 * 65 * 4 + 255) & ~255)
-    # auto: one workgroup per compute unit, at least 512 keys per range
-    assert fa.fa_kvcache_workspace_size(8, 32, 8, 1, 16384, 128, 0) == ((8 * 32 * 1 * 4 * 129 * 4 + 255) & ~255)
+    # auto: one workgroup per compute unit, at least 512 keys per range; with several ranges per sequence they
+    # are balanced over the caches laid end to end: B * S = 8 * 4 = 32 ranges per kv head, a partial per range
+    assert fa.fa_kvcache_workspace_size(8, 32, 8, 1, 16384, 128, 0) == ((8 * 32 * 1 * 32 * 129 * 4 + 255) & ~255)
     assert fa.fa_kvcache_workspace_size(1, 8, 1, 1, 2048, 128, 0) == ((1 * 8 * 1 * 4 * 129 * 4 + 255) & ~255)
     # auto: a deterministic choice; a large batch of heads needs no split
     assert fa.fa_kvcache_workspace_size(64, 64, 64, 1, 4096, 128, 0) == 0
