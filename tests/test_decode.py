@@ -100,3 +100,20 @@ def test_decode_full_size():
     _banner(f"full size {w} Nq={Nq}")
     o, lse = _run(w, inp, 0, True)
     _banner(str(_check(w, inp, o, lse, True, note="decode workload, every row")))
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_decode_balanced_ranges_over_many_short_caches(causal):
+    """The automatic split's balanced ranges lay the caches of a kv head end to
+    end, so one workgroup can cover several short caches (and the end and start
+    of two long ones). Sixteen caches of 0 to 40 keys between two long ones, with
+    empty and one-key caches among them, against the oracle; queries of empty
+    caches get O = 0 and lse = -inf."""
+    rng = np.random.default_rng(31)
+    lengths = [1500] + [int(x) for x in rng.integers(0, 41, size=16)] + [2048]
+    lengths[3], lengths[7] = 0, 1
+    w = Workload("decode_many_short", "bf16", len(lengths), 8, 2, 2048, 128, causal=causal, alibi=True)
+    inp = make_decode_inputs(w, 2, lengths, seed=33)
+    _banner(f"{w} lengths={lengths}")
+    o, lse = _run(w, inp, 0, causal)
+    _banner(str(_check(w, inp, o, lse, causal, note="balanced ranges, many short caches")))
