@@ -307,14 +307,14 @@ hipError_t launch(const Args& a, unsigned stages, hipStream_t s) {
     }
     if (stages & 4u) {
         constexpr int nw = dq_waves<D, CAUSAL, ALIBI, DROP, CAP>();
-        if constexpr (D == 64 && CAUSAL && nw == 8 && !ALIBI && !DROP && !CAP) {
+        if constexpr ((D == 64 || D == 128) && CAUSAL && nw == 8 && !ALIBI && !DROP && !CAP) {
             // short causal grids (at most two 8-wave workgroups per compute unit):
             // 4-wave workgroups, several of which share a compute unit, and twice
             // as many of them for the longest-first order to balance the causal
             // triangle (B = 4, H = 16, N = 1024: 0.0325 against 0.0273 ms; the
             // non-causal grids were 4-13% slower with 4 waves and keep 8)
             const long long wg8 = (long long)a.H * a.B * ((a.N + 255) / 256);
-            if (wg8 <= 2 * 256) {
+            if (wg8 <= 256) {
                 dim3 grid(a.H, a.B, (a.N + 127) / 128);
                 hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL, ALIBI, DROP, CAP, 4>), grid, dim3(256), 0, s, a);
                 return hipGetLastError();

@@ -339,9 +339,9 @@ hipError_t launch_shape(const Args& a, hipStream_t s) {
 constexpr int kComputeUnits = 256;
 template <typename T, int D, bool CAUSAL, bool ALIBI, bool DROP, bool CAP>
 hipError_t launch(const Args& a, hipStream_t s) {
-    if constexpr (D == 64 && !ALIBI && !DROP && !CAP) {
+    if constexpr ((D == 64 || D == 128) && !ALIBI && !DROP && !CAP) {
         const long long wg8 = (long long)a.Hkv * a.B * ((a.N + DkdvShape<D>::KV_BK - 1) / DkdvShape<D>::KV_BK);
-        if (wg8 <= 2 * kComputeUnits) return launch_shape<T, D, CAUSAL, ALIBI, DROP, CAP, 4>(a, s);
+        if (wg8 <= (D == 64 ? 2 : 1) * kComputeUnits) return launch_shape<T, D, CAUSAL, ALIBI, DROP, CAP, 4>(a, s);
     }
     return launch_shape<T, D, CAUSAL, ALIBI, DROP, CAP, 0>(a, s);
 }
