@@ -181,10 +181,19 @@ __global__ __launch_bounds__(256) void v_amax_kernel(const T* __restrict__ v, fl
     const int cg = threadIdx.x % CG, r0 = threadIdx.x / CG;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int t0 = blockIdx.y * 256, t1 = min(N, t0 + 256);
+    // all 256 / RPI loads of a thread issued before the first is used; a row
+    // past t1 re-reads row t1 - 1, which leaves every maximum unchanged
+    uint4 u[256 / RPI];
+#pragma unroll
+    for (int it = 0; it < 256 / RPI; ++it) {
+        const int t = min(t0 + r0 + it * RPI, t1 - 1);
+        u[it] = *reinterpret_cast<const uint4*>(v + (((size_t)b * N + t) * Hkv + g) * D + 8 * cg);
+    }
     float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int t = t0 + r0; t < t1; t += RPI) {
+#pragma unroll
+    for (int it = 0; it < 256 / RPI; ++it) {
         float f[8];
-        unpack8<T>(*reinterpret_cast<const uint4*>(v + (((size_t)b * N + t) * Hkv + g) * D + 8 * cg), f);
+        unpack8<T>(u[it], f);
 #pragma unroll
         for (int i = 0; i < 8; ++i) m[i] = fmaxf(m[i], fabsf(f[i]));
     }
@@ -215,11 +224,21 @@ __global__ __launch_bounds__(256) void v_quant_kernel(const T* __restrict__ v, u
     __shared__ __attribute__((aligned(16))) float tile[128 * LD];
     const int g = blockIdx.x, tt = blockIdx.y, b = blockIdx.z;  // grid x = kv head
     const int k0 = tt * 128;
+    // every load of the thread in flight before the first LDS store; keys past
+    // the end read key N - 1 and store zeros
+    constexpr int NL = 128 * CG / 256;
+    uint4 u[NL];
 #pragma unroll
-    for (int it = 0; it < 128 * CG / 256; ++it) {
-        const int ci = threadIdx.x + 256 * it, kk = ci / CG, cg = ci % CG, t = k0 + kk;
+    for (int it = 0; it < NL; ++it) {
+        const int ci = threadIdx.x + 256 * it, kk = ci / CG, cg = ci % CG;
+        const int t = min(k0 + kk, N - 1);
+        u[it] = *reinterpret_cast<const uint4*>(v + (((size_t)b * N + t) * Hkv + g) * D + 8 * cg);
+    }
+#pragma unroll
+    for (int it = 0; it < NL; ++it) {
+        const int ci = threadIdx.x + 256 * it, kk = ci / CG, cg = ci % CG;
         float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (t < N) unpack8<T>(*reinterpret_cast<const uint4*>(v + (((size_t)b * N + t) * Hkv + g) * D + 8 * cg), f);
+        if (k0 + kk < N) unpack8<T>(u[it], f);
         *reinterpret_cast<float4*>(tile + kk * LD + 8 * cg) = make_float4(f[0], f[1], f[2], f[3]);
         *reinterpret_cast<float4*>(tile + kk * LD + 8 * cg + 4) = make_float4(f[4], f[5], f[6], f[7]);
     }
