@@ -96,31 +96,51 @@ __device__ __forceinline__ uint4 pack16(const float* x) {
 
 // ---------------------------------------------------------------- Q, K
 // One workgroup of 2 waves per (head, 128-token block, sequence); each lane owns
-// one row: D / 8 loads of 16 bytes, the sign flips and all log2(D) butterfly
-// stages in registers (no cross-lane traffic), then the block maximum over
-// both waves, the scale and D / 16 stores of 16 codes.
+// one row: the sign flips and all log2(D) butterfly stages in registers (no
+// cross-lane traffic), then the block maximum over both waves, the scale and
+// the codes. Rows of one head lie H d elements apart, so the block's rows pass
+// through LDS both ways: D / 8 consecutive lanes move one row's 16-byte chunks
+// (row-contiguous loads and stores), and each lane reads back its own row.
 template <typename T, int D, bool ROT>
 __global__ __launch_bounds__(128) void quant_qk_kernel(const T* __restrict__ x, uint8_t* __restrict__ codes,
                                                        float* __restrict__ scales, int N, int H,
                                                        unsigned long long s0, unsigned long long s1) {
+    constexpr int CPR = D / 8;          // 16-byte input chunks per row
+    constexpr int RPP = QB / CPR;       // rows per pass of the workgroup
+    constexpr int LDR = 2 * D + 16;     // staged row pitch in bytes (padded against bank conflicts)
     __shared__ float wmax[2];
+    __shared__ __attribute__((aligned(16))) uint8_t stage[QB * LDR];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     // grid x = head: workgroups dispatched together read the neighbouring head
     // slices of the same token rows (contiguous memory) rather than rows H d
     // elements apart
     const int h = blockIdx.x, blk = blockIdx.y, b = blockIdx.z;
     const int nb = (N + QB - 1) / QB;
-    const int t = blk * QB + threadIdx.x;
-    const size_t row = ((size_t)b * N + t) * H + h;  // row index of [B, N, H]
-    float r[D];
-    if (t < N) {
-        const uint4* src = reinterpret_cast<const uint4*>(x + row * D);
+    {
+        // pass p: row p * RPP + threadIdx.x / CPR, chunk threadIdx.x % CPR; rows
+        // past N stage zeros. Loads in groups of 16 so that d = 256 stays in
+        // registers.
+        const int cc = threadIdx.x % CPR, r0 = threadIdx.x / CPR;
+        constexpr int NP = QB / RPP, GRP = NP < 16 ? NP : 16;
 #pragma unroll
-        for (int c = 0; c < D / 8; ++c) unpack8<T>(src[c], r + 8 * c);
-    } else {
+        for (int p0 = 0; p0 < NP; p0 += GRP) {
+            uint4 u[GRP];
 #pragma unroll
-        for (int i = 0; i < D; ++i) r[i] = 0.f;
+            for (int p = 0; p < GRP; ++p) {
+                const int rr = (p0 + p) * RPP + r0, tt = blk * QB + rr;
+                u[p] = make_uint4(0, 0, 0, 0);
+                if (tt < N) u[p] = *reinterpret_cast<const uint4*>(x + (((size_t)b * N + tt) * H + h) * D + 8 * cc);
+            }
+#pragma unroll
+            for (int p = 0; p < GRP; ++p)
+                *reinterpret_cast<uint4*>(stage + ((p0 + p) * RPP + r0) * LDR + 16 * cc) = u[p];
+        }
     }
+    __syncthreads();
+    float r[D];
+#pragma unroll
+    for (int c = 0; c < CPR; ++c)
+        unpack8<T>(*reinterpret_cast<const uint4*>(stage + threadIdx.x * LDR + 16 * c), r + 8 * c);
     if (ROT) {
         // signs (bit i % 64 of word i / 64 set: -1), then stages h = 1, 2, 4, ...:
         // the pair (i, i + h) of every 2h-block becomes (a + b, a - b)
@@ -151,12 +171,25 @@ __global__ __launch_bounds__(128) void quant_qk_kernel(const T* __restrict__ x, 
     const int e = block_exp(amax);
     const float inv = __builtin_ldexpf(1.f, -e);
     if (threadIdx.x == 0) scales[((size_t)b * H + h) * nb + blk] = __builtin_ldexpf(1.f, e);
-    if (t >= N) return;
 #pragma unroll
     for (int i = 0; i < D; ++i) r[i] *= inv;
-    uint4* dst = reinterpret_cast<uint4*>(codes + row * D);
+    // the codes of this lane's row over its own staged row (only this lane
+    // reads or writes it until the barrier), then row-contiguous stores
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) dst[c] = pack16(r + 16 * c);
+    for (int c = 0; c < D / 16; ++c)
+        *reinterpret_cast<uint4*>(stage + threadIdx.x * LDR + 16 * c) = pack16(r + 16 * c);
+    __syncthreads();
+    {
+        constexpr int CPO = D / 16, RPO = QB / CPO;  // 16-byte code chunks per row, rows per pass
+        const int cc = threadIdx.x % CPO, r0 = threadIdx.x / CPO;
+#pragma unroll
+        for (int p = 0; p < QB / RPO; ++p) {
+            const int rr = p * RPO + r0, tt = blk * QB + rr;
+            if (tt < N)
+                *reinterpret_cast<uint4*>(codes + (((size_t)b * N + tt) * H + h) * D + 16 * cc) =
+                    *reinterpret_cast<const uint4*>(stage + rr * LDR + 16 * cc);
+        }
+    }
 }
 
 // ---------------------------------------------------------------- V
